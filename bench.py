@@ -1,0 +1,192 @@
+"""Throughput of the streaming code2wav decoder on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step decodes one 25-frame chunk (2 s of audio) for each of 64 independent
+streams whose states were first warmed (untimed) to different positions: the
+whole decoder (RVQ gather-sum, causal conv, 8-layer windowed transformer, 2x2
+upsampling, BigVGAN Snake/AMP stack, tanh) over 128 s of audio.  Inputs are
+resident in device memory before timing starts; successive steps continue the
+same streams (states ping-pong).  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix peak
+HBM_PEAK_GBS = 8000.0
+FRAME_SECONDS = 0.08  # 12.5 Hz frames
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen3_b64_chunk25")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-frames", type=int, default=25)
+    return ap.parse_args()
+
+
+def warm_states(dec, codes, batch, torch):
+    """Bring stream b to position batched_warmup_frames(b) (untimed)."""
+    import synthetic as S
+
+    warm = [S.batched_warmup_frames(b) for b in range(batch)]
+    common = min(warm)
+    st_a, st_b = dec.new_state(batch), dec.new_state(batch)
+    sched = [1] + [25] * ((common - 1) // 25)
+    t0 = 0
+    for n in sched:
+        c = torch.from_numpy(np.ascontiguousarray(codes[:, t0:t0 + n])).cuda()
+        dec.decode(c, st_a, st_b)
+        st_a, st_b = st_b, st_a
+        t0 += n
+    tmp = dec.new_state(1)
+    for b in range(batch):
+        tb = t0
+        while tb < warm[b]:
+            c = torch.from_numpy(np.ascontiguousarray(codes[b:b + 1, tb:tb + 25])).cuda()
+            dec.decode(c, st_a[b:b + 1], tmp)
+            st_a[b:b + 1].copy_(tmp)
+            tb += 25
+    torch.cuda.synchronize()
+    return st_a, st_b, warm
+
+
+def cpu_baseline(model, W, codes_1, frames):
+    """The float32 oracle on the host cores, one stream, `frames` frames from a fresh state."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from oracle import decoder as O
+
+    cores = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=cores):
+        used = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        Wf = O.cast_weights(W, np.float32)
+        t0 = time.perf_counter()
+        O.decode_whole(model, Wf, codes_1[:frames], dtype=np.float32)
+        el = time.perf_counter() - t0
+    audio = frames * FRAME_SECONDS
+    return {"value": audio / el, "unit": "audio-s/s", "cores": int(used), "kind": "oracle",
+            "sample": f"1 stream x {frames} frames ({audio:g} s of audio) from a fresh state, float32 numpy "
+                      f"oracle, {el:.1f} s wall"}
+
+
+def traffic_for(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except Exception:
+        return None
+    src = os.path.join(ROOT, "vocoder_rvq_codebook_amd", "csrc", "conv_gemm.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    k = rec.get("kernels", {}).get(kernel)
+    if not k or rec.get("conv_gemm_sha256") != sha:
+        return None
+    return k.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this decoder runs on one GPU: streams are independent and shard across GPUs "
+                                   "with no collectives, but only the single-GPU path is built; run with --gpus 1"}))
+        sys.exit(2)
+    import torch
+
+    import synthetic as S
+    from vocoder_rvq_codebook_amd import Decoder, binding as vb
+
+    wl = S.workload(args.workload)
+    model = wl["model"]
+    if wl["schedule"] != "warm_then_25":
+        raise SystemExit("bench.py times the batched 25-frame workload")
+    B, T = wl["batch"], wl["frames"]
+    W = S.make_weights(model, wl["weight_seed"])
+    codes = S.workload_codes(args.workload)
+    torch.cuda.set_device(0)
+    dec = Decoder(model, torch.from_numpy(S.flatten_weights(model, W)), B, T)
+    st_a, st_b, warm = warm_states(dec, codes, B, torch)
+    chunk = torch.from_numpy(np.stack([codes[b, warm[b]:warm[b] + T] for b in range(B)])).cuda()
+    pcm = torch.empty((B, T * dec.hop), device="cuda")
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        dec.decode(chunk, st_a, st_b, pcm)
+        st_a, st_b = st_b, st_a
+    torch.cuda.synchronize()
+
+    vb.vocoder_profile_begin(dec.handle)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        dec.decode(chunk, st_a, st_b, pcm)
+        st_a, st_b = st_b, st_a
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    prof = vb.vocoder_profile_end(dec.handle)
+    if dec.status() != vb.VOCODER_OK:
+        raise SystemExit("device reported an error during the timed steps")
+    gpu_s = ev0.elapsed_time(ev1) / 1e3
+    elapsed = max(wall, gpu_s)
+    audio_per_step = B * T * FRAME_SECONDS
+    value = audio_per_step * args.steps / elapsed
+
+    flops_step = sum(k["flops"] for k in prof.values()) / args.steps
+    dom_name, dom = max(prof.items(), key=lambda kv: kv[1]["total_ms"])
+    dom_ms = dom["total_ms"] / dom["launches"]
+    dom_tflops = dom["flops"] / dom["launches"] / (dom_ms * 1e-3) / 1e12
+    kernels = {k: {"launches_per_step": v["launches"] / args.steps, "ms_per_step": v["total_ms"] / args.steps,
+                   "tflops": (v["flops"] / (v["total_ms"] * 1e-3) / 1e12) if v["flops"] else None,
+                   "gbs": v["bytes"] / (v["total_ms"] * 1e-3) / 1e9}
+               for k, v in sorted(prof.items(), key=lambda kv: -kv[1]["total_ms"])}
+
+    out = {
+        "metric": "audio-seconds/sec (x real-time) for 64 x 25-frame chunks; % fp32 MFMA peak",
+        "value": round(value, 3),
+        "unit": "audio-s/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded random-init weights, uniform random codes)",
+        "config": {"workload": args.workload, "streams": B, "frames_per_chunk": T,
+                   "samples_per_frame": dec.hop, "warm_positions": sorted(set(warm))},
+        "tflops": round(flops_step / (elapsed / args.steps) / 1e12, 3),
+        "mfma_frac": round(flops_step / (elapsed / args.steps) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4),
+        "roofline": {"kernel": dom_name, "bound": "mfma", "achieved": round(dom_tflops, 3),
+                     "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(dom_tflops / FP32_MFMA_PEAK_TFLOPS, 4),
+                     "avg_launch_ms": round(dom_ms, 4), "traffic": traffic_for(dom_name)},
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(model, W, codes[0], args.cpu_frames)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,204 @@
+/*
+ * vocoder.h -- C ABI of the streaming code2wav decoder on MI355X (gfx950).
+ *
+ * What it computes ("Edge TTS design (vLLM-Omni-compatible)", section 1.3,
+ * Codec / vocoder): each 12.5 Hz codec frame carries one code per codebook
+ * (16 codebooks); the decoder sums the selected RVQ codewords, runs a causal
+ * conv, a stack of pre-norm transformer layers with a sliding attention window
+ * (72 frames), two stride-2 transposed convs, a causal conv into the BigVGAN
+ * stack (per stage: a causal transposed conv of kernel 2 x rate, then the mean
+ * of AMP residual blocks of Snake -> dilated conv -> Snake -> conv), a final
+ * Snake -> conv -> tanh, and emits `hop` fp32 samples per frame (1920 at 24 kHz
+ * for the Qwen3-TTS-12Hz shape).  The call shape follows section 2.2
+ * (IDecoderAdapter: decode(frames), reset(), left_context_frames()) with the
+ * state made explicit as an input and an output, as section 4 proposes for the
+ * ExecuTorch decoder, and section 2.3 (the decoder's conv context and attention
+ * window live for an utterance and survive between calls).
+ *
+ * Conventions
+ *  - Every data pointer is a DEVICE pointer on the current HIP device, except
+ *    the vocoder_config pointer (host).  `stream` is a hipStream_t (NULL = the
+ *    null stream).  Calls enqueue work on `stream` and never synchronise it,
+ *    except vocoder_get_status.
+ *  - The caller owns every device buffer (raw and packed weights, workspace,
+ *    states, codes, PCM).  The library allocates no device memory; it owns only
+ *    its host-side handle.
+ *  - Return values: VOCODER_OK (0) or a negative VOCODER_E* code.  Argument
+ *    errors are detected on the host before any HIP call.  Errors the device
+ *    detects (a code out of range, a state that belongs to another decoder) are
+ *    recorded in a status word inside the workspace and reported by
+ *    vocoder_get_status.
+ *  - A handle is not thread-safe; calls on one handle must be ordered on one
+ *    stream.  Distinct handles are independent.
+ */
+#ifndef VOCODER_H
+#define VOCODER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VOCODER_OK 0
+#define VOCODER_EINVAL (-1)       /* null pointer, bad size, unsupported config */
+#define VOCODER_ESTATE (-2)       /* state header does not match this decoder (device-detected) */
+#define VOCODER_EHIP (-3)         /* a HIP call or kernel launch failed */
+#define VOCODER_ECODE (-4)        /* a code outside [0, codebook_size) (device-detected) */
+
+#define VOCODER_MAX_UP 4
+#define VOCODER_MAX_STAGES 8
+#define VOCODER_MAX_RES 4
+#define VOCODER_MAX_DIL 4
+
+/* Decoder shape.  All channel counts that feed a convolution or linear layer
+ * must be multiples of 16; model_dim / n_heads (the head size) must be at most
+ * 256 and even.  Qwen3-TTS-12Hz shape: 16, 2048, 512, 1024, 8, 16, 72, 4096,
+ * 10000, 1e-5, 3, 2, {2,2}, 1536, 7, 4, {8,5,4,3}, 3, {3,7,11}, 3, {1,3,5}, 7. */
+typedef struct vocoder_config {
+  int32_t n_codebooks;      /* codes per frame (16) */
+  int32_t codebook_size;    /* entries per codebook (2048) */
+  int32_t embed_dim;        /* codeword width (512) */
+  int32_t model_dim;        /* transformer width d (1024) */
+  int32_t n_layers;         /* transformer layers (8) */
+  int32_t n_heads;          /* attention heads (16) */
+  int32_t window;           /* attention window W in frames (72): a frame attends itself and the W before it */
+  int32_t ffn_dim;          /* FFN hidden width (4096) */
+  float rope_theta;         /* RoPE base (10000) */
+  float ln_eps;             /* LayerNorm epsilon (1e-5) */
+  int32_t pre_kernel;       /* causal conv kernel before the transformer (3) */
+  int32_t n_up;             /* transposed convs after the transformer (2) */
+  int32_t up_strides[VOCODER_MAX_UP];       /* their strides ({2,2}); kernel = 2 x stride, d -> d */
+  int32_t voc_ch0;          /* BigVGAN input channels (1536) */
+  int32_t conv_pre_kernel;  /* causal conv d -> voc_ch0 (7) */
+  int32_t n_stages;         /* BigVGAN stages (4) */
+  int32_t rates[VOCODER_MAX_STAGES];        /* stage strides ({8,5,4,3}); kernel 2 x rate, channels halve */
+  int32_t n_res;            /* AMP blocks per stage (3) */
+  int32_t res_kernels[VOCODER_MAX_RES];     /* their kernel sizes ({3,7,11}) */
+  int32_t n_dil;            /* dilations per AMP block (3) */
+  int32_t dilations[VOCODER_MAX_DIL];       /* ({1,3,5}) */
+  int32_t post_kernel;      /* final conv kernel, C -> 1 (7) */
+  int32_t max_batch;        /* largest batch a decode call may pass (sizes the workspace) */
+  int32_t max_frames;       /* largest n_frames a decode call may pass (sizes the workspace) */
+} vocoder_config;
+
+typedef struct vocoder vocoder;
+
+/* Number of floats in the raw weight vector vocoder_create reads: every
+ * parameter, C-contiguous, in this order and these PyTorch-native layouts
+ * (Linear [out][in], Conv1d [out][in][k], ConvTranspose1d [in][out][k]):
+ *   codebooks [n_codebooks][codebook_size][embed_dim];
+ *   pre_conv.weight [d][embed_dim][pre_kernel], pre_conv.bias [d];
+ *   per layer: ln1.weight, ln1.bias [d]; q_proj, k_proj, v_proj, o_proj
+ *     (.weight [d][d], .bias [d] each); ln2.weight, ln2.bias [d];
+ *     fc1.weight [ffn][d], fc1.bias [ffn]; fc2.weight [d][ffn], fc2.bias [d];
+ *   final_ln.weight, final_ln.bias [d];
+ *   per up i: weight [d][d][2*up_strides[i]], bias [d];
+ *   conv_pre.weight [voc_ch0][d][conv_pre_kernel], conv_pre.bias [voc_ch0];
+ *   per stage s (C = voc_ch0 >> s input, C/2 output):
+ *     up.weight [C][C/2][2*rates[s]], up.bias [C/2];
+ *     per AMP block j, per dilation i: act1.alpha [C/2], conv1.weight
+ *       [C/2][C/2][res_kernels[j]], conv1.bias [C/2], act2.alpha [C/2],
+ *       conv2.weight [C/2][C/2][res_kernels[j]], conv2.bias [C/2];
+ *   act_post.alpha [C_last]; conv_post.weight [1][C_last][post_kernel];
+ *   conv_post.bias [1].
+ * Returns 0 if the config is invalid. */
+size_t vocoder_raw_weights_count(const vocoder_config* cfg);
+
+/* Bytes of the packed-weight buffer (library-internal layout). 0 if invalid. */
+size_t vocoder_packed_weights_bytes(const vocoder_config* cfg);
+
+/* Bytes of the workspace for max_batch streams x max_frames frames. 0 if invalid. */
+size_t vocoder_workspace_bytes(const vocoder_config* cfg);
+
+/* Bytes of one stream's state (a header plus every carried row).  A batch of
+ * states is [batch][state_bytes], stream b at offset b * state_bytes.  The
+ * state holds the frame position, the last `window` RoPE-rotated keys and
+ * values of every layer, and the last (k-1)*dilation input rows of every
+ * convolution (one row per transposed conv).  0 if invalid. */
+size_t vocoder_state_bytes(const vocoder_config* cfg);
+
+/* Build a decoder.  `raw_weights` (device, vocoder_raw_weights_count floats)
+ * is repacked into `packed_weights` (device, vocoder_packed_weights_bytes,
+ * 256-byte aligned) by kernels on `stream`; raw_weights may be freed once
+ * `stream` has completed that work.  `workspace` (device,
+ * vocoder_workspace_bytes, 256-byte aligned) must stay valid and unshared for
+ * the handle's life.  On success *out receives the handle.
+ * Errors: VOCODER_EINVAL (bad config or pointer), VOCODER_EHIP. */
+int vocoder_create(const vocoder_config* cfg, const float* raw_weights, void* packed_weights,
+                   void* workspace, void* stream, vocoder** out);
+
+/* Reset `batch` consecutive states (device, [batch][state_bytes]) to a fresh
+ * utterance: position 0, empty window, zero conv context (the decoder
+ * adapter's reset() of section 2.2, which drops all carried context).  Errors: VOCODER_EINVAL,
+ * VOCODER_EHIP. */
+int vocoder_reset(vocoder* v, void* state, int batch, void* stream);
+
+/* Decode one chunk of n_frames frames for each of `batch` streams.
+ *   codes     int32 [batch][n_frames][n_codebooks] (device)
+ *   state_in  [batch][state_bytes] (device), read only
+ *   state_out [batch][state_bytes] (device), written; must not overlap state_in
+ *             (ping-pong two buffers across calls)
+ *   pcm       float [batch][n_frames * hop] (device), written
+ * Streams may sit at different positions.  A chunk of T frames emits exactly
+ * T * hop samples per stream; any chunking of a stream gives the same samples
+ * as decoding it whole (each output element is reduced in the same order).
+ * Errors: VOCODER_EINVAL (null pointer, batch not in [1, max_batch], n_frames
+ * not in [1, max_frames], overlapping states), VOCODER_EHIP.  Device-detected
+ * errors (VOCODER_ECODE: that chunk's PCM is unspecified and no out-of-range
+ * codeword is read; VOCODER_ESTATE: the stream is decoded from a fresh state)
+ * are reported by vocoder_get_status. */
+int vocoder_decode_chunk(vocoder* v, const int32_t* codes, int batch, int n_frames,
+                         const void* state_in, void* state_out, float* pcm, void* stream);
+
+/* Samples per frame (product of up_strides and rates): 1920 for Qwen3-TTS-12Hz. */
+int vocoder_hop(const vocoder* v);
+
+/* Frames of attention left context the state carries (= window), as
+ * IDecoderAdapter::left_context_frames(). */
+int vocoder_left_context_frames(const vocoder* v);
+
+/* Synchronise `stream`, return the first device-detected error since the last
+ * call (VOCODER_ECODE or VOCODER_ESTATE) or VOCODER_OK, and clear it. */
+int vocoder_get_status(vocoder* v, void* stream);
+
+/* Debug taps: when set, each decode call also copies the named intermediate
+ * tensor (channels-last, [batch][rows][channels]) to `dst` (device; NULL
+ * clears).  Names: "embed", "pre_conv", "layer<l>", "final_ln", "up<i>",
+ * "conv_pre", "stage<s>.up", "stage<s>" (for the last stage: after the final
+ * Snake), "pre_tanh" ([batch][n_frames*hop]).  `dst_floats` is its capacity;
+ * a decode whose tap would overflow it skips the copy.  Errors: VOCODER_EINVAL. */
+int vocoder_set_tap(vocoder* v, const char* name, float* dst, size_t dst_floats);
+
+/* Measurement.  Between vocoder_profile_begin and vocoder_profile_end, every
+ * kernel a decode call launches is bracketed by HIP events recorded on the
+ * caller's stream.  vocoder_profile_end synchronises the stream, stops
+ * recording and aggregates per kernel: launches, total device time, and the
+ * kernel's algorithmic work (FLOPs of the dense contraction it computes, and
+ * the bytes it must read and write at least once).  Up to `max_entries`
+ * records are written to `out`; *n_entries receives how many exist.  Events
+ * are created by the library (host-side objects, no device allocation) and
+ * released by vocoder_destroy.  Errors: VOCODER_EINVAL, VOCODER_EHIP. */
+typedef struct vocoder_kernel_stat {
+  char name[48];      /* kernel family, e.g. "conv_gemm_96x256_bk32" */
+  int32_t launches;
+  double total_ms;    /* sum of event-measured launch durations */
+  double flops;       /* algorithmic FLOPs summed over launches */
+  double bytes;       /* algorithmic bytes summed over launches */
+} vocoder_kernel_stat;
+
+int vocoder_profile_begin(vocoder* v);
+int vocoder_profile_end(vocoder* v, void* stream, vocoder_kernel_stat* out, int max_entries, int* n_entries);
+
+/* Free the host handle (device buffers stay the caller's). */
+void vocoder_destroy(vocoder* v);
+
+/* Static text for a status code. */
+const char* vocoder_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VOCODER_H */

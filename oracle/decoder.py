@@ -60,8 +60,9 @@ from scipy.special import erf
 def rvq_embed_sum(codebooks: np.ndarray, codes: np.ndarray) -> np.ndarray:
     """Residual-VQ decode: e[t] = sum over q of codebooks[q][codes[t, q]].
 
-    Edge TTS design, section 1.3 ("RVQ embedding sum") and section 1.2 (codebook
-    0 from the talker, 1..15 from the code predictor).  The sum is taken in
+    Edge TTS design, section 1.3 (the decoder starts from the sum of the RVQ
+    codewords) and section 1.2 (codebook 0 comes from the talker, 1..15 from
+    the code predictor).  The sum is taken in
     ascending codebook order, one rounding per add, in the codebooks' dtype;
     numpy's pairwise np.sum is deliberately not used.  Codes outside
     [0, codebook_size) are an error.

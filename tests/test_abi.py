@@ -1,0 +1,99 @@
+"""The C-ABI library loads, exports what include/vocoder.h declares, and rejects
+bad arguments on the host.  CPU only: no call here launches a kernel."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import synthetic as S
+from vocoder_rvq_codebook_amd import binding as vb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vocoder.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vocoder_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) >= 12
+    L = vb.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", vb.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (vocoder_[a-z_]+)", out))
+    assert set(names) <= exported
+
+
+def test_config_struct_matches_header_layout():
+    # 8 int32 + 2 float + 2 int32 + 4 + 3 int32 + 8 + 1 + 4 + 1 + 4 + 3 int32
+    assert ctypes.sizeof(vb.VocoderConfig) == 4 * (8 + 2 + 2 + 4 + 3 + 8 + 1 + 4 + 1 + 4 + 3)
+
+
+@pytest.mark.parametrize("model", [S.TINY, S.MINI, S.QWEN3], ids=lambda m: m["name"])
+def test_raw_weight_count_matches_manifest(model):
+    cfg = vb.make_config(model, 4, 8)
+    assert vb.vocoder_raw_weights_count(cfg) == S.n_params(model)
+
+
+def test_qwen3_sizes():
+    cfg = vb.make_config(S.QWEN3, 64, 25)
+    assert S.n_params(S.QWEN3) == 259_806_497
+    st = vb.vocoder_state_bytes(cfg)
+    # rotated K and V of 72 frames x 8 layers x 1024, plus every conv context
+    kv = 8 * 2 * 72 * 1024 * 4
+    assert kv < st < kv + 2_000_000 and st % 256 == 0
+    assert vb.vocoder_packed_weights_bytes(cfg) >= 4 * S.n_params(S.QWEN3)
+    ws = vb.vocoder_workspace_bytes(cfg)
+    assert ws % 256 == 0 and ws > 64 * 25 * 1920 * 96 * 4
+
+
+def test_invalid_configs_rejected():
+    good = dict(S.MINI)
+    assert vb.vocoder_raw_weights_count(vb.make_config(good, 1, 1)) > 0
+    for key, val in [("embed_dim", 24), ("model_dim", 66), ("n_heads", 3), ("window", 300),
+                     ("ffn_dim", 0), ("voc_ch0", 200)]:
+        bad = dict(good)
+        bad[key] = val
+        cfg = vb.make_config(bad, 1, 1)
+        assert vb.vocoder_raw_weights_count(cfg) == 0, key
+        assert vb.vocoder_state_bytes(cfg) == 0, key
+    assert vb.vocoder_workspace_bytes(vb.make_config(good, 0, 1)) == 0
+    assert vb.vocoder_workspace_bytes(vb.make_config(good, 1, 0)) == 0
+
+
+def test_null_arguments_rejected_before_any_device_call():
+    L = vb.lib()
+    cfg = vb.make_config(S.MINI, 1, 1)
+    h = ctypes.c_void_p()
+    assert L.vocoder_create(ctypes.byref(cfg), None, None, None, None, ctypes.byref(h)) == vb.VOCODER_EINVAL
+    assert h.value is None
+    assert L.vocoder_create(ctypes.byref(cfg), 256, 256, 256, None, None) == vb.VOCODER_EINVAL
+    # misaligned buffers
+    assert L.vocoder_create(ctypes.byref(cfg), 256, 260, 256, None, ctypes.byref(h)) == vb.VOCODER_EINVAL
+    assert L.vocoder_decode_chunk(None, 256, 1, 1, 256, 512, 256, None) == vb.VOCODER_EINVAL
+    assert L.vocoder_reset(None, 256, 1, None) == vb.VOCODER_EINVAL
+    assert L.vocoder_get_status(None, None) == vb.VOCODER_EINVAL
+    assert L.vocoder_hop(None) == 0
+    assert L.vocoder_set_tap(None, b"embed", None, 0) == vb.VOCODER_EINVAL
+    L.vocoder_destroy(None)
+    assert vb.vocoder_strerror(vb.VOCODER_ECODE) == "code out of range"
+    assert vb.vocoder_strerror(vb.VOCODER_ESTATE).startswith("state")
+
+
+def test_flat_weights_follow_manifest():
+    W = S.make_weights(S.TINY, 0)
+    flat = S.flatten_weights(S.TINY, W)
+    assert flat.dtype == np.float32 and flat.size == S.n_params(S.TINY)
+    off = 0
+    for name, shape, _ in S.manifest(S.TINY):
+        n = int(np.prod(shape))
+        np.testing.assert_array_equal(flat[off:off + n], W[name].ravel())
+        off += n

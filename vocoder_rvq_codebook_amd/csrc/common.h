@@ -1,0 +1,116 @@
+// Shared device-side definitions of the code2wav decoder library (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// implicit-GEMM convolution (conv1d, transposed conv, linear)
+// ---------------------------------------------------------------------------
+//
+// out[g][m] = epi( sum_{tap, c} W[m][tap][c] * X[g - (k-1-tap)*dil][c] )
+// GEMM rows g run over (stream, row) pairs, channels-last.  Rows before the
+// start of a stream's chunk come from that stream's history slot in state_in.
+
+struct EpiOut {
+  float* dst;           // [rows_out][cout] or nullptr
+  const float* alpha;   // Snake alpha per GEMM column, nullptr = no Snake
+  float* hist;          // state_out slot of stream 0 ([H][cout]) or nullptr
+  int H;                // slot rows
+  int src;              // 0: the conv value v, 1: the multi-receptive-field value s
+};
+
+enum { MRF_NONE = 0, MRF_FIRST = 1, MRF_ACCUM = 2, MRF_LAST = 3, MRF_ONLY = 4 };
+enum { ACT_NONE = 0, ACT_GELU = 1 };
+
+struct ConvParams {
+  const float* w;       // packed [Mpad][k][cin]
+  int M;                // GEMM columns (= phases * cout)
+  int k, cin, dil;
+  const float* x;       // [rows][cin]
+  const float* hin;     // state_in slot of stream 0 ([hin_rows][cin])
+  long long sstride;    // state floats per stream
+  int hin_rows;         // (k-1)*dil history rows
+  int rows;             // GEMM rows = batch * nin
+  int nin;              // GEMM rows per stream
+  // epilogue
+  const float* bias;    // [M]
+  int act;
+  const float* resid;   // [rows_out][cout] or nullptr
+  int phases, cout;     // output row = g*phases + m/cout, channel = m % cout
+  int mrf_mode;
+  float mrf_div;        // divisor of the MRF mean
+  float* mrf;           // running MRF sum [rows_out][cout] (read in ACCUM/LAST)
+  int nout;
+  EpiOut out[4];
+};
+
+// ---------------------------------------------------------------------------
+// state layout
+// ---------------------------------------------------------------------------
+
+#define VOC_STATE_MAGIC 0x56434453u  // "SDCV"
+#define VOC_STATE_VERSION 1u
+#define VOC_STATE_HEADER_FLOATS 64   // 256 bytes
+
+struct StateHeader {
+  uint32_t magic;
+  uint32_t version;
+  uint64_t cfg_hash;
+  int64_t pos;        // frames decoded since reset
+  int64_t reserved[5];
+};
+
+// A state slot: the last H rows (oldest first) of a tensor with C channels,
+// which gains `rate` rows per frame.
+struct Slot {
+  long long off;   // float offset inside one stream's state
+  long long cap;   // floats reserved for the slot (H*C rounded up to 64)
+  int H;
+  int C;
+  int rate;
+  int pad;
+};
+
+// status bits in the workspace status word
+#define VOC_STATUS_CODE 1
+#define VOC_STATUS_STATE 2
+
+// ---------------------------------------------------------------------------
+// launchers (defined in conv_gemm.hip / kernels.hip)
+// ---------------------------------------------------------------------------
+
+// tile configuration ids for the implicit-GEMM kernel
+enum GemmTile { TILE_128x128 = 0, TILE_96x256 = 1, TILE_192x128 = 2, TILE_64x64 = 3, TILE_COUNT = 4 };
+int gemm_tile_bm(int tile);
+int gemm_tile_bn(int tile);
+hipError_t launch_conv_gemm(const ConvParams& p, int tile, hipStream_t s);
+
+hipError_t launch_begin(const void* state_in, void* state_out, long long sstride, int batch, int T,
+                        uint64_t cfg_hash, const double* inv_freq, int half, float* rope_tab, int* pos,
+                        int* status, hipStream_t s);
+hipError_t launch_state_shift(const Slot* slots, int nslots, int max_h, const float* state_in,
+                              float* state_out, long long sstride, int batch, int T, hipStream_t s);
+hipError_t launch_gather(const int32_t* codes, const float* codebooks, int Q, int V, int D, int rows,
+                         int T, float* out, float* hist, int H, long long sstride, int* status,
+                         hipStream_t s);
+hipError_t launch_layernorm(const float* x, const float* g, const float* b, float eps, int rows, int d,
+                            float* out, int T, float* hist, int H, long long sstride, hipStream_t s);
+hipError_t launch_rope_kv(float* qkv, const float* rope_tab, int rows, int T, int n_heads, int hd,
+                          float* k_hist, float* v_hist, int W, long long sstride, hipStream_t s);
+hipError_t launch_attention(const float* qkv, const float* k_state, const float* v_state,
+                            long long sstride, const int* pos, int batch, int T, int n_heads, int hd,
+                            int W, float* out, hipStream_t s);
+hipError_t launch_conv_post(const float* x, const float* hin, long long sstride, int H, const float* w,
+                            const float* bias, int C, int k, int rows, int nin, float* pcm,
+                            float* pre_tanh, hipStream_t s);
+hipError_t launch_repack_conv(const float* src, float* dst, int M, int Mpad, int cin, int k,
+                              hipStream_t s);
+hipError_t launch_repack_convT(const float* src, float* dst, int cin, int cout, int stride, int Mpad,
+                               hipStream_t s);
+hipError_t launch_expand_vec(const float* src, float* dst, int C, int phases, int Mpad, hipStream_t s);
+hipError_t launch_fill(void* dst, size_t bytes, hipStream_t s);
+hipError_t launch_reset_headers(void* state, long long sstride, int batch, uint64_t cfg_hash,
+                                hipStream_t s);

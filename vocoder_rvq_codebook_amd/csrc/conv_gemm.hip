@@ -1,0 +1,306 @@
+// Implicit-GEMM causal convolution on fp32 MFMA (gfx950).
+//
+// One kernel serves every dense contraction of the decoder:
+//  - causal dilated Conv1d (pre-conv, conv_pre, the AMP convs of every BigVGAN
+//    stage): A = weights [Cout][tap][Cin], B = input rows shifted by
+//    (k-1-tap)*dil, rows before the chunk read from the stream's history slot;
+//  - causal ConvTranspose1d with kernel 2 x stride: each output phase p is a
+//    2-tap conv of the input (tap 0 -> row t-1, tap 1 -> row t), and the s
+//    phases are stacked along M, so [T][s*Cout] written channels-last is
+//    exactly the upsampled [T*s][Cout] (blixt/phonon, Weights: a transposed
+//    conv becomes one GEMM per output phase that gathers its inputs);
+//  - transformer linears (k = 1).
+// The epilogue fuses bias, GELU, residual add, the multi-receptive-field mean,
+// one to four Snake outputs (x + sin^2(alpha x)/alpha), and the write of each
+// output's last rows into the stream's next state.
+//
+// Each output element's reduction order depends only on (tap, channel): the K
+// loop is fixed and never split, so results are bitwise independent of batch,
+// chunking and tile shape.
+
+#include "common.h"
+
+namespace {
+
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, BK = BK_;
+  static constexpr int NT = WAVES_M * WAVES_N * 64;
+  static constexpr int WTM = BM / WAVES_M;
+  static constexpr int WTN = BN / WAVES_N;
+  static constexpr int FM = WTM / 16;
+  static constexpr int FN = WTN / 16;
+  static constexpr int LDK = BK + 4;  // padded LDS row (floats): 16-byte rows shift 4 banks
+  static constexpr int KV = BK / 4;   // float4 per row per k-step
+  static constexpr int A_F4 = BM * KV;
+  static constexpr int B_F4 = BN * KV;
+  static constexpr int A_LD = (A_F4 + NT - 1) / NT;
+  static constexpr int B_LD = (B_F4 + NT - 1) / NT;
+  static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be a multiple of 16");
+  static_assert(BK % 16 == 0, "BK must be a multiple of 16");
+};
+
+__device__ __forceinline__ float snake1(float v, float a) {
+  float s = sinf(a * v);
+  return v + (s * s) / a;
+}
+
+__device__ __forceinline__ float gelu1(float v) {
+  return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
+}
+
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ void st4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+
+template <class C>
+__global__ __launch_bounds__(C::NT) void conv_gemm_kernel(const ConvParams p) {
+  __shared__ __attribute__((aligned(16))) float As[2][C::BM * C::LDK];
+  __shared__ __attribute__((aligned(16))) float Bs[2][C::BN * C::LDK];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave % C::WAVES_M;
+  const int wn = wave / C::WAVES_M;
+
+  // XCD-aware tile order: workgroups are dealt round-robin to the 8 XCDs, so
+  // give each XCD a contiguous run of tiles, M-tiles fastest, so the blocks
+  // that share an input tile share an L2.
+  const int mtiles = (p.M + C::BM - 1) / C::BM;
+  int tile_id;
+  {
+    const int L = blockIdx.x, nb = gridDim.x;
+    const int xcd = L & 7, i = L >> 3;
+    const int per = nb >> 3, extra = nb & 7;
+    tile_id = xcd * per + (xcd < extra ? xcd : extra) + i;
+  }
+  const int mt = tile_id % mtiles;
+  const int nt = tile_id / mtiles;
+  const int m0 = mt * C::BM;
+  const int g0 = nt * C::BN;
+
+  const int cin = p.cin;
+  const int ksteps_per_tap = cin / C::BK;
+  const int nsteps = p.k * ksteps_per_tap;
+
+  // per-thread load slots
+  int a_row[C::A_LD], a_col[C::A_LD];
+  bool a_ok[C::A_LD];
+#pragma unroll
+  for (int i = 0; i < C::A_LD; ++i) {
+    const int idx = tid + i * C::NT;
+    a_ok[i] = (C::A_F4 % C::NT == 0) || idx < C::A_F4;
+    a_row[i] = idx / C::KV;
+    a_col[i] = (idx % C::KV) * 4;
+  }
+  int b_row[C::B_LD], b_col[C::B_LD], b_g[C::B_LD], b_n[C::B_LD];
+  bool b_ok[C::B_LD];
+#pragma unroll
+  for (int i = 0; i < C::B_LD; ++i) {
+    const int idx = tid + i * C::NT;
+    const bool in_tile = (C::B_F4 % C::NT == 0) || idx < C::B_F4;
+    b_row[i] = idx / C::KV;
+    b_col[i] = (idx % C::KV) * 4;
+    const int g = g0 + b_row[i];
+    b_ok[i] = in_tile && g < p.rows;
+    b_g[i] = g;
+    const int b = b_ok[i] ? g / p.nin : 0;
+    b_n[i] = g - b * p.nin;
+  }
+
+  f32x4 ra[C::A_LD], rb[C::B_LD];
+
+  auto gload = [&](int s) {
+    const int tap = s / ksteps_per_tap;
+    const int c0 = (s - tap * ksteps_per_tap) * C::BK;
+    const int shift = (p.k - 1 - tap) * p.dil;
+#pragma unroll
+    for (int i = 0; i < C::A_LD; ++i) {
+      if (a_ok[i]) {
+        const size_t off = ((size_t)(m0 + a_row[i]) * p.k + tap) * cin + c0 + a_col[i];
+        ra[i] = ld4(p.w + off);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < C::B_LD; ++i) {
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      if (b_ok[i]) {
+        const int n2 = b_n[i] - shift;
+        const float* src;
+        if (n2 >= 0) {
+          src = p.x + (size_t)(b_g[i] - shift) * cin;
+        } else {
+          const int b = (b_g[i] - b_n[i]) / p.nin;
+          src = p.hin + (size_t)b * p.sstride + (size_t)(p.hin_rows + n2) * cin;
+        }
+        v = ld4(src + c0 + b_col[i]);
+      }
+      rb[i] = v;
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < C::A_LD; ++i)
+      if (a_ok[i]) st4(&As[buf][a_row[i] * C::LDK + a_col[i]], ra[i]);
+#pragma unroll
+    for (int i = 0; i < C::B_LD; ++i)
+      if ((C::B_F4 % C::NT == 0) || tid + i * C::NT < C::B_F4)
+        st4(&Bs[buf][b_row[i] * C::LDK + b_col[i]], rb[i]);
+  };
+
+  // Two-level accumulation: the MFMA chain runs into `part` for GROUP_K
+  // reduction values (32 MFMAs at most), then `part` is added to `acc`.  A
+  // single chain over all k*cin values loses about 4x more precision; the
+  // grouping depends only on the K index, so it is the same for every tile.
+  constexpr int GROUP_K = 128;
+  constexpr int GROUP_STEPS = GROUP_K / C::BK;
+  f32x4 acc[C::FM][C::FN], part[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+      acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      part[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+
+  // MFMA 16x16x4 f32: lane l supplies A[l%16][k] and B[k][l%16] with
+  // k = l/16.  Lane group l/16 owns 4 consecutive k of a 16-wide slab, read
+  // as one float4, and the 4 MFMAs of the slab take its components in turn.
+  const int lr = lane & 15;
+  const int lk = (lane >> 4) * 4;
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int s = 0; s < nsteps; ++s) {
+    const int cur = s & 1;
+    if (s + 1 < nsteps) gload(s + 1);
+    const float* Ab = As[cur];
+    const float* Bb = Bs[cur];
+#pragma unroll
+    for (int kk = 0; kk < C::BK; kk += 16) {
+      f32x4 af[C::FM], bf[C::FN];
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i) af[i] = ld4(&Ab[(wm * C::WTM + i * 16 + lr) * C::LDK + kk + lk]);
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) bf[j] = ld4(&Bb[(wn * C::WTN + j * 16 + lr) * C::LDK + kk + lk]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j)
+            part[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i][q], bf[j][q], part[i][j], 0, 0, 0);
+    }
+    if ((s + 1) % GROUP_STEPS == 0 || s + 1 == nsteps) {
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+          acc[i][j] += part[i][j];
+          part[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    if (s + 1 < nsteps) lstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds rows m..m+3 (4*(l/16) + r) of column g (l%16)
+  const int nout_rows = p.nin * p.phases;
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) {
+    const int m = m0 + wm * C::WTM + i * 16 + (lane >> 4) * 4;
+    if (m >= p.M) continue;
+    const f32x4 bias = ld4(p.bias + m);
+    const int ph = m / p.cout;
+    const int c = m - ph * p.cout;
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+      const int g = g0 + wn * C::WTN + j * 16 + lr;
+      if (g >= p.rows) continue;
+      f32x4 v = acc[i][j] + bias;
+      if (p.act == ACT_GELU) {
+        v.x = gelu1(v.x); v.y = gelu1(v.y); v.z = gelu1(v.z); v.w = gelu1(v.w);
+      }
+      const size_t orow = (size_t)g * p.phases + ph;
+      const size_t oidx = orow * p.cout + c;
+      if (p.resid) v = v + ld4(p.resid + oidx);
+      f32x4 sm = v;
+      if (p.mrf_mode == MRF_FIRST) {
+        sm = v;
+      } else if (p.mrf_mode == MRF_ACCUM) {
+        sm = ld4(p.mrf + oidx) + v;
+      } else if (p.mrf_mode == MRF_LAST) {
+        sm = (ld4(p.mrf + oidx) + v) / p.mrf_div;
+      } else if (p.mrf_mode == MRF_ONLY) {
+        sm = v / p.mrf_div;
+      }
+      const int b = g / p.nin;
+      const int no = (g - b * p.nin) * p.phases + ph;
+#pragma unroll
+      for (int o = 0; o < 4; ++o) {
+        if (o >= p.nout) break;
+        const EpiOut& eo = p.out[o];
+        f32x4 val = eo.src ? sm : v;
+        if (eo.alpha) {
+          const f32x4 a = ld4(eo.alpha + m);
+          val.x = snake1(val.x, a.x); val.y = snake1(val.y, a.y);
+          val.z = snake1(val.z, a.z); val.w = snake1(val.w, a.w);
+        }
+        if (eo.dst) st4(eo.dst + oidx, val);
+        if (eo.hist && no >= nout_rows - eo.H) {
+          st4(eo.hist + (size_t)b * p.sstride + (size_t)(eo.H - nout_rows + no) * p.cout + c, val);
+        }
+      }
+    }
+  }
+}
+
+template <class C>
+hipError_t launch_cfg(const ConvParams& p, hipStream_t s) {
+  const int mtiles = (p.M + C::BM - 1) / C::BM;
+  const int ntiles = (p.rows + C::BN - 1) / C::BN;
+  const long long nb = (long long)mtiles * ntiles;
+  if (nb <= 0) return hipSuccess;
+  if (nb > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(conv_gemm_kernel<C>, dim3((unsigned)nb), dim3(C::NT), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int gemm_tile_bm(int tile) {
+  switch (tile) {
+    case TILE_128x128: return 128;
+    case TILE_96x256: return 96;
+    case TILE_192x128: return 192;
+    case TILE_64x64: return 64;
+  }
+  return 0;
+}
+
+int gemm_tile_bn(int tile) {
+  switch (tile) {
+    case TILE_128x128: return 128;
+    case TILE_96x256: return 256;
+    case TILE_192x128: return 128;
+    case TILE_64x64: return 64;
+  }
+  return 0;
+}
+
+hipError_t launch_conv_gemm(const ConvParams& p, int tile, hipStream_t s) {
+  const bool bk32 = (p.cin % 32) == 0;
+  if (p.cin % 16 != 0) return hipErrorInvalidValue;
+  switch (tile) {
+    case TILE_128x128:
+      return bk32 ? launch_cfg<TileCfg<128, 128, 2, 2, 32>>(p, s) : launch_cfg<TileCfg<128, 128, 2, 2, 16>>(p, s);
+    case TILE_96x256:
+      return bk32 ? launch_cfg<TileCfg<96, 256, 1, 4, 32>>(p, s) : launch_cfg<TileCfg<96, 256, 1, 4, 16>>(p, s);
+    case TILE_192x128:
+      return bk32 ? launch_cfg<TileCfg<192, 128, 2, 2, 32>>(p, s) : launch_cfg<TileCfg<192, 128, 2, 2, 16>>(p, s);
+    case TILE_64x64:
+      return bk32 ? launch_cfg<TileCfg<64, 64, 2, 2, 32>>(p, s) : launch_cfg<TileCfg<64, 64, 2, 2, 16>>(p, s);
+  }
+  return hipErrorInvalidValue;
+}

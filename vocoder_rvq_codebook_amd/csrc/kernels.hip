@@ -1,0 +1,478 @@
+// Bandwidth-bound and small kernels of the code2wav decoder (gfx950):
+// state header / RoPE table, state shift, RVQ gather-sum, LayerNorm, RoPE +
+// key/value state write, sliding-window attention, the final C -> 1 conv with
+// tanh, weight repacking and fills.
+
+#include "common.h"
+
+namespace {
+
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ void st4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+inline unsigned cdiv(long long a, long long b) { return (unsigned)((a + b - 1) / b); }
+
+// ---------------------------------------------------------------------------
+// begin: validate each stream's state header, publish its position, write the
+// next state's header, and build the RoPE cos/sin table [batch][T][half] for
+// absolute positions pos + t (angles in float64).
+// ---------------------------------------------------------------------------
+__global__ void begin_kernel(const float* __restrict__ sin_, float* __restrict__ sout, long long sstride,
+                             int batch, int T, uint64_t hash, const double* __restrict__ inv, int half,
+                             float* __restrict__ tab, int* __restrict__ pos, int* __restrict__ status) {
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long per_stream = (long long)T * (half > 0 ? half : 1);
+  if (idx >= (long long)batch * per_stream) return;
+  const int b = (int)(idx / per_stream);
+  const int r = (int)(idx - (long long)b * per_stream);
+  const StateHeader* h = reinterpret_cast<const StateHeader*>(sin_ + (size_t)b * sstride);
+  const bool ok = h->magic == VOC_STATE_MAGIC && h->version == VOC_STATE_VERSION && h->cfg_hash == hash &&
+                  h->pos >= 0 && h->pos < (1LL << 40);
+  const long long p0 = ok ? h->pos : 0;
+  if (r == 0) {
+    if (!ok) atomicOr(status, VOC_STATUS_STATE);
+    pos[b] = (int)(p0 & 0x7fffffff);
+    StateHeader* ho = reinterpret_cast<StateHeader*>(sout + (size_t)b * sstride);
+    ho->magic = VOC_STATE_MAGIC;
+    ho->version = VOC_STATE_VERSION;
+    ho->cfg_hash = hash;
+    ho->pos = p0 + T;
+    for (int i = 0; i < 5; ++i) ho->reserved[i] = 0;
+    float* rest = sout + (size_t)b * sstride;
+    for (int i = (int)(sizeof(StateHeader) / 4); i < VOC_STATE_HEADER_FLOATS; ++i) rest[i] = 0.f;
+  }
+  if (half > 0) {
+    const int t = r / half, i = r - t * half;
+    const double ang = (double)(p0 + t) * inv[i];
+    float* o = tab + (((size_t)b * T + t) * half + i) * 2;
+    o[0] = (float)cos(ang);
+    o[1] = (float)sin(ang);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// state shift: for a slot of H rows that gains N = T*rate rows this call,
+// rows [N, H) of the old state become rows [0, H-N) of the new one (the rest
+// is written by the kernel that produces the new rows).  The slot's alignment
+// padding is zeroed, so every byte of the new state is defined.
+// ---------------------------------------------------------------------------
+__global__ void state_shift_kernel(const Slot* __restrict__ slots, const float* __restrict__ sin_,
+                                   float* __restrict__ sout, long long sstride, int T) {
+  const Slot sl = slots[blockIdx.x];
+  const int b = blockIdx.y;
+  float* dst = sout + (size_t)b * sstride + sl.off;
+  const long long used = (long long)sl.H * sl.C;
+  for (long long i = used + threadIdx.x; i < sl.cap; i += blockDim.x) dst[i] = 0.f;
+  const long long N = (long long)T * sl.rate;
+  if (N >= sl.H) return;
+  const long long keep = (long long)(sl.H - N) * sl.C;
+  const float* src = sin_ + (size_t)b * sstride + sl.off + N * sl.C;
+  for (long long i = threadIdx.x; i < keep; i += blockDim.x) dst[i] = src[i];
+}
+
+// ---------------------------------------------------------------------------
+// RVQ gather-sum: e[row] = sum over q (ascending) of codebooks[q][codes[row][q]],
+// one fp32 add per codebook.  A code outside [0, V) flags the status word and
+// contributes nothing (its row is never read).
+// ---------------------------------------------------------------------------
+__global__ void gather_kernel(const int32_t* __restrict__ codes, const float* __restrict__ cb, int Q, int V,
+                              int D, int rows, int T, float* __restrict__ out, float* __restrict__ hist, int H,
+                              long long sstride, int* __restrict__ status) {
+  const int D4 = D / 4;
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (long long)rows * D4) return;
+  const int row = (int)(idx / D4);
+  const int c = (int)(idx - (long long)row * D4) * 4;
+  const int32_t* cr = codes + (size_t)row * Q;
+  f32x4 e = {0.f, 0.f, 0.f, 0.f};
+  bool bad = false;
+  for (int q = 0; q < Q; ++q) {
+    const int code = cr[q];
+    if (code < 0 || code >= V) {
+      bad = true;
+      continue;
+    }
+    const f32x4 w = ld4(cb + ((size_t)q * V + code) * D + c);
+    if (q == 0) {
+      e = w;
+    } else {
+      e.x = __fadd_rn(e.x, w.x);
+      e.y = __fadd_rn(e.y, w.y);
+      e.z = __fadd_rn(e.z, w.z);
+      e.w = __fadd_rn(e.w, w.w);
+    }
+  }
+  if (bad && c == 0) atomicOr(status, VOC_STATUS_CODE);
+  st4(out + (size_t)row * D + c, e);
+  const int b = row / T, t = row - b * T;
+  if (hist && t >= T - H) st4(hist + (size_t)b * sstride + (size_t)(H - T + t) * D + c, e);
+}
+
+// ---------------------------------------------------------------------------
+// LayerNorm over d channels, one wave per row, biased variance, two passes.
+// Optionally writes the last H rows of each stream into a state slot.
+// ---------------------------------------------------------------------------
+__global__ void layernorm_kernel(const float* __restrict__ x, const float* __restrict__ g,
+                                 const float* __restrict__ bta, float eps, int rows, int d,
+                                 float* __restrict__ out, int T, float* __restrict__ hist, int H,
+                                 long long sstride) {
+  const int row = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const float* xr = x + (size_t)row * d;
+  const int d4 = d / 4;
+  float s = 0.f;
+  for (int c = lane; c < d4; c += 64) {
+    const f32x4 v = ld4(xr + 4 * c);
+    s += (v.x + v.y) + (v.z + v.w);
+  }
+  const float mean = wave_sum(s) / (float)d;
+  float q = 0.f;
+  for (int c = lane; c < d4; c += 64) {
+    const f32x4 v = ld4(xr + 4 * c) - mean;
+    q += (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
+  }
+  const float var = wave_sum(q) / (float)d;
+  const float rstd = 1.0f / sqrtf(var + eps);
+  const int b = row / T, t = row - b * T;
+  const bool tail = hist && t >= T - H;
+  for (int c = lane; c < d4; c += 64) {
+    const f32x4 v = (ld4(xr + 4 * c) - mean) * rstd * ld4(g + 4 * c) + ld4(bta + 4 * c);
+    st4(out + (size_t)row * d + 4 * c, v);
+    if (tail) st4(hist + (size_t)b * sstride + (size_t)(H - T + t) * d + 4 * c, v);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// RoPE on q and k (rotate-half pairs (i, i + hd/2)) in place in the fused
+// qkv rows; the last W frames' rotated k and raw v go to the state slots.
+// ---------------------------------------------------------------------------
+__global__ void rope_kv_kernel(float* __restrict__ qkv, const float* __restrict__ tab, int rows, int T,
+                               int n_heads, int hd, float* __restrict__ kh, float* __restrict__ vh, int W,
+                               long long sstride) {
+  const int half = hd / 2;
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long per_row = (long long)n_heads * half;
+  if (idx >= (long long)rows * per_row) return;
+  const int row = (int)(idx / per_row);
+  const int r = (int)(idx - (long long)row * per_row);
+  const int h = r / half, i = r - h * half;
+  const int d = n_heads * hd;
+  const int b = row / T, t = row - b * T;
+  const float c = tab[((size_t)row * half + i) * 2 + 0];
+  const float sn = tab[((size_t)row * half + i) * 2 + 1];
+  float* q = qkv + (size_t)row * 3 * d + h * hd;
+  float* k = q + d;
+  const float* v = q + 2 * d;
+  const float q1 = q[i], q2 = q[i + half];
+  q[i] = q1 * c - q2 * sn;
+  q[i + half] = q1 * sn + q2 * c;
+  const float k1 = k[i], k2 = k[i + half];
+  const float kr1 = k1 * c - k2 * sn, kr2 = k1 * sn + k2 * c;
+  k[i] = kr1;
+  k[i + half] = kr2;
+  if (W > 0 && t >= T - W) {
+    const size_t o = (size_t)b * sstride + (size_t)(W - T + t) * d + h * hd;
+    kh[o + i] = kr1;
+    kh[o + i + half] = kr2;
+    vh[o + i] = v[i];
+    vh[o + i + half] = v[i + half];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Sliding-window attention.  Block = (query tile of QT frames, head, stream);
+// the keys and values the tile needs (state window + new frames) are staged
+// in LDS.  Query at absolute position P attends positions [P - W, P]; lane
+// o <-> key position P - W + o, so every reduction order depends only on
+// absolute positions.
+// ---------------------------------------------------------------------------
+constexpr int ATT_QT = 16;
+constexpr int ATT_THREADS = 256;
+
+__global__ __launch_bounds__(ATT_THREADS) void attention_kernel(
+    const float* __restrict__ qkv, const float* __restrict__ ks, const float* __restrict__ vs, long long sstride,
+    const int* __restrict__ pos, int T, int n_heads, int hd, int W, float* __restrict__ out) {
+  extern __shared__ float smem[];
+  const int d = n_heads * hd;
+  const int t0 = blockIdx.x * ATT_QT, h = blockIdx.y, b = blockIdx.z;
+  const int p0 = pos[b];
+  const int nq = min(ATT_QT, T - t0);
+  const int nk = nq + W;  // concat rows j in [t0, t0 + nq - 1 + W]
+  const int ldk = hd + 1;
+  float* Ks = smem;                       // [(QT + W)][ldk]
+  float* Vs = Ks + (ATT_QT + W) * ldk;    // [(QT + W)][hd]
+  float* Qs = Vs + (ATT_QT + W) * hd;     // [QT][hd]
+  const int tid = threadIdx.x;
+  for (int idx = tid; idx < nk * hd; idx += ATT_THREADS) {
+    const int r = idx / hd, c = idx - r * hd;
+    const int j = t0 + r;  // concat index: j < W state row, else new frame j - W
+    float kv = 0.f, vv = 0.f;
+    if (j < W) {
+      if (p0 - W + j >= 0) {
+        const size_t o = (size_t)b * sstride + (size_t)j * d + h * hd + c;
+        kv = ks[o];
+        vv = vs[o];
+      }
+    } else if (j - W < T) {
+      const float* row = qkv + ((size_t)b * T + (j - W)) * 3 * d;
+      kv = row[d + h * hd + c];
+      vv = row[2 * d + h * hd + c];
+    }
+    Ks[r * ldk + c] = kv;
+    Vs[r * hd + c] = vv;
+  }
+  for (int idx = tid; idx < nq * hd; idx += ATT_THREADS) {
+    const int r = idx / hd, c = idx - r * hd;
+    Qs[r * hd + c] = qkv[((size_t)b * T + t0 + r) * 3 * d + h * hd + c];
+  }
+  __syncthreads();
+  const int lane = tid & 63, wave = tid >> 6;
+  const float scale = 1.0f / sqrtf((float)hd);
+  for (int tl = wave; tl < nq; tl += ATT_THREADS / 64) {
+    const long long P = (long long)p0 + t0 + tl;
+    const float* qv = Qs + tl * hd;
+    float e[4];
+    float m = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int o = lane + 64 * u;
+      e[u] = -INFINITY;
+      if (o <= W && P - W + o >= 0) {
+        const float* kr = Ks + (tl + o) * ldk;
+        float s = 0.f;
+        for (int c = 0; c < hd; ++c) s += qv[c] * kr[c];
+        e[u] = s * scale;
+        m = fmaxf(m, e[u]);
+      }
+    }
+    m = wave_max(m);
+    float part = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int o = lane + 64 * u;
+      e[u] = (o <= W && P - W + o >= 0) ? expf(e[u] - m) : 0.f;
+      part += e[u];
+    }
+    const float denom = wave_sum(part);
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ub = 0; ub < 4; ++ub) {
+      for (int oo = 0; oo < 64; ++oo) {
+        const int o = 64 * ub + oo;
+        if (o > W) break;
+        const float pw = __shfl(e[ub], oo, 64);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int c = lane + 64 * u;
+          if (c < hd) acc[u] += pw * Vs[(tl + o) * hd + c];
+        }
+      }
+    }
+    float* orow = out + ((size_t)b * T + t0 + tl) * d + h * hd;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = lane + 64 * u;
+      if (c < hd) orow[c] = acc[u] / denom;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Final conv C -> 1 (kernel k, causal, history from the state) and tanh.
+// One thread per output sample; the C-channel rows are read as float4.
+// ---------------------------------------------------------------------------
+__global__ void conv_post_kernel(const float* __restrict__ x, const float* __restrict__ hin, long long sstride,
+                                 int H, const float* __restrict__ w, const float* __restrict__ bias, int C, int k,
+                                 int rows, int nin, float* __restrict__ pcm, float* __restrict__ pre) {
+  const int g = blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= rows) return;
+  const int b = g / nin, n = g - b * nin;
+  float acc = bias[0];
+  for (int j = 0; j < k; ++j) {
+    const int n2 = n - (k - 1 - j);
+    const float* src = n2 >= 0 ? x + (size_t)(g - (k - 1 - j)) * C
+                               : hin + (size_t)b * sstride + (size_t)(H + n2) * C;
+    const float* wj = w + (size_t)j * C;
+    float dot = 0.f;
+    for (int c = 0; c < C; c += 4) {
+      const f32x4 xv = ld4(src + c), wv = ld4(wj + c);
+      dot = fmaf(wv.x, xv.x, dot);
+      dot = fmaf(wv.y, xv.y, dot);
+      dot = fmaf(wv.z, xv.z, dot);
+      dot = fmaf(wv.w, xv.w, dot);
+    }
+    acc += dot;
+  }
+  if (pre) pre[g] = acc;
+  pcm[g] = tanhf(acc);
+}
+
+// ---------------------------------------------------------------------------
+// weight repacking (create time)
+// ---------------------------------------------------------------------------
+// Conv1d / Linear [M][cin][k] -> [Mpad][k][cin], zero rows past M.
+__global__ void repack_conv_kernel(const float* __restrict__ src, float* __restrict__ dst, int M, int Mpad,
+                                   int cin, int k) {
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long total = (long long)Mpad * k * cin;
+  if (idx >= total) return;
+  const int c = (int)(idx % cin);
+  const long long r = idx / cin;
+  const int j = (int)(r % k);
+  const int m = (int)(r / k);
+  dst[idx] = m < M ? src[((size_t)m * cin + c) * k + j] : 0.f;
+}
+
+// ConvTranspose1d [cin][cout][2s] -> [Mpad][2][cin] with row m = p*cout + o:
+// tap 0 (input row t-1) takes kernel index p + s, tap 1 (row t) takes p.
+__global__ void repack_convT_kernel(const float* __restrict__ src, float* __restrict__ dst, int cin, int cout,
+                                    int s, int Mpad) {
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long total = (long long)Mpad * 2 * cin;
+  if (idx >= total) return;
+  const int c = (int)(idx % cin);
+  const long long r = idx / cin;
+  const int j = (int)(r % 2);
+  const int m = (int)(r / 2);
+  float v = 0.f;
+  if (m < s * cout) {
+    const int p = m / cout, o = m - p * cout;
+    const int kk = j == 0 ? p + s : p;
+    v = src[((size_t)c * cout + o) * (2 * s) + kk];
+  }
+  dst[idx] = v;
+}
+
+// per-channel vector [C] -> [Mpad] indexed by GEMM column m = p*C + c
+__global__ void expand_vec_kernel(const float* __restrict__ src, float* __restrict__ dst, int C, int phases,
+                                  int Mpad) {
+  const int m = blockIdx.x * blockDim.x + threadIdx.x;
+  if (m >= Mpad) return;
+  dst[m] = m < C * phases ? src[m % C] : 0.f;
+}
+
+__global__ void fill_kernel(uint32_t* __restrict__ dst, size_t words) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += (size_t)gridDim.x * blockDim.x)
+    dst[i] = 0u;
+}
+
+__global__ void reset_headers_kernel(float* __restrict__ state, long long sstride, int batch, uint64_t hash) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= batch) return;
+  StateHeader* h = reinterpret_cast<StateHeader*>(state + (size_t)b * sstride);
+  h->magic = VOC_STATE_MAGIC;
+  h->version = VOC_STATE_VERSION;
+  h->cfg_hash = hash;
+  h->pos = 0;
+  for (int i = 0; i < 5; ++i) h->reserved[i] = 0;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+
+hipError_t launch_begin(const void* state_in, void* state_out, long long sstride, int batch, int T,
+                        uint64_t cfg_hash, const double* inv_freq, int half, float* rope_tab, int* pos,
+                        int* status, hipStream_t s) {
+  const long long n = (long long)batch * T * (half > 0 ? half : 1);
+  hipLaunchKernelGGL(begin_kernel, dim3(cdiv(n, 256)), dim3(256), 0, s, (const float*)state_in,
+                     (float*)state_out, sstride, batch, T, cfg_hash, inv_freq, half, rope_tab, pos, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_shift(const Slot* slots, int nslots, int max_h, const float* state_in, float* state_out,
+                              long long sstride, int batch, int T, hipStream_t s) {
+  (void)max_h;
+  if (nslots == 0) return hipSuccess;
+  hipLaunchKernelGGL(state_shift_kernel, dim3(nslots, batch), dim3(256), 0, s, slots, state_in, state_out,
+                     sstride, T);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const int32_t* codes, const float* codebooks, int Q, int V, int D, int rows, int T,
+                         float* out, float* hist, int H, long long sstride, int* status, hipStream_t s) {
+  const long long n = (long long)rows * (D / 4);
+  hipLaunchKernelGGL(gather_kernel, dim3(cdiv(n, 256)), dim3(256), 0, s, codes, codebooks, Q, V, D, rows, T, out,
+                     hist, H, sstride, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_layernorm(const float* x, const float* g, const float* b, float eps, int rows, int d, float* out,
+                            int T, float* hist, int H, long long sstride, hipStream_t s) {
+  hipLaunchKernelGGL(layernorm_kernel, dim3(cdiv(rows, 4)), dim3(256), 0, s, x, g, b, eps, rows, d, out, T, hist,
+                     H, sstride);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_kv(float* qkv, const float* rope_tab, int rows, int T, int n_heads, int hd, float* k_hist,
+                          float* v_hist, int W, long long sstride, hipStream_t s) {
+  const long long n = (long long)rows * n_heads * (hd / 2);
+  hipLaunchKernelGGL(rope_kv_kernel, dim3(cdiv(n, 256)), dim3(256), 0, s, qkv, rope_tab, rows, T, n_heads, hd,
+                     k_hist, v_hist, W, sstride);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention(const float* qkv, const float* k_state, const float* v_state, long long sstride,
+                            const int* pos, int batch, int T, int n_heads, int hd, int W, float* out,
+                            hipStream_t s) {
+  const size_t smem = ((size_t)(ATT_QT + W) * (hd + 1) + (size_t)(ATT_QT + W) * hd + (size_t)ATT_QT * hd) *
+                      sizeof(float);
+  if (smem > 64 * 1024) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(attention_kernel, dim3(cdiv(T, ATT_QT), n_heads, batch), dim3(ATT_THREADS), smem, s, qkv,
+                     k_state, v_state, sstride, pos, T, n_heads, hd, W, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_conv_post(const float* x, const float* hin, long long sstride, int H, const float* w,
+                            const float* bias, int C, int k, int rows, int nin, float* pcm, float* pre_tanh,
+                            hipStream_t s) {
+  hipLaunchKernelGGL(conv_post_kernel, dim3(cdiv(rows, 256)), dim3(256), 0, s, x, hin, sstride, H, w, bias, C, k,
+                     rows, nin, pcm, pre_tanh);
+  return hipGetLastError();
+}
+
+hipError_t launch_repack_conv(const float* src, float* dst, int M, int Mpad, int cin, int k, hipStream_t s) {
+  const long long n = (long long)Mpad * k * cin;
+  hipLaunchKernelGGL(repack_conv_kernel, dim3(cdiv(n, 256)), dim3(256), 0, s, src, dst, M, Mpad, cin, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_repack_convT(const float* src, float* dst, int cin, int cout, int stride, int Mpad,
+                               hipStream_t s) {
+  const long long n = (long long)Mpad * 2 * cin;
+  hipLaunchKernelGGL(repack_convT_kernel, dim3(cdiv(n, 256)), dim3(256), 0, s, src, dst, cin, cout, stride, Mpad);
+  return hipGetLastError();
+}
+
+hipError_t launch_expand_vec(const float* src, float* dst, int C, int phases, int Mpad, hipStream_t s) {
+  hipLaunchKernelGGL(expand_vec_kernel, dim3(cdiv(Mpad, 256)), dim3(256), 0, s, src, dst, C, phases, Mpad);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill(void* dst, size_t bytes, hipStream_t s) {
+  const size_t words = bytes / 4;
+  if (words == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)std::min<size_t>((words + 255) / 256, 65536);
+  hipLaunchKernelGGL(fill_kernel, dim3(blocks), dim3(256), 0, s, (uint32_t*)dst, words);
+  return hipGetLastError();
+}
+
+hipError_t launch_reset_headers(void* state, long long sstride, int batch, uint64_t cfg_hash, hipStream_t s) {
+  hipLaunchKernelGGL(reset_headers_kernel, dim3(cdiv(batch, 256)), dim3(256), 0, s, (float*)state, sstride, batch,
+                     cfg_hash);
+  return hipGetLastError();
+}

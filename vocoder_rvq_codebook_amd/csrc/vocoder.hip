@@ -1,0 +1,934 @@
+// Host side of the code2wav decoder library: config checks, the packed-weight,
+// state and workspace layouts, create / reset / decode_chunk.
+//
+// The decoder ("Edge TTS design (vLLM-Omni-compatible)", section 1.3): RVQ
+// embedding sum -> causal conv -> sliding-window transformer -> 2x2 transposed
+// conv upsampling -> BigVGAN Snake/AMP stack -> tanh, with the conv context and
+// the attention window carried across chunks as explicit state (sections 2.2,
+// 2.3 and the ExecuTorch note of section 4).
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/vocoder.h"
+#include "common.h"
+
+namespace {
+
+constexpr long long ALIGN = 64;  // floats (256 bytes)
+inline long long align_up(long long x, long long a = ALIGN) { return (x + a - 1) / a * a; }
+inline int round_up_i(int x, int a) { return (x + a - 1) / a * a; }
+
+// ---------------------------------------------------------------------------
+// config
+// ---------------------------------------------------------------------------
+
+bool config_valid(const vocoder_config* c) {
+  if (!c) return false;
+  auto m16 = [](int v) { return v > 0 && v % 16 == 0; };
+  if (c->n_codebooks < 1 || c->n_codebooks > 64 || c->codebook_size < 1) return false;
+  if (!m16(c->embed_dim) || !m16(c->model_dim) || !m16(c->ffn_dim)) return false;
+  if (c->n_layers < 0 || c->n_layers > 64 || c->n_heads < 1 || c->model_dim % c->n_heads) return false;
+  const int hd = c->model_dim / c->n_heads;
+  if (hd % 2 || hd > 256) return false;
+  if (c->window < 0 || c->window > 255) return false;
+  // the attention kernel stages (16 + window) keys and values plus 16 queries in 64 KB of LDS
+  if ((16LL + c->window) * (2LL * hd + 1) + 16LL * hd > 16384) return false;
+  if (!(c->ln_eps > 0.f) || !(c->rope_theta > 0.f)) return false;
+  if (c->pre_kernel < 1 || c->pre_kernel > 64) return false;
+  if (c->n_up < 0 || c->n_up > VOCODER_MAX_UP) return false;
+  for (int i = 0; i < c->n_up; ++i)
+    if (c->up_strides[i] < 1 || c->up_strides[i] > 64) return false;
+  if (c->n_stages < 1 || c->n_stages > VOCODER_MAX_STAGES) return false;
+  if (c->voc_ch0 <= 0 || c->voc_ch0 % (16 << c->n_stages)) return false;
+  if (c->conv_pre_kernel < 1 || c->conv_pre_kernel > 64) return false;
+  for (int s = 0; s < c->n_stages; ++s)
+    if (c->rates[s] < 1 || c->rates[s] > 64) return false;
+  if (c->n_res < 1 || c->n_res > VOCODER_MAX_RES || c->n_dil < 1 || c->n_dil > VOCODER_MAX_DIL) return false;
+  for (int j = 0; j < c->n_res; ++j)
+    if (c->res_kernels[j] < 1 || c->res_kernels[j] > 64) return false;
+  for (int i = 0; i < c->n_dil; ++i)
+    if (c->dilations[i] < 1 || c->dilations[i] > 64) return false;
+  if (c->post_kernel < 1 || c->post_kernel > 64) return false;
+  if (c->max_batch < 1 || c->max_frames < 1) return false;
+  // every GEMM row count must fit in int
+  long long hop = 1;
+  for (int i = 0; i < c->n_up; ++i) hop *= c->up_strides[i];
+  for (int s = 0; s < c->n_stages; ++s) hop *= c->rates[s];
+  if (hop > (1 << 20)) return false;
+  if ((long long)c->max_batch * c->max_frames * hop >= (1LL << 31) / 4) return false;
+  return true;
+}
+
+uint64_t config_hash(const vocoder_config* c) {
+  // FNV-1a over the model fields (max_batch / max_frames excluded: they size
+  // the workspace, not the state)
+  vocoder_config k = *c;
+  k.max_batch = 0;
+  k.max_frames = 0;
+  const unsigned char* b = reinterpret_cast<const unsigned char*>(&k);
+  uint64_t h = 1469598103934665603ULL;
+  for (size_t i = 0; i < sizeof(k); ++i) {
+    h ^= b[i];
+    h *= 1099511628211ULL;
+  }
+  return h;
+}
+
+int hop_of(const vocoder_config& c) {
+  int h = 1;
+  for (int i = 0; i < c.n_up; ++i) h *= c.up_strides[i];
+  for (int s = 0; s < c.n_stages; ++s) h *= c.rates[s];
+  return h;
+}
+
+// ---------------------------------------------------------------------------
+// layout plan (shared by size queries and create)
+// ---------------------------------------------------------------------------
+
+struct GemmW {
+  long long w = -1, bias = -1;  // packed float offsets
+  long long raw_w = -1, raw_b = -1;
+  int M = 0, Mpad = 0, k = 1, cin = 0, phases = 1, cout = 0;
+};
+
+struct LayerP {
+  long long ln1_g, ln1_b, ln2_g, ln2_b;         // packed
+  long long raw_ln1_g, raw_ln1_b, raw_ln2_g, raw_ln2_b;
+  long long raw_q_w, raw_q_b, raw_k_w, raw_k_b, raw_v_w, raw_v_b;
+  GemmW qkv, o, fc1, fc2;
+  int slot_k, slot_v;
+};
+
+struct AmpP {
+  GemmW conv1, conv2;
+  long long act1 = -1, act2 = -1;          // packed alpha [C]
+  long long raw_act1 = -1, raw_act2 = -1;
+  int slot1 = -1, slot2 = -1;              // conv1 / conv2 input slots
+};
+
+struct StageP {
+  GemmW up;                                // transposed conv, M = r * C
+  std::vector<long long> up_alpha;         // expanded act1 alpha of dilation 0, per AMP block
+  int slot_up = -1;                        // ConvT input slot (1 row)
+  std::vector<AmpP> amp;                   // [n_res * n_dil]
+  int cin = 0, c = 0, r = 1;
+  long long rate = 1;                      // rows per frame at the output
+};
+
+struct Plan {
+  vocoder_config cfg{};
+  int d = 0, hd = 0, half = 0, hop = 0;
+  long long raw_count = 0;
+  // packed
+  long long raw_codebooks = 0, codebooks = 0;
+  GemmW pre;
+  int slot_pre = -1;
+  std::vector<LayerP> layers;
+  long long raw_fln_g = 0, raw_fln_b = 0, fln_g = 0, fln_b = 0;
+  std::vector<GemmW> ups;
+  std::vector<int> slot_ups;               // input slot of each up
+  GemmW conv_pre;
+  int slot_conv_pre = -1;
+  std::vector<StageP> stages;
+  long long raw_post_alpha = 0, post_alpha = 0, raw_post_w = 0, raw_post_b = 0, post_w = 0, post_b = 0;
+  int slot_post = -1;
+  long long inv_freq = 0;                  // packed doubles (offset in floats)
+  long long slots_off = 0;                 // packed Slot table (offset in floats)
+  long long packed_floats = 0;
+  // state
+  std::vector<Slot> slots;
+  long long state_floats = 0;
+  // workspace (float offsets)
+  long long ws_status = 0, ws_pos = 0, ws_rope = 0, ws_emb = 0, ws_h = 0, ws_u = 0, ws_qkv = 0, ws_att = 0,
+            ws_ffn = 0;
+  std::vector<long long> ws_up;
+  long long ws_X0 = 0, ws_T = 0, ws_Xr = 0, ws_An = 0, ws_S[2] = {0, 0};
+  std::vector<long long> ws_A;
+  long long ws_floats = 0;
+};
+
+int add_slot(Plan& P, int H, int C, long long rate) {
+  Slot s{};
+  s.off = P.state_floats;
+  s.H = H;
+  s.C = C;
+  s.rate = (int)rate;
+  s.cap = align_up((long long)H * C);
+  P.slots.push_back(s);
+  P.state_floats += align_up((long long)H * C);
+  return (int)P.slots.size() - 1;
+}
+
+bool make_plan(const vocoder_config* cp, Plan& P) {
+  if (!config_valid(cp)) return false;
+  const vocoder_config& c = *cp;
+  P.cfg = c;
+  P.d = c.model_dim;
+  P.hd = c.model_dim / c.n_heads;
+  P.half = P.hd / 2;
+  P.hop = hop_of(c);
+  const int d = P.d, De = c.embed_dim, F = c.ffn_dim;
+
+  long long raw = 0, pk = 0;
+  auto R = [&](long long n) { long long o = raw; raw += n; return o; };
+  auto K = [&](long long n) { long long o = pk; pk += align_up(n); return o; };
+  auto gemm = [&](GemmW& g, int M, int k, int cin, int phases, int cout) {
+    g.M = M;
+    g.Mpad = round_up_i(M, 128);
+    g.k = k;
+    g.cin = cin;
+    g.phases = phases;
+    g.cout = cout;
+    g.w = K((long long)g.Mpad * k * cin);
+    g.bias = K(g.Mpad);
+  };
+
+  P.state_floats = VOC_STATE_HEADER_FLOATS;
+
+  // codebooks and pre-conv
+  P.raw_codebooks = R((long long)c.n_codebooks * c.codebook_size * De);
+  P.codebooks = K((long long)c.n_codebooks * c.codebook_size * De);
+  gemm(P.pre, d, c.pre_kernel, De, 1, d);
+  P.pre.raw_w = R((long long)d * De * c.pre_kernel);
+  P.pre.raw_b = R(d);
+  P.slot_pre = add_slot(P, c.pre_kernel - 1, De, 1);
+
+  // transformer
+  P.layers.resize(c.n_layers);
+  for (int l = 0; l < c.n_layers; ++l) {
+    LayerP& L = P.layers[l];
+    L.raw_ln1_g = R(d); L.raw_ln1_b = R(d);
+    L.raw_q_w = R((long long)d * d); L.raw_q_b = R(d);
+    L.raw_k_w = R((long long)d * d); L.raw_k_b = R(d);
+    L.raw_v_w = R((long long)d * d); L.raw_v_b = R(d);
+    gemm(L.o, d, 1, d, 1, d);
+    L.o.raw_w = R((long long)d * d); L.o.raw_b = R(d);
+    L.raw_ln2_g = R(d); L.raw_ln2_b = R(d);
+    gemm(L.fc1, F, 1, d, 1, F);
+    L.fc1.raw_w = R((long long)F * d); L.fc1.raw_b = R(F);
+    gemm(L.fc2, d, 1, F, 1, d);
+    L.fc2.raw_w = R((long long)d * F); L.fc2.raw_b = R(d);
+    gemm(L.qkv, 3 * d, 1, d, 1, 3 * d);
+    L.ln1_g = K(d); L.ln1_b = K(d); L.ln2_g = K(d); L.ln2_b = K(d);
+    L.slot_k = add_slot(P, c.window, d, 1);
+    L.slot_v = add_slot(P, c.window, d, 1);
+  }
+  P.raw_fln_g = R(d);
+  P.raw_fln_b = R(d);
+  P.fln_g = K(d);
+  P.fln_b = K(d);
+
+  // 2x2 upsampling
+  long long rate = 1;
+  P.ups.resize(c.n_up);
+  for (int i = 0; i < c.n_up; ++i) {
+    const int s = c.up_strides[i];
+    gemm(P.ups[i], s * d, 2, d, s, d);
+    P.ups[i].raw_w = R((long long)d * d * 2 * s);
+    P.ups[i].raw_b = R(d);
+    P.slot_ups.push_back(add_slot(P, 1, d, rate));
+    rate *= s;
+  }
+  // conv_pre
+  const int C0 = c.voc_ch0;
+  gemm(P.conv_pre, C0, c.conv_pre_kernel, d, 1, C0);
+  P.conv_pre.raw_w = R((long long)C0 * d * c.conv_pre_kernel);
+  P.conv_pre.raw_b = R(C0);
+  P.slot_conv_pre = add_slot(P, c.conv_pre_kernel - 1, d, rate);
+
+  // BigVGAN stages
+  P.stages.resize(c.n_stages);
+  int cin = C0;
+  for (int si = 0; si < c.n_stages; ++si) {
+    StageP& S = P.stages[si];
+    const int r = c.rates[si], co = cin / 2;
+    S.cin = cin;
+    S.c = co;
+    S.r = r;
+    gemm(S.up, r * co, 2, cin, r, co);
+    S.up.raw_w = R((long long)cin * co * 2 * r);
+    S.up.raw_b = R(co);
+    S.slot_up = add_slot(P, 1, cin, rate);
+    rate *= r;
+    S.rate = rate;
+    S.amp.resize((size_t)c.n_res * c.n_dil);
+    for (int j = 0; j < c.n_res; ++j) {
+      const int k = c.res_kernels[j];
+      for (int i = 0; i < c.n_dil; ++i) {
+        AmpP& A = S.amp[(size_t)j * c.n_dil + i];
+        A.raw_act1 = R(co);
+        gemm(A.conv1, co, k, co, 1, co);
+        A.conv1.raw_w = R((long long)co * co * k);
+        A.conv1.raw_b = R(co);
+        A.raw_act2 = R(co);
+        gemm(A.conv2, co, k, co, 1, co);
+        A.conv2.raw_w = R((long long)co * co * k);
+        A.conv2.raw_b = R(co);
+        A.act1 = K(co);
+        A.act2 = K(co);
+        A.slot1 = add_slot(P, (k - 1) * c.dilations[i], co, rate);
+        A.slot2 = add_slot(P, k - 1, co, rate);
+      }
+    }
+    for (int j = 0; j < c.n_res; ++j) S.up_alpha.push_back(K(S.up.Mpad));
+    cin = co;
+  }
+  P.raw_post_alpha = R(cin);
+  P.raw_post_w = R((long long)cin * c.post_kernel);
+  P.raw_post_b = R(1);
+  P.post_alpha = K(cin);
+  P.post_w = K((long long)cin * c.post_kernel);
+  P.post_b = K(4);
+  P.slot_post = add_slot(P, c.post_kernel - 1, cin, rate);
+
+  P.inv_freq = K(2LL * std::max(P.half, 1));
+  P.slots_off = K((long long)(sizeof(Slot) / 4) * (long long)P.slots.size());
+  P.raw_count = raw;
+  P.packed_floats = pk;
+
+  // workspace, sized for max_batch x max_frames
+  const long long Rr = (long long)c.max_batch * c.max_frames;
+  long long ws = 0;
+  auto Wk = [&](long long n) { long long o = ws; ws += align_up(n); return o; };
+  P.ws_status = Wk(64);
+  P.ws_pos = Wk(c.max_batch);
+  P.ws_rope = Wk(Rr * std::max(P.half, 1) * 2);
+  P.ws_emb = Wk(Rr * De);
+  P.ws_h = Wk(Rr * d);
+  P.ws_u = Wk(Rr * d);
+  P.ws_qkv = Wk(Rr * 3 * d);
+  P.ws_att = Wk(Rr * d);
+  P.ws_ffn = Wk(Rr * F);
+  long long ur = 1;
+  for (int i = 0; i < c.n_up; ++i) {
+    ur *= c.up_strides[i];
+    P.ws_up.push_back(Wk(Rr * ur * d));
+  }
+  long long big = Rr * ur * C0;  // conv_pre output
+  for (const StageP& S : P.stages) big = std::max(big, Rr * S.rate * S.c);
+  P.ws_X0 = Wk(big);
+  for (int j = 0; j < c.n_res; ++j) P.ws_A.push_back(Wk(big));
+  P.ws_T = Wk(big);
+  P.ws_Xr = Wk(big);
+  P.ws_An = Wk(big);
+  P.ws_S[0] = Wk(big);
+  P.ws_S[1] = Wk(big);
+  P.ws_floats = ws;
+  return true;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// handle
+// ---------------------------------------------------------------------------
+
+struct vocoder {
+  Plan P;
+  uint64_t hash = 0;
+  float* packed = nullptr;
+  float* ws = nullptr;
+  std::map<std::string, std::pair<float*, size_t>> taps;
+  // measurement: event pairs around each launch while profiling is on
+  struct Rec {
+    int name;
+    double flops, bytes;
+  };
+  bool prof = false;
+  std::vector<hipEvent_t> events;
+  std::vector<Rec> recs;
+  std::vector<std::string> prof_names;
+  ~vocoder() {
+    for (hipEvent_t e : events) (void)hipEventDestroy(e);
+  }
+};
+
+namespace {
+
+#define HIP_OK(x)                          \
+  do {                                     \
+    if ((x) != hipSuccess) return VOCODER_EHIP; \
+  } while (0)
+
+// Brackets one kernel launch with HIP events while profiling is on.
+class Prof {
+ public:
+  Prof(vocoder* v, hipStream_t s, const std::string& name, double flops, double bytes) : v_(v), s_(s) {
+    if (!v->prof) return;
+    int id = -1;
+    for (size_t i = 0; i < v->prof_names.size(); ++i)
+      if (v->prof_names[i] == name) id = (int)i;
+    if (id < 0) {
+      v->prof_names.push_back(name);
+      id = (int)v->prof_names.size() - 1;
+    }
+    const size_t k = v->recs.size();
+    while (v->events.size() < 2 * (k + 1)) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) return;
+      v->events.push_back(e);
+    }
+    if (hipEventRecord(v->events[2 * k], s) != hipSuccess) return;
+    v->recs.push_back({id, flops, bytes});
+    idx_ = (long long)k;
+  }
+  ~Prof() {
+    if (idx_ >= 0) (void)hipEventRecord(v_->events[2 * idx_ + 1], s_);
+  }
+
+ private:
+  vocoder* v_;
+  hipStream_t s_;
+  long long idx_ = -1;
+};
+
+int pick_tile(int M, long long rows) {
+  const long long rt128 = (rows + 127) / 128;
+  if (M % 96 == 0 && M <= 288 && rows >= 4096) return TILE_96x256;
+  if (M == 192 && rows >= 4096) return TILE_192x128;
+  if ((long long)((M + 127) / 128) * rt128 < 1024) return TILE_64x64;
+  return TILE_128x128;
+}
+
+struct Ctx {
+  vocoder* v;
+  hipStream_t s;
+  const float* sin_;
+  float* sout;
+  long long sstride;
+  int B, T;
+};
+
+ConvParams base_params(const Ctx& cx, const GemmW& g, const float* x, int rows, int nin, int dil,
+                       int hslot) {
+  const Plan& P = cx.v->P;
+  ConvParams p{};
+  p.w = cx.v->packed + g.w;
+  p.M = g.M;
+  p.k = g.k;
+  p.cin = g.cin;
+  p.dil = dil;
+  p.x = x;
+  p.sstride = cx.sstride;
+  if (hslot >= 0) {
+    p.hin = cx.sin_ + P.slots[hslot].off;
+    p.hin_rows = P.slots[hslot].H;
+  }
+  p.rows = rows;
+  p.nin = nin;
+  p.bias = cx.v->packed + g.bias;
+  p.act = ACT_NONE;
+  p.phases = g.phases;
+  p.cout = g.cout;
+  p.mrf_mode = MRF_NONE;
+  p.mrf_div = 1.f;
+  p.nout = 0;
+  return p;
+}
+
+void add_out(const Ctx& cx, ConvParams& p, float* dst, const float* alpha, int hslot, int src = 0) {
+  EpiOut& o = p.out[p.nout++];
+  o.dst = dst;
+  o.alpha = alpha;
+  o.src = src;
+  if (hslot >= 0) {
+    o.hist = cx.sout + cx.v->P.slots[hslot].off;
+    o.H = cx.v->P.slots[hslot].H;
+  } else {
+    o.hist = nullptr;
+    o.H = 0;
+  }
+}
+
+int run_gemm(const Ctx& cx, const ConvParams& p) {
+  const int tile = pick_tile(p.M, p.rows);
+  const int bm = gemm_tile_bm(tile);
+  const int mt = (p.M + bm - 1) / bm;
+  const GemmW* dummy = nullptr;
+  (void)dummy;
+  // A-tile rows read must lie inside the packed (zero-padded) weight rows
+  if ((long long)mt * bm > round_up_i(p.M, 128)) return VOCODER_EINVAL;
+  if (p.hin_rows < (p.k - 1) * p.dil) return VOCODER_EINVAL;
+  const double K = (double)p.k * p.cin;
+  const double flops = 2.0 * p.M * K * p.rows;
+  double bytes = 4.0 * ((double)p.M * K + (double)p.rows * p.cin + (double)p.nout * p.rows * p.M);
+  if (p.resid) bytes += 4.0 * p.rows * p.M;
+  if (p.mrf_mode == MRF_ACCUM || p.mrf_mode == MRF_LAST) bytes += 4.0 * p.rows * p.M;
+  char name[48];
+  snprintf(name, sizeof(name), "conv_gemm_%dx%d_bk%d", bm, gemm_tile_bn(tile), p.cin % 32 == 0 ? 32 : 16);
+  Prof pr(cx.v, cx.s, name, flops, bytes);
+  HIP_OK(launch_conv_gemm(p, tile, cx.s));
+  return VOCODER_OK;
+}
+
+void tap(const Ctx& cx, const char* name, const float* src, long long count) {
+  auto it = cx.v->taps.find(name);
+  if (it == cx.v->taps.end() || !it->second.first) return;
+  if ((size_t)count > it->second.second) return;
+  (void)hipMemcpyAsync(it->second.first, src, (size_t)count * sizeof(float), hipMemcpyDeviceToDevice, cx.s);
+}
+
+int repack_gemm(vocoder* v, const float* raw, const GemmW& g, bool transposed, hipStream_t s) {
+  float* pk = v->packed;
+  if (transposed) {
+    HIP_OK(launch_repack_convT(raw + g.raw_w, pk + g.w, g.cin, g.cout, g.phases, g.Mpad, s));
+    HIP_OK(launch_expand_vec(raw + g.raw_b, pk + g.bias, g.cout, g.phases, g.Mpad, s));
+  } else {
+    HIP_OK(launch_repack_conv(raw + g.raw_w, pk + g.w, g.M, g.Mpad, g.cin, g.k, s));
+    HIP_OK(launch_expand_vec(raw + g.raw_b, pk + g.bias, g.M, 1, g.Mpad, s));
+  }
+  return VOCODER_OK;
+}
+
+int copy_d2d(float* dst, const float* src, long long n, hipStream_t s) {
+  HIP_OK(hipMemcpyAsync(dst, src, (size_t)n * sizeof(float), hipMemcpyDeviceToDevice, s));
+  return VOCODER_OK;
+}
+
+#define CHECK(x)                   \
+  do {                             \
+    int _r = (x);                  \
+    if (_r != VOCODER_OK) return _r; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+size_t vocoder_raw_weights_count(const vocoder_config* cfg) {
+  Plan P;
+  return make_plan(cfg, P) ? (size_t)P.raw_count : 0;
+}
+
+size_t vocoder_packed_weights_bytes(const vocoder_config* cfg) {
+  Plan P;
+  return make_plan(cfg, P) ? (size_t)P.packed_floats * 4 : 0;
+}
+
+size_t vocoder_workspace_bytes(const vocoder_config* cfg) {
+  Plan P;
+  return make_plan(cfg, P) ? (size_t)P.ws_floats * 4 : 0;
+}
+
+size_t vocoder_state_bytes(const vocoder_config* cfg) {
+  Plan P;
+  return make_plan(cfg, P) ? (size_t)P.state_floats * 4 : 0;
+}
+
+int vocoder_create(const vocoder_config* cfg, const float* raw_weights, void* packed_weights, void* workspace,
+                   void* stream, vocoder** out) {
+  if (!out) return VOCODER_EINVAL;
+  *out = nullptr;
+  if (!raw_weights || !packed_weights || !workspace) return VOCODER_EINVAL;
+  if (((uintptr_t)packed_weights & 255) || ((uintptr_t)workspace & 255)) return VOCODER_EINVAL;
+  vocoder* v = new (std::nothrow) vocoder();
+  if (!v) return VOCODER_EINVAL;
+  if (!make_plan(cfg, v->P)) {
+    delete v;
+    return VOCODER_EINVAL;
+  }
+  v->hash = config_hash(cfg);
+  v->packed = (float*)packed_weights;
+  v->ws = (float*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  const Plan& P = v->P;
+  const vocoder_config& c = P.cfg;
+  const float* raw = raw_weights;
+  float* pk = v->packed;
+  int rc = VOCODER_OK;
+  auto fail = [&](int r) { delete v; return r; };
+
+  if (launch_fill(pk, (size_t)P.packed_floats * 4, s) != hipSuccess) return fail(VOCODER_EHIP);
+  if ((rc = copy_d2d(pk + P.codebooks, raw + P.raw_codebooks,
+                     (long long)c.n_codebooks * c.codebook_size * c.embed_dim, s))) return fail(rc);
+  if ((rc = repack_gemm(v, raw, P.pre, false, s))) return fail(rc);
+  const int d = P.d;
+  for (const LayerP& L : P.layers) {
+    if ((rc = copy_d2d(pk + L.ln1_g, raw + L.raw_ln1_g, d, s))) return fail(rc);
+    if ((rc = copy_d2d(pk + L.ln1_b, raw + L.raw_ln1_b, d, s))) return fail(rc);
+    if ((rc = copy_d2d(pk + L.ln2_g, raw + L.raw_ln2_g, d, s))) return fail(rc);
+    if ((rc = copy_d2d(pk + L.ln2_b, raw + L.raw_ln2_b, d, s))) return fail(rc);
+    // q, k, v stacked along M into one [3d][1][d] GEMM
+    const long long raw_w[3] = {L.raw_q_w, L.raw_k_w, L.raw_v_w};
+    const long long raw_b[3] = {L.raw_q_b, L.raw_k_b, L.raw_v_b};
+    for (int t = 0; t < 3; ++t) {
+      if (launch_repack_conv(raw + raw_w[t], pk + L.qkv.w + (long long)t * d * d, d, d, d, 1, s) != hipSuccess)
+        return fail(VOCODER_EHIP);
+      if ((rc = copy_d2d(pk + L.qkv.bias + (long long)t * d, raw + raw_b[t], d, s))) return fail(rc);
+    }
+    if ((rc = repack_gemm(v, raw, L.o, false, s))) return fail(rc);
+    if ((rc = repack_gemm(v, raw, L.fc1, false, s))) return fail(rc);
+    if ((rc = repack_gemm(v, raw, L.fc2, false, s))) return fail(rc);
+  }
+  if ((rc = copy_d2d(pk + P.fln_g, raw + P.raw_fln_g, d, s))) return fail(rc);
+  if ((rc = copy_d2d(pk + P.fln_b, raw + P.raw_fln_b, d, s))) return fail(rc);
+  for (const GemmW& g : P.ups)
+    if ((rc = repack_gemm(v, raw, g, true, s))) return fail(rc);
+  if ((rc = repack_gemm(v, raw, P.conv_pre, false, s))) return fail(rc);
+  for (const StageP& S : P.stages) {
+    if ((rc = repack_gemm(v, raw, S.up, true, s))) return fail(rc);
+    for (int j = 0; j < c.n_res; ++j) {
+      const AmpP& A0 = S.amp[(size_t)j * c.n_dil];
+      if (launch_expand_vec(raw + A0.raw_act1, pk + S.up_alpha[j], S.c, S.r, S.up.Mpad, s) != hipSuccess)
+        return fail(VOCODER_EHIP);
+    }
+    for (const AmpP& A : S.amp) {
+      if ((rc = repack_gemm(v, raw, A.conv1, false, s))) return fail(rc);
+      if ((rc = repack_gemm(v, raw, A.conv2, false, s))) return fail(rc);
+      if ((rc = copy_d2d(pk + A.act1, raw + A.raw_act1, S.c, s))) return fail(rc);
+      if ((rc = copy_d2d(pk + A.act2, raw + A.raw_act2, S.c, s))) return fail(rc);
+    }
+  }
+  const int CL = P.stages.back().c;
+  if ((rc = copy_d2d(pk + P.post_alpha, raw + P.raw_post_alpha, CL, s))) return fail(rc);
+  // conv_post [1][C][k] -> [k][C]
+  if (launch_repack_conv(raw + P.raw_post_w, pk + P.post_w, 1, 1, CL, c.post_kernel, s) != hipSuccess)
+    return fail(VOCODER_EHIP);
+  if ((rc = copy_d2d(pk + P.post_b, raw + P.raw_post_b, 1, s))) return fail(rc);
+
+  // RoPE inverse frequencies (float64) and the slot table, staged from the host
+  std::vector<double> inv(std::max(P.half, 1), 0.0);
+  for (int i = 0; i < P.half; ++i) inv[i] = std::pow((double)c.rope_theta, -2.0 * i / (double)P.hd);
+  if (hipMemcpyAsync(pk + P.inv_freq, inv.data(), inv.size() * sizeof(double), hipMemcpyHostToDevice, s) !=
+      hipSuccess)
+    return fail(VOCODER_EHIP);
+  if (!P.slots.empty() && hipMemcpyAsync(pk + P.slots_off, P.slots.data(), P.slots.size() * sizeof(Slot),
+                                         hipMemcpyHostToDevice, s) != hipSuccess)
+    return fail(VOCODER_EHIP);
+  // the host vectors above are released on return: wait for the copies
+  if (hipStreamSynchronize(s) != hipSuccess) return fail(VOCODER_EHIP);
+  if (launch_fill(v->ws + P.ws_status, 256, s) != hipSuccess) return fail(VOCODER_EHIP);
+  *out = v;
+  return VOCODER_OK;
+}
+
+int vocoder_reset(vocoder* v, void* state, int batch, void* stream) {
+  if (!v || !state || batch < 1) return VOCODER_EINVAL;
+  if ((uintptr_t)state & 255) return VOCODER_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  HIP_OK(launch_fill(state, (size_t)batch * v->P.state_floats * 4, s));
+  HIP_OK(launch_reset_headers(state, v->P.state_floats, batch, v->hash, s));
+  return VOCODER_OK;
+}
+
+int vocoder_decode_chunk(vocoder* v, const int32_t* codes, int batch, int n_frames, const void* state_in,
+                         void* state_out, float* pcm, void* stream) {
+  if (!v || !codes || !state_in || !state_out || !pcm) return VOCODER_EINVAL;
+  const Plan& P = v->P;
+  const vocoder_config& c = P.cfg;
+  if (batch < 1 || batch > c.max_batch || n_frames < 1 || n_frames > c.max_frames) return VOCODER_EINVAL;
+  if (((uintptr_t)state_in & 255) || ((uintptr_t)state_out & 255)) return VOCODER_EINVAL;
+  {
+    const char* a = (const char*)state_in;
+    const char* b = (const char*)state_out;
+    const size_t n = (size_t)batch * P.state_floats * 4;
+    if (a < b + n && b < a + n) return VOCODER_EINVAL;
+  }
+  Ctx cx;
+  cx.v = v;
+  cx.s = (hipStream_t)stream;
+  cx.sin_ = (const float*)state_in;
+  cx.sout = (float*)state_out;
+  cx.sstride = P.state_floats;
+  cx.B = batch;
+  cx.T = n_frames;
+  const int B = batch, T = n_frames, d = P.d;
+  const int R = B * T;
+  float* ws = v->ws;
+  const float* pk = v->packed;
+  int* status = reinterpret_cast<int*>(ws + P.ws_status);
+  int* pos = reinterpret_cast<int*>(ws + P.ws_pos);
+  float* rope = ws + P.ws_rope;
+
+  {
+  Prof pr(v, cx.s, "begin", 0, 4.0 * B * (double)T * P.half * 2);
+  HIP_OK(launch_begin(state_in, state_out, cx.sstride, B, T, v->hash,
+                      reinterpret_cast<const double*>(pk + P.inv_freq), P.half, rope, pos, status, cx.s));
+  }
+  {
+  Prof pr(v, cx.s, "state_shift", 0, 0);
+  HIP_OK(launch_state_shift(reinterpret_cast<const Slot*>(pk + P.slots_off), (int)P.slots.size(), 0, cx.sin_,
+                            cx.sout, cx.sstride, B, T, cx.s));
+  }
+
+  // RVQ embedding sum
+  float* emb = ws + P.ws_emb;
+  const Slot& spre = P.slots[P.slot_pre];
+  {
+  Prof pr(v, cx.s, "gather", 0, (double)R * c.n_codebooks * (4.0 + 4.0 * c.embed_dim) + 4.0 * R * c.embed_dim);
+  HIP_OK(launch_gather(codes, pk + P.codebooks, c.n_codebooks, c.codebook_size, c.embed_dim, R, T, emb,
+                       spre.H > 0 ? cx.sout + spre.off : nullptr, spre.H, cx.sstride, status, cx.s));
+  }
+  tap(cx, "embed", emb, (long long)R * c.embed_dim);
+
+  // causal conv before the transformer
+  float* h = ws + P.ws_h;
+  {
+    ConvParams p = base_params(cx, P.pre, emb, R, T, 1, P.slot_pre);
+    add_out(cx, p, h, nullptr, -1);
+    CHECK(run_gemm(cx, p));
+  }
+  tap(cx, "pre_conv", h, (long long)R * d);
+
+  // transformer
+  float* u = ws + P.ws_u;
+  float* qkv = ws + P.ws_qkv;
+  float* att = ws + P.ws_att;
+  float* ffn = ws + P.ws_ffn;
+  for (int l = 0; l < c.n_layers; ++l) {
+    const LayerP& L = P.layers[l];
+    {
+      Prof pr(v, cx.s, "layernorm", 0, 8.0 * R * d);
+      HIP_OK(launch_layernorm(h, pk + L.ln1_g, pk + L.ln1_b, c.ln_eps, R, d, u, T, nullptr, 0, 0, cx.s));
+    }
+    {
+      ConvParams p = base_params(cx, L.qkv, u, R, T, 1, -1);
+      add_out(cx, p, qkv, nullptr, -1);
+      CHECK(run_gemm(cx, p));
+    }
+    const Slot& sk = P.slots[L.slot_k];
+    const Slot& sv = P.slots[L.slot_v];
+    {
+      Prof pr(v, cx.s, "rope_kv", 0, 4.0 * R * d * 4);
+      HIP_OK(launch_rope_kv(qkv, rope, R, T, c.n_heads, P.hd, cx.sout + sk.off, cx.sout + sv.off, c.window,
+                            cx.sstride, cx.s));
+    }
+    {
+      const double keys = (double)c.window + 1;
+      Prof pr(v, cx.s, "attention", 4.0 * R * keys * d, 4.0 * ((double)B * c.window * 2 * d + 3.0 * R * d + R * d));
+      HIP_OK(launch_attention(qkv, cx.sin_ + sk.off, cx.sin_ + sv.off, cx.sstride, pos, B, T, c.n_heads, P.hd,
+                              c.window, att, cx.s));
+    }
+    {
+      ConvParams p = base_params(cx, L.o, att, R, T, 1, -1);
+      p.resid = h;
+      add_out(cx, p, h, nullptr, -1);
+      CHECK(run_gemm(cx, p));
+    }
+    {
+      Prof pr(v, cx.s, "layernorm", 0, 8.0 * R * d);
+      HIP_OK(launch_layernorm(h, pk + L.ln2_g, pk + L.ln2_b, c.ln_eps, R, d, u, T, nullptr, 0, 0, cx.s));
+    }
+    {
+      ConvParams p = base_params(cx, L.fc1, u, R, T, 1, -1);
+      p.act = ACT_GELU;
+      add_out(cx, p, ffn, nullptr, -1);
+      CHECK(run_gemm(cx, p));
+    }
+    {
+      ConvParams p = base_params(cx, L.fc2, ffn, R, T, 1, -1);
+      p.resid = h;
+      add_out(cx, p, h, nullptr, -1);
+      CHECK(run_gemm(cx, p));
+    }
+    char nm[32];
+    snprintf(nm, sizeof(nm), "layer%d", l);
+    tap(cx, nm, h, (long long)R * d);
+  }
+  // final LayerNorm; its last row feeds the first transposed conv's history
+  {
+    const int s0 = c.n_up > 0 ? P.slot_ups[0] : P.slot_conv_pre;
+    const Slot& so = P.slots[s0];
+    Prof pr(v, cx.s, "layernorm", 0, 8.0 * R * d);
+    HIP_OK(launch_layernorm(h, pk + P.fln_g, pk + P.fln_b, c.ln_eps, R, d, u, T, cx.sout + so.off, so.H,
+                            cx.sstride, cx.s));
+  }
+  tap(cx, "final_ln", u, (long long)R * d);
+
+  // 2x2 upsampling: transposed convs as phase-stacked 2-tap GEMMs
+  const float* x = u;
+  long long nin = T;
+  for (int i = 0; i < c.n_up; ++i) {
+    const GemmW& g = P.ups[i];
+    float* y = ws + P.ws_up[i];
+    ConvParams p = base_params(cx, g, x, (int)(B * nin), (int)nin, 1, P.slot_ups[i]);
+    const int next = i + 1 < c.n_up ? P.slot_ups[i + 1] : P.slot_conv_pre;
+    add_out(cx, p, y, nullptr, next);
+    CHECK(run_gemm(cx, p));
+    nin *= g.phases;
+    char nm[32];
+    snprintf(nm, sizeof(nm), "up%d", i);
+    tap(cx, nm, y, B * nin * d);
+    x = y;
+  }
+  // conv_pre into the first stage's input
+  int sbuf = 0;
+  float* S_in = ws + P.ws_S[sbuf];
+  {
+    ConvParams p = base_params(cx, P.conv_pre, x, (int)(B * nin), (int)nin, 1, P.slot_conv_pre);
+    add_out(cx, p, S_in, nullptr, P.stages[0].slot_up);
+    CHECK(run_gemm(cx, p));
+  }
+  tap(cx, "conv_pre", S_in, B * nin * c.voc_ch0);
+
+  // BigVGAN stages
+  float* X0 = ws + P.ws_X0;
+  float* Tb = ws + P.ws_T;
+  float* Xr = ws + P.ws_Xr;
+  float* An = ws + P.ws_An;
+  for (int si = 0; si < c.n_stages; ++si) {
+    const StageP& S = P.stages[si];
+    const bool last_stage = si + 1 == c.n_stages;
+    float* S_out = ws + P.ws_S[sbuf ^ 1];
+    // transposed conv: raw output + the first Snake of every AMP block
+    {
+      ConvParams p = base_params(cx, S.up, S_in, (int)(B * nin), (int)nin, 1, S.slot_up);
+      add_out(cx, p, X0, nullptr, -1);
+      for (int j = 0; j < c.n_res; ++j)
+        add_out(cx, p, ws + P.ws_A[j], pk + S.up_alpha[j], S.amp[(size_t)j * c.n_dil].slot1);
+      CHECK(run_gemm(cx, p));
+    }
+    nin *= S.r;
+    const int rows = (int)(B * nin);
+    {
+      char nm[32];
+      snprintf(nm, sizeof(nm), "stage%d.up", si);
+      tap(cx, nm, X0, (long long)rows * S.c);
+    }
+    for (int j = 0; j < c.n_res; ++j) {
+      const int k = c.res_kernels[j];
+      for (int i = 0; i < c.n_dil; ++i) {
+        const AmpP& A = S.amp[(size_t)j * c.n_dil + i];
+        const float* a_in = i == 0 ? ws + P.ws_A[j] : An;
+        // conv(k, d) of Snake_1(x), then Snake_2
+        {
+          ConvParams p = base_params(cx, A.conv1, a_in, rows, (int)nin, c.dilations[i], A.slot1);
+          add_out(cx, p, Tb, pk + A.act2, A.slot2);
+          CHECK(run_gemm(cx, p));
+        }
+        // conv(k, 1) + residual
+        {
+          ConvParams p = base_params(cx, A.conv2, Tb, rows, (int)nin, 1, A.slot2);
+          p.resid = i == 0 ? X0 : Xr;
+          if (i + 1 < c.n_dil) {
+            const AmpP& An1 = S.amp[(size_t)j * c.n_dil + i + 1];
+            add_out(cx, p, Xr, nullptr, -1);
+            add_out(cx, p, An, pk + An1.act1, An1.slot1);
+          } else {
+            p.mrf = S_out;
+            p.mrf_div = (float)c.n_res;
+            if (c.n_res == 1) p.mrf_mode = MRF_ONLY;
+            else if (j == 0) p.mrf_mode = MRF_FIRST;
+            else if (j + 1 == c.n_res) p.mrf_mode = MRF_LAST;
+            else p.mrf_mode = MRF_ACCUM;
+            const bool fin = p.mrf_mode == MRF_LAST || p.mrf_mode == MRF_ONLY;
+            if (!fin) {
+              add_out(cx, p, S_out, nullptr, -1, 1);
+            } else if (!last_stage) {
+              add_out(cx, p, S_out, nullptr, P.stages[si + 1].slot_up, 1);
+            } else {
+              add_out(cx, p, S_out, pk + P.post_alpha, P.slot_post, 1);
+            }
+          }
+          CHECK(run_gemm(cx, p));
+        }
+        (void)k;
+      }
+    }
+    {
+      char nm[32];
+      snprintf(nm, sizeof(nm), "stage%d", si);
+      tap(cx, nm, S_out, (long long)rows * S.c);
+    }
+    sbuf ^= 1;
+    S_in = S_out;
+  }
+  // final Snake is already applied: conv_post + tanh
+  {
+    const Slot& sp = P.slots[P.slot_post];
+    auto it = v->taps.find("pre_tanh");
+    float* pre = nullptr;
+    const long long rows = B * nin;
+    if (it != v->taps.end() && it->second.first && (size_t)rows <= it->second.second) pre = it->second.first;
+    const double C = P.stages.back().c;
+    Prof pr(v, cx.s, "conv_post", 2.0 * rows * C * c.post_kernel, 4.0 * rows * (C + 1 + (pre ? 1 : 0)));
+    HIP_OK(launch_conv_post(S_in, cx.sin_ + sp.off, cx.sstride, sp.H, pk + P.post_w, pk + P.post_b,
+                            P.stages.back().c, c.post_kernel, (int)rows, (int)nin, pcm, pre, cx.s));
+  }
+  return VOCODER_OK;
+}
+
+int vocoder_profile_begin(vocoder* v) {
+  if (!v) return VOCODER_EINVAL;
+  v->prof = true;
+  v->recs.clear();
+  return VOCODER_OK;
+}
+
+int vocoder_profile_end(vocoder* v, void* stream, vocoder_kernel_stat* out, int max_entries, int* n_entries) {
+  if (!v || max_entries < 0 || (max_entries > 0 && !out)) return VOCODER_EINVAL;
+  v->prof = false;
+  HIP_OK(hipStreamSynchronize((hipStream_t)stream));
+  std::vector<vocoder_kernel_stat> agg(v->prof_names.size());
+  for (size_t i = 0; i < agg.size(); ++i) {
+    memset(&agg[i], 0, sizeof(agg[i]));
+    snprintf(agg[i].name, sizeof(agg[i].name), "%s", v->prof_names[i].c_str());
+  }
+  for (size_t k = 0; k < v->recs.size(); ++k) {
+    float ms = 0.f;
+    HIP_OK(hipEventElapsedTime(&ms, v->events[2 * k], v->events[2 * k + 1]));
+    vocoder_kernel_stat& a = agg[v->recs[k].name];
+    a.launches += 1;
+    a.total_ms += ms;
+    a.flops += v->recs[k].flops;
+    a.bytes += v->recs[k].bytes;
+  }
+  v->recs.clear();
+  int n = 0;
+  for (const auto& a : agg) {
+    if (a.launches == 0) continue;
+    if (n < max_entries) out[n] = a;
+    ++n;
+  }
+  if (n_entries) *n_entries = n;
+  return VOCODER_OK;
+}
+
+int vocoder_hop(const vocoder* v) { return v ? v->P.hop : 0; }
+
+int vocoder_left_context_frames(const vocoder* v) { return v ? v->P.cfg.window : 0; }
+
+int vocoder_get_status(vocoder* v, void* stream) {
+  if (!v) return VOCODER_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  int st = 0;
+  HIP_OK(hipStreamSynchronize(s));
+  HIP_OK(hipMemcpy(&st, v->ws + v->P.ws_status, sizeof(int), hipMemcpyDeviceToHost));
+  HIP_OK(launch_fill(v->ws + v->P.ws_status, 256, s));
+  HIP_OK(hipStreamSynchronize(s));
+  if (st & VOC_STATUS_CODE) return VOCODER_ECODE;
+  if (st & VOC_STATUS_STATE) return VOCODER_ESTATE;
+  return VOCODER_OK;
+}
+
+int vocoder_set_tap(vocoder* v, const char* name, float* dst, size_t dst_floats) {
+  if (!v || !name) return VOCODER_EINVAL;
+  if (!dst) {
+    v->taps.erase(name);
+    return VOCODER_OK;
+  }
+  v->taps[name] = {dst, dst_floats};
+  return VOCODER_OK;
+}
+
+void vocoder_destroy(vocoder* v) { delete v; }
+
+const char* vocoder_strerror(int status) {
+  switch (status) {
+    case VOCODER_OK: return "ok";
+    case VOCODER_EINVAL: return "invalid argument";
+    case VOCODER_ESTATE: return "state does not belong to this decoder";
+    case VOCODER_EHIP: return "HIP error";
+    case VOCODER_ECODE: return "code out of range";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"
