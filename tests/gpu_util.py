@@ -47,6 +47,7 @@ def rel_l2(got, ref):
 def check_close(got, ref, what, rel=REL_L2, max_abs=None):
     r = rel_l2(got, ref)
     msg = f"{what}: rel-L2 {r:.3g}"
+    print("  " + msg, flush=True)
     assert r <= rel, msg
     if max_abs is not None:
         m = float(np.max(np.abs(np.asarray(got, np.float64) - np.asarray(ref, np.float64))))

@@ -18,6 +18,8 @@
 // loop is fixed and never split, so results are bitwise independent of batch,
 // chunking and tile shape.
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace {
@@ -40,9 +42,14 @@ struct TileCfg {
   static_assert(BK % 16 == 0, "BK must be a multiple of 16");
 };
 
+// Snake x + sin^2(a x)/a.  The sine is the hardware instruction (argument in
+// revolutions) applied to the angle reduced to [-1/2, 1/2] revolution: the
+// subtraction of the nearest integer is exact, so the only angle error is the
+// rounding of a*x/(2 pi), the same size as the rounding of a*x itself.
 __device__ __forceinline__ float snake1(float v, float a) {
-  float s = sinf(a * v);
-  return v + (s * s) / a;
+  const float t = (a * v) * 0.159154943091895336f;
+  const float s = __builtin_amdgcn_sinf(t - rintf(t));
+  return v + (s * s) * __builtin_amdgcn_rcpf(a);
 }
 
 __device__ __forceinline__ float gelu1(float v) {
@@ -83,29 +90,37 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_kernel(const ConvParams p) {
   const int ksteps_per_tap = cin / C::BK;
   const int nsteps = p.k * ksteps_per_tap;
 
-  // per-thread load slots
-  int a_row[C::A_LD], a_col[C::A_LD];
-  bool a_ok[C::A_LD];
+  // Per-thread load slots.  Each thread loads the same rows at every K-step;
+  // only a uniform offset (tap shift and channel block) changes, so the row
+  // base pointers are computed once.  A row whose shifted position falls
+  // before the chunk reads the stream's history slot instead: both bases are
+  // kept and selected per step, without branches.  Rows past the end clamp to
+  // the last row (their outputs are never stored).
+  const float* a_base[C::A_LD];
+  int a_lds[C::A_LD];
 #pragma unroll
   for (int i = 0; i < C::A_LD; ++i) {
-    const int idx = tid + i * C::NT;
-    a_ok[i] = (C::A_F4 % C::NT == 0) || idx < C::A_F4;
-    a_row[i] = idx / C::KV;
-    a_col[i] = (idx % C::KV) * 4;
+    int idx = tid + i * C::NT;
+    if (C::A_F4 % C::NT != 0 && idx >= C::A_F4) idx = C::A_F4 - 1;  // duplicate load, same value
+    const int row = idx / C::KV, col = (idx % C::KV) * 4;
+    a_base[i] = p.w + (size_t)(m0 + row) * p.k * cin + col;
+    a_lds[i] = row * C::LDK + col;
   }
-  int b_row[C::B_LD], b_col[C::B_LD], b_g[C::B_LD], b_n[C::B_LD];
-  bool b_ok[C::B_LD];
+  const float* bx[C::B_LD];
+  const float* bh[C::B_LD];
+  int bn[C::B_LD], b_lds[C::B_LD];
 #pragma unroll
   for (int i = 0; i < C::B_LD; ++i) {
-    const int idx = tid + i * C::NT;
-    const bool in_tile = (C::B_F4 % C::NT == 0) || idx < C::B_F4;
-    b_row[i] = idx / C::KV;
-    b_col[i] = (idx % C::KV) * 4;
-    const int g = g0 + b_row[i];
-    b_ok[i] = in_tile && g < p.rows;
-    b_g[i] = g;
-    const int b = b_ok[i] ? g / p.nin : 0;
-    b_n[i] = g - b * p.nin;
+    int idx = tid + i * C::NT;
+    if (C::B_F4 % C::NT != 0 && idx >= C::B_F4) idx = C::B_F4 - 1;
+    const int row = idx / C::KV, col = (idx % C::KV) * 4;
+    const int g = min(g0 + row, p.rows - 1);
+    const int b = g / p.nin;
+    const int n = g - b * p.nin;
+    bn[i] = n;
+    bx[i] = p.x + (size_t)g * cin + col;
+    bh[i] = p.hin ? p.hin + (size_t)b * p.sstride + (ptrdiff_t)(p.hin_rows + n) * cin + col : bx[i];
+    b_lds[i] = row * C::LDK + col;
   }
 
   f32x4 ra[C::A_LD], rb[C::B_LD];
@@ -114,54 +129,19 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_kernel(const ConvParams p) {
     const int tap = s / ksteps_per_tap;
     const int c0 = (s - tap * ksteps_per_tap) * C::BK;
     const int shift = (p.k - 1 - tap) * p.dil;
+    const ptrdiff_t aoff = (ptrdiff_t)tap * cin + c0;
+    const ptrdiff_t boff = c0 - (ptrdiff_t)shift * cin;
 #pragma unroll
-    for (int i = 0; i < C::A_LD; ++i) {
-      if (a_ok[i]) {
-        const size_t off = ((size_t)(m0 + a_row[i]) * p.k + tap) * cin + c0 + a_col[i];
-        ra[i] = ld4(p.w + off);
-      }
-    }
+    for (int i = 0; i < C::A_LD; ++i) ra[i] = ld4(a_base[i] + aoff);
 #pragma unroll
-    for (int i = 0; i < C::B_LD; ++i) {
-      f32x4 v = {0.f, 0.f, 0.f, 0.f};
-      if (b_ok[i]) {
-        const int n2 = b_n[i] - shift;
-        const float* src;
-        if (n2 >= 0) {
-          src = p.x + (size_t)(b_g[i] - shift) * cin;
-        } else {
-          const int b = (b_g[i] - b_n[i]) / p.nin;
-          src = p.hin + (size_t)b * p.sstride + (size_t)(p.hin_rows + n2) * cin;
-        }
-        v = ld4(src + c0 + b_col[i]);
-      }
-      rb[i] = v;
-    }
+    for (int i = 0; i < C::B_LD; ++i) rb[i] = ld4((bn[i] >= shift ? bx[i] : bh[i]) + boff);
   };
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < C::A_LD; ++i)
-      if (a_ok[i]) st4(&As[buf][a_row[i] * C::LDK + a_col[i]], ra[i]);
+    for (int i = 0; i < C::A_LD; ++i) st4(&As[buf][a_lds[i]], ra[i]);
 #pragma unroll
-    for (int i = 0; i < C::B_LD; ++i)
-      if ((C::B_F4 % C::NT == 0) || tid + i * C::NT < C::B_F4)
-        st4(&Bs[buf][b_row[i] * C::LDK + b_col[i]], rb[i]);
+    for (int i = 0; i < C::B_LD; ++i) st4(&Bs[buf][b_lds[i]], rb[i]);
   };
-
-  // Two-level accumulation: the MFMA chain runs into `part` for GROUP_K
-  // reduction values (32 MFMAs at most), then `part` is added to `acc`.  A
-  // single chain over all k*cin values loses about 4x more precision; the
-  // grouping depends only on the K index, so it is the same for every tile.
-  constexpr int GROUP_K = 128;
-  constexpr int GROUP_STEPS = GROUP_K / C::BK;
-  f32x4 acc[C::FM][C::FN], part[C::FM][C::FN];
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j) {
-      acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
-      part[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    }
 
   // MFMA 16x16x4 f32: lane l supplies A[l%16][k] and B[k][l%16] with
   // k = l/16.  Lane group l/16 owns 4 consecutive k of a 16-wide slab, read
@@ -169,12 +149,20 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_kernel(const ConvParams p) {
   const int lr = lane & 15;
   const int lk = (lane >> 4) * 4;
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int s = 0; s < nsteps; ++s) {
-    const int cur = s & 1;
-    if (s + 1 < nsteps) gload(s + 1);
+  // Two-level accumulation: the MFMA chain of one group of GROUP_K reduction
+  // values (32 MFMAs deep at most) starts from zero, and each group's partial
+  // sum is added to `acc`.  A single chain over all k*cin values loses about
+  // 4x more precision; the grouping depends only on the K index, so every
+  // tile shape reduces each output in the same order.
+  constexpr int GROUP_K = 128;
+  constexpr int GROUP_STEPS = GROUP_K / C::BK;
+  f32x4 acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  auto mma_step = [&](int cur, f32x4 (&part)[C::FM][C::FN], auto first) {
     const float* Ab = As[cur];
     const float* Bb = Bs[cur];
 #pragma unroll
@@ -189,20 +177,36 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_kernel(const ConvParams p) {
 #pragma unroll
         for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-          for (int j = 0; j < C::FN; ++j)
-            part[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i][q], bf[j][q], part[i][j], 0, 0, 0);
+          for (int j = 0; j < C::FN; ++j) {
+            if (decltype(first)::value && kk == 0 && q == 0)
+              part[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i][q], bf[j][q], (f32x4){0.f, 0.f, 0.f, 0.f},
+                                                                0, 0, 0);
+            else
+              part[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i][q], bf[j][q], part[i][j], 0, 0, 0);
+          }
     }
-    if ((s + 1) % GROUP_STEPS == 0 || s + 1 == nsteps) {
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j) {
-          acc[i][j] += part[i][j];
-          part[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        }
+  };
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int gs = 0; gs < nsteps; gs += GROUP_STEPS) {
+    const int ge = min(gs + GROUP_STEPS, nsteps);
+    f32x4 part[C::FM][C::FN];
+    for (int s = gs; s < ge; ++s) {
+      const int cur = s & 1;
+      if (s + 1 < nsteps) gload(s + 1);
+      if (s == gs)
+        mma_step(cur, part, std::true_type{});
+      else
+        mma_step(cur, part, std::false_type{});
+      if (s + 1 < nsteps) lstore(cur ^ 1);
+      __syncthreads();
     }
-    if (s + 1 < nsteps) lstore(cur ^ 1);
-    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) acc[i][j] += part[i][j];
   }
 
   // epilogue: lane holds rows m..m+3 (4*(l/16) + r) of column g (l%16)
@@ -275,6 +279,7 @@ int gemm_tile_bm(int tile) {
     case TILE_96x256: return 96;
     case TILE_192x128: return 192;
     case TILE_64x64: return 64;
+    case TILE_96x128: return 96;
   }
   return 0;
 }
@@ -285,6 +290,7 @@ int gemm_tile_bn(int tile) {
     case TILE_96x256: return 256;
     case TILE_192x128: return 128;
     case TILE_64x64: return 64;
+    case TILE_96x128: return 128;
   }
   return 0;
 }
@@ -301,6 +307,8 @@ hipError_t launch_conv_gemm(const ConvParams& p, int tile, hipStream_t s) {
       return bk32 ? launch_cfg<TileCfg<192, 128, 2, 2, 32>>(p, s) : launch_cfg<TileCfg<192, 128, 2, 2, 16>>(p, s);
     case TILE_64x64:
       return bk32 ? launch_cfg<TileCfg<64, 64, 2, 2, 32>>(p, s) : launch_cfg<TileCfg<64, 64, 2, 2, 16>>(p, s);
+    case TILE_96x128:
+      return bk32 ? launch_cfg<TileCfg<96, 128, 1, 4, 32>>(p, s) : launch_cfg<TileCfg<96, 128, 1, 4, 16>>(p, s);
   }
   return hipErrorInvalidValue;
 }

@@ -291,27 +291,50 @@ __global__ __launch_bounds__(ATT_THREADS) void attention_kernel(
 
 // ---------------------------------------------------------------------------
 // Final conv C -> 1 (kernel k, causal, history from the state) and tanh.
-// One thread per output sample; the C-channel rows are read as float4.
+// A block owns POST_ROWS consecutive output samples: it stages those input
+// rows and the k-1 rows before them in LDS with coalesced float4 loads (row
+// stride C+1 so that lanes reading different rows hit different banks), then
+// each thread reduces its own sample in a fixed (tap, channel) order.  Rows
+// before a stream's chunk come from its history slot.
 // ---------------------------------------------------------------------------
-__global__ void conv_post_kernel(const float* __restrict__ x, const float* __restrict__ hin, long long sstride,
-                                 int H, const float* __restrict__ w, const float* __restrict__ bias, int C, int k,
-                                 int rows, int nin, float* __restrict__ pcm, float* __restrict__ pre) {
-  const int g = blockIdx.x * blockDim.x + threadIdx.x;
+constexpr int POST_ROWS = 128;
+
+__global__ __launch_bounds__(POST_ROWS) void conv_post_kernel(
+    const float* __restrict__ x, const float* __restrict__ hin, long long sstride, int H,
+    const float* __restrict__ w, const float* __restrict__ bias, int C, int k, int rows, int nin,
+    float* __restrict__ pcm, float* __restrict__ pre) {
+  extern __shared__ float sm[];
+  const int ld = C + 1;
+  float* ws = sm;                        // [k][C]
+  float* xs = sm + k * C;                // [(POST_ROWS + k - 1)][ld]
+  const int g0 = blockIdx.x * POST_ROWS;
+  const int nr = min(POST_ROWS, rows - g0) + k - 1;
+  for (int i = threadIdx.x; i < k * C; i += POST_ROWS) ws[i] = w[i];
+  const int c4n = C / 4;
+  for (int i = threadIdx.x; i < nr * c4n; i += POST_ROWS) {
+    const int r = i / c4n, c = (i - r * c4n) * 4;
+    const int g = g0 - (k - 1) + r;      // global input row; rows of another stream are staged but unused
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    if (g >= 0) v = ld4(x + (size_t)g * C + c);
+    float* d = xs + r * ld + c;
+    d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+  }
+  __syncthreads();
+  const int t = threadIdx.x;
+  const int g = g0 + t;
   if (g >= rows) return;
   const int b = g / nin, n = g - b * nin;
   float acc = bias[0];
   for (int j = 0; j < k; ++j) {
     const int n2 = n - (k - 1 - j);
-    const float* src = n2 >= 0 ? x + (size_t)(g - (k - 1 - j)) * C
-                               : hin + (size_t)b * sstride + (size_t)(H + n2) * C;
-    const float* wj = w + (size_t)j * C;
+    const float* wj = ws + j * C;
     float dot = 0.f;
-    for (int c = 0; c < C; c += 4) {
-      const f32x4 xv = ld4(src + c), wv = ld4(wj + c);
-      dot = fmaf(wv.x, xv.x, dot);
-      dot = fmaf(wv.y, xv.y, dot);
-      dot = fmaf(wv.z, xv.z, dot);
-      dot = fmaf(wv.w, xv.w, dot);
+    if (n2 >= 0) {
+      const float* xr = xs + (t + j) * ld;
+      for (int c = 0; c < C; ++c) dot = fmaf(wj[c], xr[c], dot);
+    } else {
+      const float* xr = hin + (size_t)b * sstride + (size_t)(H + n2) * C;
+      for (int c = 0; c < C; ++c) dot = fmaf(wj[c], xr[c], dot);
     }
     acc += dot;
   }
@@ -440,8 +463,10 @@ hipError_t launch_attention(const float* qkv, const float* k_state, const float*
 hipError_t launch_conv_post(const float* x, const float* hin, long long sstride, int H, const float* w,
                             const float* bias, int C, int k, int rows, int nin, float* pcm, float* pre_tanh,
                             hipStream_t s) {
-  hipLaunchKernelGGL(conv_post_kernel, dim3(cdiv(rows, 256)), dim3(256), 0, s, x, hin, sstride, H, w, bias, C, k,
-                     rows, nin, pcm, pre_tanh);
+  const size_t smem = ((size_t)k * C + (size_t)(POST_ROWS + k - 1) * (C + 1)) * sizeof(float);
+  if (smem > 64 * 1024) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(conv_post_kernel, dim3(cdiv(rows, POST_ROWS)), dim3(POST_ROWS), smem, s, x, hin, sstride, H, w,
+                     bias, C, k, rows, nin, pcm, pre_tanh);
   return hipGetLastError();
 }
 

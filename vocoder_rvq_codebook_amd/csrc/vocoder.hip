@@ -56,6 +56,11 @@ bool config_valid(const vocoder_config* c) {
   for (int i = 0; i < c->n_dil; ++i)
     if (c->dilations[i] < 1 || c->dilations[i] > 64) return false;
   if (c->post_kernel < 1 || c->post_kernel > 64) return false;
+  {
+    // the final conv stages 128 + post_kernel - 1 rows of the last stage's channels in 64 KB of LDS
+    const long long cl = c->voc_ch0 >> c->n_stages;
+    if ((long long)c->post_kernel * cl + (128LL + c->post_kernel - 1) * (cl + 1) > 16384) return false;
+  }
   if (c->max_batch < 1 || c->max_frames < 1) return false;
   // every GEMM row count must fit in int
   long long hop = 1;
@@ -391,7 +396,7 @@ class Prof {
 
 int pick_tile(int M, long long rows) {
   const long long rt128 = (rows + 127) / 128;
-  if (M % 96 == 0 && M <= 288 && rows >= 4096) return TILE_96x256;
+  if (M % 96 == 0 && M <= 288 && rows >= 4096) return TILE_96x128;
   if (M == 192 && rows >= 4096) return TILE_192x128;
   if ((long long)((M + 127) / 128) * rt128 < 1024) return TILE_64x64;
   return TILE_128x128;
