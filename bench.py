@@ -35,8 +35,84 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="qwen3_b64_chunk25")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-frames", type=int, default=25)
+    ap.add_argument("--cpu-frames", type=int, default=100)
+    # measurement helpers (each replaces the timed run)
+    ap.add_argument("--counters", action="store_true",
+                    help="decode exactly one batched step from fresh states, for rocprofv3 --pmc runs")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="run one device-to-device copy of this many bytes (counter calibration)")
+    ap.add_argument("--trace-summary", default=None,
+                    help="summarise a rocprofv3 --kernel-trace CSV over the last --steps decode calls")
+    ap.add_argument("--traffic-summary", nargs=4, default=None,
+                    metavar=("GEMM_FETCH", "GEMM_WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="turn rocprofv3 --pmc CSVs into profiles/traffic.json")
     return ap.parse_args()
+
+
+def _kernel_family(name):
+    import re
+    m = re.search(r"TileCfg<(\d+), (\d+), \d+, \d+, (\d+)>", name)
+    if m:
+        return f"conv_gemm_{m.group(1)}x{m.group(2)}_bk{m.group(3)}"
+    m = re.search(r"(\w+)\(", name.replace("(anonymous namespace)::", ""))
+    return m.group(1) if m else name[:40]
+
+
+def trace_summary(path, steps):
+    """Per-kernel launches and mean duration over the last `steps` decode calls
+    of a kernel-trace CSV (each decode call starts with begin_kernel)."""
+    import csv
+
+    rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Start_Timestamp"]))
+    starts = [i for i, r in enumerate(rows) if "begin_kernel" in r["Kernel_Name"]]
+    first = starts[-steps]
+    agg = {}
+    for r in rows[first:]:
+        k = _kernel_family(r["Kernel_Name"])
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6
+        a = agg.setdefault(k, [0, 0.0])
+        a[0] += 1
+        a[1] += d
+    print(f"last {steps} decode calls of {path}")
+    print(f"{'kernel':28s} {'launches':>9s} {'total ms':>10s} {'avg ms':>9s}")
+    for k, (n, t) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
+        print(f"{k:28s} {n:9d} {t:10.3f} {t / n:9.4f}")
+
+
+def traffic_summary(gemm_fetch, gemm_write, copy_fetch, copy_write, copy_bytes):
+    """HBM bytes per launch of every conv GEMM family, from FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each scaled so that a plain copy of
+    `copy_bytes` reads and writes exactly that many bytes."""
+    import csv
+
+    def per_kernel(path, counter):
+        out = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            k = _kernel_family(r["Kernel_Name"])
+            out.setdefault(k, []).append(float(r["Counter_Value"]) * 1024.0)
+        return out
+
+    cf = per_kernel(copy_fetch, "FETCH_SIZE")
+    cw = per_kernel(copy_write, "WRITE_SIZE")
+    ck = max(cf, key=lambda k: max(cf[k]))
+    f_scale = copy_bytes / max(cf[ck])
+    w_scale = copy_bytes / max(cw[ck])
+    gf = per_kernel(gemm_fetch, "FETCH_SIZE")
+    gw = per_kernel(gemm_write, "WRITE_SIZE")
+    src = os.path.join(ROOT, "vocoder_rvq_codebook_amd", "csrc", "conv_gemm.hip")
+    rec = {"conv_gemm_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
+           "copy_kernel": ck, "copy_bytes": copy_bytes, "fetch_scale": f_scale, "write_scale": w_scale,
+           "kernels": {}}
+    for k in gf:
+        fb = sum(gf[k]) / len(gf[k]) * f_scale
+        wb = sum(gw.get(k, [0.0])) / max(1, len(gw.get(k, []))) * w_scale
+        rec["kernels"][k] = {"launches": len(gf[k]), "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
+                             "hbm_bytes_per_launch": fb + wb}
+    print(json.dumps(rec, indent=1))
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(rec, f, indent=1)
 
 
 def warm_states(dec, codes, batch, torch):
@@ -104,6 +180,12 @@ def traffic_for(kernel):
 
 def main():
     args = parse()
+    if args.trace_summary:
+        trace_summary(args.trace_summary, args.steps)
+        return
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary, copy_bytes=args.copy_bytes or (1 << 30))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this decoder runs on one GPU: streams are independent and shard across GPUs "
                                    "with no collectives, but only the single-GPU path is built; run with --gpus 1"}))
@@ -112,6 +194,15 @@ def main():
 
     import synthetic as S
     from vocoder_rvq_codebook_amd import Decoder, binding as vb
+
+    if args.copy_bytes:
+        src = torch.ones(args.copy_bytes // 4, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"copied {args.copy_bytes} bytes", flush=True)
+        return
 
     wl = S.workload(args.workload)
     model = wl["model"]
@@ -122,6 +213,12 @@ def main():
     codes = S.workload_codes(args.workload)
     torch.cuda.set_device(0)
     dec = Decoder(model, torch.from_numpy(S.flatten_weights(model, W)), B, T)
+    if args.counters:
+        st_a, st_b = dec.new_state(B), dec.new_state(B)
+        dec.decode(torch.from_numpy(np.ascontiguousarray(codes[:, :T])).cuda(), st_a, st_b)
+        torch.cuda.synchronize()
+        print("decoded one batched step", flush=True)
+        return
     st_a, st_b, warm = warm_states(dec, codes, B, torch)
     chunk = torch.from_numpy(np.stack([codes[b, warm[b]:warm[b] + T] for b in range(B)])).cuda()
     pcm = torch.empty((B, T * dec.hop), device="cuda")
