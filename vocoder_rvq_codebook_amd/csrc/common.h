@@ -83,7 +83,7 @@ struct Slot {
 // ---------------------------------------------------------------------------
 
 // tile configuration ids for the implicit-GEMM kernel
-enum GemmTile { TILE_128x128 = 0, TILE_96x256 = 1, TILE_192x128 = 2, TILE_64x64 = 3, TILE_96x128 = 4, TILE_COUNT = 5 };
+enum GemmTile { TILE_128x128 = 0, TILE_96x256 = 1, TILE_192x128 = 2, TILE_64x64 = 3, TILE_96x128 = 4, TILE_256x128 = 5, TILE_COUNT = 6 };
 int gemm_tile_bm(int tile);
 int gemm_tile_bn(int tile);
 hipError_t launch_conv_gemm(const ConvParams& p, int tile, hipStream_t s);

@@ -280,6 +280,7 @@ int gemm_tile_bm(int tile) {
     case TILE_192x128: return 192;
     case TILE_64x64: return 64;
     case TILE_96x128: return 96;
+    case TILE_256x128: return 256;
   }
   return 0;
 }
@@ -291,6 +292,7 @@ int gemm_tile_bn(int tile) {
     case TILE_192x128: return 128;
     case TILE_64x64: return 64;
     case TILE_96x128: return 128;
+    case TILE_256x128: return 128;
   }
   return 0;
 }
@@ -300,7 +302,10 @@ hipError_t launch_conv_gemm(const ConvParams& p, int tile, hipStream_t s) {
   if (p.cin % 16 != 0) return hipErrorInvalidValue;
   switch (tile) {
     case TILE_128x128:
-      return bk32 ? launch_cfg<TileCfg<128, 128, 2, 2, 32>>(p, s) : launch_cfg<TileCfg<128, 128, 2, 2, 16>>(p, s);
+      // 8 waves of 64x32 with BK = 16: four waves per SIMD (measured 119
+      // TFLOP/s; 4 waves of 64x64 at BK = 32 fit one wave per SIMD and reach
+      // 101).  The reduction order does not depend on BK or the wave layout.
+      return launch_cfg<TileCfg<128, 128, 2, 4, 16>>(p, s);
     case TILE_96x256:
       return bk32 ? launch_cfg<TileCfg<96, 256, 1, 4, 32>>(p, s) : launch_cfg<TileCfg<96, 256, 1, 4, 16>>(p, s);
     case TILE_192x128:
@@ -308,7 +313,10 @@ hipError_t launch_conv_gemm(const ConvParams& p, int tile, hipStream_t s) {
     case TILE_64x64:
       return bk32 ? launch_cfg<TileCfg<64, 64, 2, 2, 32>>(p, s) : launch_cfg<TileCfg<64, 64, 2, 2, 16>>(p, s);
     case TILE_96x128:
-      return bk32 ? launch_cfg<TileCfg<96, 128, 1, 4, 32>>(p, s) : launch_cfg<TileCfg<96, 128, 1, 4, 16>>(p, s);
+      // 8 waves of 48x32: four waves per SIMD
+      return bk32 ? launch_cfg<TileCfg<96, 128, 2, 4, 32>>(p, s) : launch_cfg<TileCfg<96, 128, 2, 4, 16>>(p, s);
+    case TILE_256x128:
+      return bk32 ? launch_cfg<TileCfg<256, 128, 4, 2, 32>>(p, s) : launch_cfg<TileCfg<256, 128, 4, 2, 16>>(p, s);
   }
   return hipErrorInvalidValue;
 }

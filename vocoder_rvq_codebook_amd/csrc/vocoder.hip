@@ -16,7 +16,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/vocoder.h"
+#include "vocoder.h"  // include/, on the compiler include path
 #include "common.h"
 
 namespace {
