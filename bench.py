@@ -160,6 +160,53 @@ def cpu_baseline(model, W, codes_1, frames):
                       f"oracle, {el:.1f} s wall"}
 
 
+def stream_latency(args, wl, torch, S, Decoder, vb):
+    """Streaming latency: decode the workload's chunk schedule for its streams
+    (warm-up passes untimed), timing every chunk call with HIP events on the
+    caller's stream.  Prints one JSON line (not the headline metric)."""
+    model = wl["model"]
+    sched = wl["schedule"]
+    B = wl["batch"]
+    W = S.make_weights(model, wl["weight_seed"])
+    codes = S.workload_codes(args.workload)
+    dec = Decoder(model, torch.from_numpy(S.flatten_weights(model, W)), B, max(sched))
+    chunks, t0 = [], 0
+    for n in sched:
+        chunks.append(torch.from_numpy(np.ascontiguousarray(codes[:, t0:t0 + n])).cuda())
+        t0 += n
+    pcm = [torch.empty((B, n * dec.hop), device="cuda") for n in sched]
+    st_a, st_b = dec.new_state(B), dec.new_state(B)
+    stream = torch.cuda.current_stream()
+    times = []
+    for rep in range(args.warmup + args.steps):
+        dec.reset(st_a)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(sched) + 1)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for i, n in enumerate(sched):
+            dec.decode(chunks[i], st_a, st_b, pcm[i])
+            st_a, st_b = st_b, st_a
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        if rep >= args.warmup:
+            times.append([ev[i].elapsed_time(ev[i + 1]) for i in range(len(sched))])
+    if dec.status() != vb.VOCODER_OK:
+        raise SystemExit("device reported an error")
+    t = np.array(times)  # [reps][chunks] ms
+    per_chunk = np.median(t, axis=0)
+    total = t.sum(axis=1)
+    audio = sum(sched) * FRAME_SECONDS * B
+    out = {"metric": "streaming chunk latency (ms) and audio-seconds/sec", "workload": args.workload,
+           "streams": B, "schedule": sched, "reps": args.steps,
+           "first_chunk_ms": round(float(per_chunk[0]), 3),
+           "chunk_ms_median_by_length": {str(n): round(float(np.median(t[:, [i for i, m in enumerate(sched) if m == n]])), 3)
+                                         for n in sorted(set(sched))},
+           "total_ms_median": round(float(np.median(total)), 3),
+           "audio_s_per_s": round(audio / (float(np.median(total)) / 1e3), 2),
+           "dtype": "f32", "data": "synthetic"}
+    print(json.dumps(out), flush=True)
+
+
 def traffic_for(kernel):
     """HBM bytes per launch of `kernel` from the committed counter summary, if it
     was taken on the current kernel source; else None."""
@@ -206,8 +253,11 @@ def main():
 
     wl = S.workload(args.workload)
     model = wl["model"]
+    if isinstance(wl["schedule"], list):
+        stream_latency(args, wl, torch, S, Decoder, vb)
+        return
     if wl["schedule"] != "warm_then_25":
-        raise SystemExit("bench.py times the batched 25-frame workload")
+        raise SystemExit("bench.py times the batched 25-frame workload or a chunk schedule")
     B, T = wl["batch"], wl["frames"]
     W = S.make_weights(model, wl["weight_seed"])
     codes = S.workload_codes(args.workload)

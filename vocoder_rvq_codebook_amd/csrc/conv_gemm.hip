@@ -24,9 +24,11 @@
 
 namespace {
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_>
+// IGLP_: the compiler's MFMA/LDS interleaving strategy for the K-step body
+// (__builtin_amdgcn_iglp_opt), or -1 for none; chosen per tile by measurement.
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int IGLP_ = -1>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, BK = BK_;
+  static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, BK = BK_, IGLP = IGLP_;
   static constexpr int NT = WAVES_M * WAVES_N * 64;
   static constexpr int WTM = BM / WAVES_M;
   static constexpr int WTN = BN / WAVES_N;
@@ -150,11 +152,11 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_kernel(const ConvParams p) {
   const int lk = (lane >> 4) * 4;
 
   // Two-level accumulation: the MFMA chain of one group of GROUP_K reduction
-  // values (32 MFMAs deep at most) starts from zero, and each group's partial
+  // values (64 MFMAs deep at most) starts from zero, and each group's partial
   // sum is added to `acc`.  A single chain over all k*cin values loses about
   // 4x more precision; the grouping depends only on the K index, so every
   // tile shape reduces each output in the same order.
-  constexpr int GROUP_K = 128;
+  constexpr int GROUP_K = 256;
   constexpr int GROUP_STEPS = GROUP_K / C::BK;
   f32x4 acc[C::FM][C::FN];
 #pragma unroll
@@ -163,6 +165,7 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_kernel(const ConvParams p) {
     for (int j = 0; j < C::FN; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
   auto mma_step = [&](int cur, f32x4 (&part)[C::FM][C::FN], auto first) {
+    if constexpr (C::IGLP >= 0) __builtin_amdgcn_iglp_opt(C::IGLP);
     const float* Ab = As[cur];
     const float* Bb = Bs[cur];
 #pragma unroll
@@ -305,7 +308,7 @@ hipError_t launch_conv_gemm(const ConvParams& p, int tile, hipStream_t s) {
       // 8 waves of 64x32 with BK = 16: four waves per SIMD (measured 119
       // TFLOP/s; 4 waves of 64x64 at BK = 32 fit one wave per SIMD and reach
       // 101).  The reduction order does not depend on BK or the wave layout.
-      return launch_cfg<TileCfg<128, 128, 2, 4, 16>>(p, s);
+      return launch_cfg<TileCfg<128, 128, 2, 4, 16, 1>>(p, s);
     case TILE_96x256:
       return bk32 ? launch_cfg<TileCfg<96, 256, 1, 4, 32>>(p, s) : launch_cfg<TileCfg<96, 256, 1, 4, 16>>(p, s);
     case TILE_192x128:
@@ -314,7 +317,7 @@ hipError_t launch_conv_gemm(const ConvParams& p, int tile, hipStream_t s) {
       return bk32 ? launch_cfg<TileCfg<64, 64, 2, 2, 32>>(p, s) : launch_cfg<TileCfg<64, 64, 2, 2, 16>>(p, s);
     case TILE_96x128:
       // 8 waves of 48x32: four waves per SIMD
-      return bk32 ? launch_cfg<TileCfg<96, 128, 2, 4, 32>>(p, s) : launch_cfg<TileCfg<96, 128, 2, 4, 16>>(p, s);
+      return bk32 ? launch_cfg<TileCfg<96, 128, 2, 4, 32, 0>>(p, s) : launch_cfg<TileCfg<96, 128, 2, 4, 16, 0>>(p, s);
     case TILE_256x128:
       return bk32 ? launch_cfg<TileCfg<256, 128, 4, 2, 32>>(p, s) : launch_cfg<TileCfg<256, 128, 4, 2, 16>>(p, s);
   }
