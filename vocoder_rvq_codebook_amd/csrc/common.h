@@ -45,7 +45,14 @@ struct ConvParams {
   float* mrf;           // running MRF sum [rows_out][cout] (read in ACCUM/LAST)
   int nout;
   EpiOut out[4];
+  // split-K: splits > 1 stores per-group partials to `partial`
+  // ([ceil(k*cin/256)][rows][M] floats), folded by a second kernel
+  int splits;
+  float* partial;
 };
+
+// reduction values per split-K group (and per accumulation group)
+#define VOC_GROUP_K 256
 
 // ---------------------------------------------------------------------------
 // state layout
@@ -86,6 +93,7 @@ struct Slot {
 enum GemmTile { TILE_128x128 = 0, TILE_96x256 = 1, TILE_192x128 = 2, TILE_64x64 = 3, TILE_96x128 = 4, TILE_256x128 = 5, TILE_COUNT = 6 };
 int gemm_tile_bm(int tile);
 int gemm_tile_bn(int tile);
+int gemm_tile_bk(int tile, int cin);
 hipError_t launch_conv_gemm(const ConvParams& p, int tile, hipStream_t s);
 
 hipError_t launch_begin(const void* state_in, void* state_out, long long sstride, int batch, int T,

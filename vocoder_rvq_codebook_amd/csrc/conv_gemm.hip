@@ -61,7 +61,62 @@ __device__ __forceinline__ float gelu1(float v) {
 __device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 __device__ __forceinline__ void st4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
 
-template <class C>
+// Epilogue of output rows m..m+3 (GEMM columns) of GEMM row g, given the
+// reduced sum `acc`: bias, activation, residual, multi-receptive-field mean,
+// then up to four stores, each optionally through Snake and each optionally
+// also written to the stream's state tail.  Shared by the GEMM and the
+// split-K reduction, so both give the same bits.
+__device__ __forceinline__ void epilogue4(const ConvParams& p, int m, int g, f32x4 acc) {
+  const int nout_rows = p.nin * p.phases;
+  const int ph = m / p.cout;
+  const int c = m - ph * p.cout;
+  f32x4 v = acc + ld4(p.bias + m);
+  if (p.act == ACT_GELU) {
+    v.x = gelu1(v.x); v.y = gelu1(v.y); v.z = gelu1(v.z); v.w = gelu1(v.w);
+  }
+  const size_t orow = (size_t)g * p.phases + ph;
+  const size_t oidx = orow * p.cout + c;
+  if (p.resid) v = v + ld4(p.resid + oidx);
+  f32x4 sm = v;
+  if (p.mrf_mode == MRF_FIRST) {
+    sm = v;
+  } else if (p.mrf_mode == MRF_ACCUM) {
+    sm = ld4(p.mrf + oidx) + v;
+  } else if (p.mrf_mode == MRF_LAST) {
+    sm = (ld4(p.mrf + oidx) + v) / p.mrf_div;
+  } else if (p.mrf_mode == MRF_ONLY) {
+    sm = v / p.mrf_div;
+  }
+  const int b = g / p.nin;
+  const int no = (g - b * p.nin) * p.phases + ph;
+#pragma unroll
+  for (int o = 0; o < 4; ++o) {
+    if (o >= p.nout) break;
+    const EpiOut& eo = p.out[o];
+    f32x4 val = eo.src ? sm : v;
+    if (eo.alpha) {
+      const f32x4 a = ld4(eo.alpha + m);
+      val.x = snake1(val.x, a.x); val.y = snake1(val.y, a.y);
+      val.z = snake1(val.z, a.z); val.w = snake1(val.w, a.w);
+    }
+    if (eo.dst) st4(eo.dst + oidx, val);
+    if (eo.hist && no >= nout_rows - eo.H) {
+      st4(eo.hist + (size_t)b * p.sstride + (size_t)(eo.H - nout_rows + no) * p.cout + c, val);
+    }
+  }
+}
+
+// Reduction values per accumulation group (see the two-level accumulation
+// below); split-K splits only at group boundaries.
+constexpr int GROUP_K = VOC_GROUP_K;
+
+// SPLIT = false: one block computes a whole output tile and runs the epilogue.
+// SPLIT = true: blocks are (tile, split) pairs; a split owns a contiguous,
+// non-empty range of accumulation groups and stores each group's partial sum,
+// unreduced, to p.partial[group][row][M]; splitk_reduce_kernel then folds the
+// groups in order and runs the same epilogue.  Every group's partial is the
+// same MFMA chain in both modes, so both modes give the same bits.
+template <class C, bool SPLIT>
 __global__ __launch_bounds__(C::NT) void conv_gemm_kernel(const ConvParams p) {
   __shared__ __attribute__((aligned(16))) float As[2][C::BM * C::LDK];
   __shared__ __attribute__((aligned(16))) float Bs[2][C::BN * C::LDK];
@@ -83,6 +138,11 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_kernel(const ConvParams p) {
     const int per = nb >> 3, extra = nb & 7;
     tile_id = xcd * per + (xcd < extra ? xcd : extra) + i;
   }
+  int split = 0;
+  if (SPLIT) {
+    split = tile_id % p.splits;
+    tile_id /= p.splits;
+  }
   const int mt = tile_id % mtiles;
   const int nt = tile_id / mtiles;
   const int m0 = mt * C::BM;
@@ -90,7 +150,17 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_kernel(const ConvParams p) {
 
   const int cin = p.cin;
   const int ksteps_per_tap = cin / C::BK;
-  const int nsteps = p.k * ksteps_per_tap;
+  const int nsteps_all = p.k * ksteps_per_tap;
+  constexpr int GROUP_STEPS = GROUP_K / C::BK;
+  // K-steps [s_begin, nsteps) of this block: all of them, or one split's groups
+  int s_begin = 0, nsteps = nsteps_all;
+  if (SPLIT) {
+    const int ngroups = (nsteps_all + GROUP_STEPS - 1) / GROUP_STEPS;
+    const int gps = (ngroups + p.splits - 1) / p.splits;
+    s_begin = min(split * gps, ngroups) * GROUP_STEPS;
+    nsteps = min(min((split + 1) * gps, ngroups) * GROUP_STEPS, nsteps_all);
+    if (s_begin >= nsteps) return;
+  }
 
   // Per-thread load slots.  Each thread loads the same rows at every K-step;
   // only a uniform offset (tap shift and channel block) changes, so the row
@@ -156,8 +226,6 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_kernel(const ConvParams p) {
   // sum is added to `acc`.  A single chain over all k*cin values loses about
   // 4x more precision; the grouping depends only on the K index, so every
   // tile shape reduces each output in the same order.
-  constexpr int GROUP_K = 256;
-  constexpr int GROUP_STEPS = GROUP_K / C::BK;
   f32x4 acc[C::FM][C::FN];
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
@@ -190,10 +258,10 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_kernel(const ConvParams p) {
     }
   };
 
-  gload(0);
-  lstore(0);
+  gload(s_begin);
+  lstore(s_begin & 1);
   __syncthreads();
-  for (int gs = 0; gs < nsteps; gs += GROUP_STEPS) {
+  for (int gs = s_begin; gs < nsteps; gs += GROUP_STEPS) {
     const int ge = min(gs + GROUP_STEPS, nsteps);
     f32x4 part[C::FM][C::FN];
     for (int s = gs; s < ge; ++s) {
@@ -206,71 +274,78 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_kernel(const ConvParams p) {
       if (s + 1 < nsteps) lstore(cur ^ 1);
       __syncthreads();
     }
+    if (SPLIT) {
+      // store this group's partial sums: partial[group][g][m]
+      const size_t gbase = (size_t)(gs / GROUP_STEPS) * p.rows;
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i)
+      for (int i = 0; i < C::FM; ++i) {
+        const int m = m0 + wm * C::WTM + i * 16 + (lane >> 4) * 4;
+        if (m >= p.M) continue;
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j) acc[i][j] += part[i][j];
+        for (int j = 0; j < C::FN; ++j) {
+          const int g = g0 + wn * C::WTN + j * 16 + lr;
+          if (g < p.rows) st4(p.partial + (gbase + g) * p.M + m, part[i][j]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) acc[i][j] += part[i][j];
+    }
   }
+  if (SPLIT) return;
 
   // epilogue: lane holds rows m..m+3 (4*(l/16) + r) of column g (l%16)
-  const int nout_rows = p.nin * p.phases;
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) {
     const int m = m0 + wm * C::WTM + i * 16 + (lane >> 4) * 4;
     if (m >= p.M) continue;
-    const f32x4 bias = ld4(p.bias + m);
-    const int ph = m / p.cout;
-    const int c = m - ph * p.cout;
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) {
       const int g = g0 + wn * C::WTN + j * 16 + lr;
-      if (g >= p.rows) continue;
-      f32x4 v = acc[i][j] + bias;
-      if (p.act == ACT_GELU) {
-        v.x = gelu1(v.x); v.y = gelu1(v.y); v.z = gelu1(v.z); v.w = gelu1(v.w);
-      }
-      const size_t orow = (size_t)g * p.phases + ph;
-      const size_t oidx = orow * p.cout + c;
-      if (p.resid) v = v + ld4(p.resid + oidx);
-      f32x4 sm = v;
-      if (p.mrf_mode == MRF_FIRST) {
-        sm = v;
-      } else if (p.mrf_mode == MRF_ACCUM) {
-        sm = ld4(p.mrf + oidx) + v;
-      } else if (p.mrf_mode == MRF_LAST) {
-        sm = (ld4(p.mrf + oidx) + v) / p.mrf_div;
-      } else if (p.mrf_mode == MRF_ONLY) {
-        sm = v / p.mrf_div;
-      }
-      const int b = g / p.nin;
-      const int no = (g - b * p.nin) * p.phases + ph;
-#pragma unroll
-      for (int o = 0; o < 4; ++o) {
-        if (o >= p.nout) break;
-        const EpiOut& eo = p.out[o];
-        f32x4 val = eo.src ? sm : v;
-        if (eo.alpha) {
-          const f32x4 a = ld4(eo.alpha + m);
-          val.x = snake1(val.x, a.x); val.y = snake1(val.y, a.y);
-          val.z = snake1(val.z, a.z); val.w = snake1(val.w, a.w);
-        }
-        if (eo.dst) st4(eo.dst + oidx, val);
-        if (eo.hist && no >= nout_rows - eo.H) {
-          st4(eo.hist + (size_t)b * p.sstride + (size_t)(eo.H - nout_rows + no) * p.cout + c, val);
-        }
-      }
+      if (g < p.rows) epilogue4(p, m, g, acc[i][j]);
     }
   }
+}
+
+// Fold the split-K group partials of one output element (4 consecutive M)
+// in group order, starting from zero as the unsplit loop does, then run the
+// epilogue.  A separate launch: the kernel boundary makes every partial
+// visible, which on a multi-XCD GPU is far cheaper than device-scope fences
+// in the GEMM blocks.
+__global__ void splitk_reduce_kernel(const ConvParams p, int ngroups) {
+  const int M4 = p.M / 4;
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (long long)p.rows * M4) return;
+  const int g = (int)(idx / M4);
+  const int m = (int)(idx - (long long)g * M4) * 4;
+  const size_t stride = (size_t)p.rows * p.M;
+  const float* src = p.partial + (size_t)g * p.M + m;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < ngroups; ++j) acc += ld4(src + j * stride);
+  epilogue4(p, m, g, acc);
 }
 
 template <class C>
 hipError_t launch_cfg(const ConvParams& p, hipStream_t s) {
   const int mtiles = (p.M + C::BM - 1) / C::BM;
   const int ntiles = (p.rows + C::BN - 1) / C::BN;
-  const long long nb = (long long)mtiles * ntiles;
-  if (nb <= 0) return hipSuccess;
-  if (nb > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(conv_gemm_kernel<C>, dim3((unsigned)nb), dim3(C::NT), 0, s, p);
+  const long long tiles = (long long)mtiles * ntiles;
+  if (tiles <= 0) return hipSuccess;
+  if (p.splits <= 1) {
+    if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((conv_gemm_kernel<C, false>), dim3((unsigned)tiles), dim3(C::NT), 0, s, p);
+    return hipGetLastError();
+  }
+  const long long nb = tiles * p.splits;
+  if (nb > 0x7fffffffLL || !p.partial) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((conv_gemm_kernel<C, true>), dim3((unsigned)nb), dim3(C::NT), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int ngroups = (p.k * p.cin + GROUP_K - 1) / GROUP_K;
+  const long long n = (long long)p.rows * (p.M / 4);
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, ngroups);
   return hipGetLastError();
 }
 
@@ -299,6 +374,8 @@ int gemm_tile_bn(int tile) {
   }
   return 0;
 }
+
+int gemm_tile_bk(int tile, int cin) { return tile == TILE_128x128 || cin % 32 != 0 ? 16 : 32; }
 
 hipError_t launch_conv_gemm(const ConvParams& p, int tile, hipStream_t s) {
   const bool bk32 = (p.cin % 32) == 0;

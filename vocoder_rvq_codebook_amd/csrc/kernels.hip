@@ -67,18 +67,22 @@ __global__ void begin_kernel(const float* __restrict__ sin_, float* __restrict__
 // is written by the kernel that produces the new rows).  The slot's alignment
 // padding is zeroed, so every byte of the new state is defined.
 // ---------------------------------------------------------------------------
+// grid: (slot, stream, part); the parts split each slot's copy evenly.
 __global__ void state_shift_kernel(const Slot* __restrict__ slots, const float* __restrict__ sin_,
                                    float* __restrict__ sout, long long sstride, int T) {
   const Slot sl = slots[blockIdx.x];
   const int b = blockIdx.y;
   float* dst = sout + (size_t)b * sstride + sl.off;
   const long long used = (long long)sl.H * sl.C;
-  for (long long i = used + threadIdx.x; i < sl.cap; i += blockDim.x) dst[i] = 0.f;
+  if (blockIdx.z == 0)
+    for (long long i = used + threadIdx.x; i < sl.cap; i += blockDim.x) dst[i] = 0.f;
   const long long N = (long long)T * sl.rate;
   if (N >= sl.H) return;
-  const long long keep = (long long)(sl.H - N) * sl.C;
+  const long long keep = (long long)(sl.H - N) * sl.C;  // a multiple of 4 (C is)
   const float* src = sin_ + (size_t)b * sstride + sl.off + N * sl.C;
-  for (long long i = threadIdx.x; i < keep; i += blockDim.x) dst[i] = src[i];
+  const long long per = (keep / 4 + gridDim.z - 1) / gridDim.z;
+  const long long i0 = per * blockIdx.z, i1 = min(keep / 4, i0 + per);
+  for (long long i = i0 + threadIdx.x; i < i1; i += blockDim.x) st4(dst + 4 * i, ld4(src + 4 * i));
 }
 
 // ---------------------------------------------------------------------------
@@ -421,7 +425,7 @@ hipError_t launch_state_shift(const Slot* slots, int nslots, int max_h, const fl
                               long long sstride, int batch, int T, hipStream_t s) {
   (void)max_h;
   if (nslots == 0) return hipSuccess;
-  hipLaunchKernelGGL(state_shift_kernel, dim3(nslots, batch), dim3(256), 0, s, slots, state_in, state_out,
+  hipLaunchKernelGGL(state_shift_kernel, dim3(nslots, batch, 16), dim3(256), 0, s, slots, state_in, state_out,
                      sstride, T);
   return hipGetLastError();
 }

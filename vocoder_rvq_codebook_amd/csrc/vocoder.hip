@@ -155,6 +155,7 @@ struct Plan {
             ws_ffn = 0;
   std::vector<long long> ws_up;
   long long ws_X0 = 0, ws_T = 0, ws_Xr = 0, ws_An = 0, ws_S[2] = {0, 0};
+  long long ws_partial = 0, partial_floats = 0;  // split-K group partials
   std::vector<long long> ws_A;
   long long ws_floats = 0;
 };
@@ -325,6 +326,10 @@ bool make_plan(const vocoder_config* cp, Plan& P) {
   P.ws_An = Wk(big);
   P.ws_S[0] = Wk(big);
   P.ws_S[1] = Wk(big);
+  // split-K partials: used only by launches with few output tiles, which are
+  // small; 32 M floats (128 MB) bounds the split factor of the rest
+  P.partial_floats = 32LL << 20;
+  P.ws_partial = Wk(P.partial_floats);
   P.ws_floats = ws;
   return true;
 }
@@ -394,11 +399,12 @@ class Prof {
   long long idx_ = -1;
 };
 
+// Tile per GEMM shape: 64x64 up to 2048 rows (transformer linears, the first
+// stages of short chunks), 96x128 when M is 96, 192 or 288 (BigVGAN stages
+// 3-4), 128x128 otherwise.  Launches with few tiles are split along K.
 int pick_tile(int M, long long rows) {
-  const long long rt128 = (rows + 127) / 128;
-  if (M % 96 == 0 && M <= 288 && rows >= 4096) return TILE_96x128;
-  if (M == 192 && rows >= 4096) return TILE_192x128;
-  if ((long long)((M + 127) / 128) * rt128 < 1024) return TILE_64x64;
+  if (rows <= 2048) return TILE_64x64;
+  if (M % 96 == 0 && M <= 288) return TILE_96x128;
   return TILE_128x128;
 }
 
@@ -435,6 +441,8 @@ ConvParams base_params(const Ctx& cx, const GemmW& g, const float* x, int rows, 
   p.mrf_mode = MRF_NONE;
   p.mrf_div = 1.f;
   p.nout = 0;
+  p.splits = 1;
+  p.partial = nullptr;
   return p;
 }
 
@@ -452,12 +460,29 @@ void add_out(const Ctx& cx, ConvParams& p, float* dst, const float* alpha, int h
   }
 }
 
-int run_gemm(const Ctx& cx, const ConvParams& p) {
+// Split a launch along K (at accumulation-group boundaries) when it has too
+// few output tiles to fill the GPU: up to ~1024 blocks, if the group partials
+// fit the workspace.  The result is bitwise the same either way.
+int pick_splits(const Plan& P, int tile, int M, long long rows, int k, int cin) {
+  const long long tiles = (long long)((M + gemm_tile_bm(tile) - 1) / gemm_tile_bm(tile)) *
+                          ((rows + gemm_tile_bn(tile) - 1) / gemm_tile_bn(tile));
+  const long long ngroups = ((long long)k * cin + VOC_GROUP_K - 1) / VOC_GROUP_K;
+  if (tiles >= 256 || ngroups < 2) return 1;
+  if (ngroups * rows * M > P.partial_floats) return 1;
+  long long splits = std::min<long long>(ngroups, (1024 + tiles - 1) / tiles);
+  // every split owns at least one group
+  const long long gps = (ngroups + splits - 1) / splits;
+  splits = (ngroups + gps - 1) / gps;
+  return (int)std::max<long long>(splits, 1);
+}
+
+int run_gemm(const Ctx& cx, const ConvParams& pin) {
+  ConvParams p = pin;
   const int tile = pick_tile(p.M, p.rows);
   const int bm = gemm_tile_bm(tile);
   const int mt = (p.M + bm - 1) / bm;
-  const GemmW* dummy = nullptr;
-  (void)dummy;
+  p.splits = pick_splits(cx.v->P, tile, p.M, p.rows, p.k, p.cin);
+  p.partial = p.splits > 1 ? cx.v->ws + cx.v->P.ws_partial : nullptr;
   // A-tile rows read must lie inside the packed (zero-padded) weight rows
   if ((long long)mt * bm > round_up_i(p.M, 128)) return VOCODER_EINVAL;
   if (p.hin_rows < (p.k - 1) * p.dil) return VOCODER_EINVAL;
@@ -467,7 +492,8 @@ int run_gemm(const Ctx& cx, const ConvParams& p) {
   if (p.resid) bytes += 4.0 * p.rows * p.M;
   if (p.mrf_mode == MRF_ACCUM || p.mrf_mode == MRF_LAST) bytes += 4.0 * p.rows * p.M;
   char name[48];
-  snprintf(name, sizeof(name), "conv_gemm_%dx%d_bk%d", bm, gemm_tile_bn(tile), p.cin % 32 == 0 ? 32 : 16);
+  snprintf(name, sizeof(name), "conv_gemm_%dx%d_bk%d%s", bm, gemm_tile_bn(tile), gemm_tile_bk(tile, p.cin),
+           p.splits > 1 ? "_splitk" : "");
   Prof pr(cx.v, cx.s, name, flops, bytes);
   HIP_OK(launch_conv_gemm(p, tile, cx.s));
   return VOCODER_OK;
