@@ -51,9 +51,10 @@ def parse():
 
 def _kernel_family(name):
     import re
-    m = re.search(r"TileCfg<(\d+), (\d+), \d+, \d+, (\d+)>", name)
+    m = re.search(r"TileCfg<(\d+), (\d+), \d+, \d+, (\d+)(?:, -?\d+)?\s*>(?:, (true|false))?", name)
     if m:
-        return f"conv_gemm_{m.group(1)}x{m.group(2)}_bk{m.group(3)}"
+        split = "_splitk" if m.group(4) == "true" else ""
+        return f"conv_gemm_{m.group(1)}x{m.group(2)}_bk{m.group(3)}{split}"
     m = re.search(r"(\w+)\(", name.replace("(anonymous namespace)::", ""))
     return m.group(1) if m else name[:40]
 
