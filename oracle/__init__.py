@@ -18,6 +18,8 @@ from .decoder import (  # noqa: F401
     layer_norm,
     new_state,
     rope_rotate,
+    round_operand,
+    cast_operand_weights,
     rvq_embed_sum,
     snake,
     transformer_layer,

@@ -187,6 +187,28 @@ def linear(x, w, b):
     return x @ w.T + b
 
 
+def round_operand(a, operands):
+    """Round a contraction operand to the operand format, keeping its dtype.
+
+    operands=None leaves `a` unchanged; operands="f16" rounds every element to
+    the nearest IEEE binary16 value (ties to even), the format the pages allow
+    for the decoder at most ("Edge TTS design", section 1.5: quality row).
+    Products and sums stay in the working dtype.
+    """
+    if operands is None:
+        return a
+    if operands != "f16":
+        raise ValueError(f"unknown operand format {operands!r}")
+    return np.asarray(a).astype(np.float16).astype(np.asarray(a).dtype)
+
+
+# Contraction weights that the fp16-operand mode rounds: every conv, transposed
+# conv and linear weight except the final C -> 1 conv (not a matrix product).
+def _is_contraction_weight(name):
+    return name.endswith(".weight") and not (
+        ".ln" in name or name.startswith("final_ln") or name.startswith("conv_post"))
+
+
 # ---------------------------------------------------------------------------
 # decoder
 # ---------------------------------------------------------------------------
@@ -229,21 +251,23 @@ def cast_weights(weights, dtype):
     return {k: np.asarray(v).astype(dtype, copy=False) for k, v in weights.items()}
 
 
-def transformer_layer(h, W, l, cache, positions, cfg):
+def transformer_layer(h, W, l, cache, positions, cfg, operands=None):
     """One pre-norm layer: windowed self-attention with RoPE, then a GELU FFN.
 
     h [T][d] at absolute positions `positions`; cache = (k, v) of earlier
     frames.  Returns (h_out, new_cache) where new_cache keeps the last
-    `window` frames.
+    `window` frames.  operands="f16" rounds the inputs of the four linear
+    products (their weights are expected already rounded).
     """
+    r = lambda a: round_operand(a, operands)  # noqa: E731
     p = f"layers.{l}."
     T, d = h.shape
     H, hd, Wn = cfg["n_heads"], cfg["head_dim"], cfg["window"]
     eps = cfg["ln_eps"]
     u = layer_norm(h, W[p + "ln1.weight"], W[p + "ln1.bias"], eps)
-    q = linear(u, W[p + "q_proj.weight"], W[p + "q_proj.bias"]).reshape(T, H, hd)
-    k = linear(u, W[p + "k_proj.weight"], W[p + "k_proj.bias"]).reshape(T, H, hd)
-    v = linear(u, W[p + "v_proj.weight"], W[p + "v_proj.bias"]).reshape(T, H, hd)
+    q = linear(r(u), W[p + "q_proj.weight"], W[p + "q_proj.bias"]).reshape(T, H, hd)
+    k = linear(r(u), W[p + "k_proj.weight"], W[p + "k_proj.bias"]).reshape(T, H, hd)
+    v = linear(r(u), W[p + "v_proj.weight"], W[p + "v_proj.bias"]).reshape(T, H, hd)
     q = rope_rotate(q, positions, cfg["rope_theta"])
     k = rope_rotate(k, positions, cfg["rope_theta"])
     kc, vc = cache
@@ -252,21 +276,35 @@ def transformer_layer(h, W, l, cache, positions, cfg):
     p0 = int(positions[0])
     kpos = np.arange(p0 - kc.shape[0], p0 + T)
     o = window_attention(q, K, V, positions, kpos, Wn).reshape(T, d)
-    h = h + linear(o, W[p + "o_proj.weight"], W[p + "o_proj.bias"])
+    h = h + linear(r(o), W[p + "o_proj.weight"], W[p + "o_proj.bias"])
     u = layer_norm(h, W[p + "ln2.weight"], W[p + "ln2.bias"], eps)
-    f = gelu(linear(u, W[p + "fc1.weight"], W[p + "fc1.bias"]))
-    h = h + linear(f, W[p + "fc2.weight"], W[p + "fc2.bias"])
+    f = gelu(linear(r(u), W[p + "fc1.weight"], W[p + "fc1.bias"]))
+    h = h + linear(r(f), W[p + "fc2.weight"], W[p + "fc2.bias"])
     keep = min(Wn, K.shape[0])
     return h, (K[K.shape[0] - keep:].copy(), V[V.shape[0] - keep:].copy())
 
 
-def decode_chunk(cfg, weights, codes, state: OracleState, dtype=np.float64, taps=None):
+def cast_operand_weights(weights, dtype, operands):
+    """Weights in `dtype`, with every contraction weight rounded to the operand format."""
+    W = cast_weights(weights, dtype)
+    if operands is None:
+        return W
+    return {k: (round_operand(v, operands) if _is_contraction_weight(k) else v) for k, v in W.items()}
+
+
+def decode_chunk(cfg, weights, codes, state: OracleState, dtype=np.float64, taps=None, operands=None):
     """Decode one chunk of T frames of one stream; returns (pcm [T*hop], state).
 
     `state` is updated in place and returned.  `taps`, if a dict, receives each
     stage's output (channels-last) for stage-by-stage comparison.
+    operands="f16": every matrix product (convs, transposed convs, linears; not
+    the final C -> 1 conv) takes fp16-rounded operands -- weights, inputs and
+    history rows -- and sums the exact products in `dtype`; everything else
+    (embedding sum, LayerNorm, attention, GELU, Snake, residuals, biases) stays
+    in `dtype`.
     """
-    W = cast_weights(weights, dtype)
+    W = cast_operand_weights(weights, dtype, operands)
+    r = lambda a: round_operand(a, operands)  # noqa: E731
     codes = np.asarray(codes)
     T = codes.shape[0]
 
@@ -277,31 +315,31 @@ def decode_chunk(cfg, weights, codes, state: OracleState, dtype=np.float64, taps
     e = rvq_embed_sum(W["codebooks"], codes)
     tap("embed", e)
     h, state.hist["pre_conv"] = causal_conv1d(
-        e, W["pre_conv.weight"], W["pre_conv.bias"], 1,
-        _get_hist(state, "pre_conv", cfg["pre_kernel"] - 1, cfg["embed_dim"], dtype))
+        r(e), W["pre_conv.weight"], W["pre_conv.bias"], 1,
+        r(_get_hist(state, "pre_conv", cfg["pre_kernel"] - 1, cfg["embed_dim"], dtype)))
     tap("pre_conv", h)
     positions = state.pos + np.arange(T)
     for l in range(cfg["n_layers"]):
-        h, state.kv[l] = transformer_layer(h, W, l, state.kv[l], positions, cfg)
+        h, state.kv[l] = transformer_layer(h, W, l, state.kv[l], positions, cfg, operands)
         tap(f"layer{l}", h)
     x = layer_norm(h, W["final_ln.weight"], W["final_ln.bias"], cfg["ln_eps"])
     tap("final_ln", x)
     d = cfg["model_dim"]
     for i, s in enumerate(cfg["up_strides"]):
         x, state.hist[f"ups.{i}"] = conv_transpose1d_causal(
-            x, W[f"ups.{i}.weight"], W[f"ups.{i}.bias"], s, _get_hist(state, f"ups.{i}", 1, d, dtype))
+            r(x), W[f"ups.{i}.weight"], W[f"ups.{i}.bias"], s, r(_get_hist(state, f"ups.{i}", 1, d, dtype)))
         tap(f"up{i}", x)
     x, state.hist["conv_pre"] = causal_conv1d(
-        x, W["conv_pre.weight"], W["conv_pre.bias"], 1,
-        _get_hist(state, "conv_pre", cfg["conv_pre_kernel"] - 1, d, dtype))
+        r(x), W["conv_pre.weight"], W["conv_pre.bias"], 1,
+        r(_get_hist(state, "conv_pre", cfg["conv_pre_kernel"] - 1, d, dtype)))
     tap("conv_pre", x)
     chans = cfg["stage_channels"]
     n_res = len(cfg["res_kernels"])
-    for si, r in enumerate(cfg["rates"]):
+    for si, rate in enumerate(cfg["rates"]):
         p = f"stages.{si}."
         cin, c = chans[si], chans[si + 1]
         x, state.hist[p + "up"] = conv_transpose1d_causal(
-            x, W[p + "up.weight"], W[p + "up.bias"], r, _get_hist(state, p + "up", 1, cin, dtype))
+            r(x), W[p + "up.weight"], W[p + "up.bias"], rate, r(_get_hist(state, p + "up", 1, cin, dtype)))
         tap(f"stage{si}.up", x)
         acc = None
         for j, k in enumerate(cfg["res_kernels"]):
@@ -310,12 +348,12 @@ def decode_chunk(cfg, weights, codes, state: OracleState, dtype=np.float64, taps
                 q = p + f"blocks.{j}.{i}."
                 a = snake(y, W[q + "act1.alpha"])
                 t, state.hist[q + "conv1"] = causal_conv1d(
-                    a, W[q + "conv1.weight"], W[q + "conv1.bias"], dil,
-                    _get_hist(state, q + "conv1", (k - 1) * dil, c, dtype))
+                    r(a), W[q + "conv1.weight"], W[q + "conv1.bias"], dil,
+                    r(_get_hist(state, q + "conv1", (k - 1) * dil, c, dtype)))
                 bb = snake(t, W[q + "act2.alpha"])
                 uo, state.hist[q + "conv2"] = causal_conv1d(
-                    bb, W[q + "conv2.weight"], W[q + "conv2.bias"], 1,
-                    _get_hist(state, q + "conv2", k - 1, c, dtype))
+                    r(bb), W[q + "conv2.weight"], W[q + "conv2.bias"], 1,
+                    r(_get_hist(state, q + "conv2", k - 1, c, dtype)))
                 y = y + uo
             acc = y if acc is None else acc + y
         x = acc / n_res
@@ -331,19 +369,19 @@ def decode_chunk(cfg, weights, codes, state: OracleState, dtype=np.float64, taps
     return pcm, state
 
 
-def decode_whole(cfg, weights, codes, dtype=np.float64, taps=None):
+def decode_whole(cfg, weights, codes, dtype=np.float64, taps=None, operands=None):
     """Decode a whole sequence of one stream from a fresh state."""
-    pcm, _ = decode_chunk(cfg, weights, codes, new_state(cfg, dtype), dtype, taps)
+    pcm, _ = decode_chunk(cfg, weights, codes, new_state(cfg, dtype), dtype, taps, operands)
     return pcm
 
 
-def decode_schedule(cfg, weights, codes, schedule, dtype=np.float64, state=None):
+def decode_schedule(cfg, weights, codes, schedule, dtype=np.float64, state=None, operands=None):
     """Decode one stream chunk by chunk (chunk lengths in `schedule`), concatenating the PCM."""
-    W = cast_weights(weights, dtype)
+    W = cast_operand_weights(weights, dtype, operands)
     st = new_state(cfg, dtype) if state is None else state
     out, t0 = [], 0
     for n in schedule:
-        pcm, st = decode_chunk(cfg, W, codes[t0:t0 + n], st, dtype)
+        pcm, st = decode_chunk(cfg, W, codes[t0:t0 + n], st, dtype, operands=operands)
         out.append(pcm)
         t0 += n
     return np.concatenate(out), st

@@ -106,3 +106,14 @@ def test_float32_mode_close_to_float64(tiny):
     assert got.dtype == np.float32
     rel = np.linalg.norm(got - whole) / np.linalg.norm(whole)
     assert rel < 1e-5
+
+
+@pytest.mark.parametrize("schedule", [[1] * 12 + [28], [13, 27]])
+def test_f16_operand_mode_streamed_equals_whole(mini, schedule):
+    cfg, W, codes, whole = mini
+    whole16 = O.decode_whole(cfg, W, codes, operands="f16")
+    got, _ = O.decode_schedule(cfg, W, codes, schedule, operands="f16")
+    np.testing.assert_allclose(got, whole16, rtol=0, atol=1e-12)
+    # the rounding is applied and moves the result, but only by fp16-operand error
+    rel = np.linalg.norm(whole16 - whole) / np.linalg.norm(whole)
+    assert 1e-6 < rel < 5e-2

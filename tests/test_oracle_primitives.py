@@ -340,3 +340,36 @@ def test_transformer_layer_matches_torch_composition():
     assert kc.shape[0] == cfg["window"]
     np.testing.assert_allclose(kc, k.numpy()[-cfg["window"]:], rtol=0, atol=1e-12)
     np.testing.assert_allclose(vc, v.numpy()[-cfg["window"]:], rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# fp16-operand mode: rounding of contraction operands
+# ---------------------------------------------------------------------------
+
+
+def test_round_operand_matches_ieee_half():
+    x = np.concatenate([RNG.standard_normal(10000) * 50, RNG.standard_normal(1000) * 1e-5,
+                        [0.0, -0.0, 1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11, 65504.0, 6.1e-5, 2049.0, 2051.0]])
+    # float32-representable inputs: torch converts float64 -> float16 through
+    # float32, which is a single rounding only for such values
+    x = x.astype(np.float32).astype(np.float64)
+    ref = torch.from_numpy(x).to(torch.float16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.round_operand(x, "f16"), ref)
+    # ties go to even: 1 + 2^-11 is halfway between 1 and 1 + 2^-10
+    assert O.round_operand(np.array([1.0 + 2.0 ** -11]), "f16")[0] == 1.0
+    assert O.round_operand(np.array([1.0 + 3 * 2.0 ** -11]), "f16")[0] == 1.0 + 2 * 2.0 ** -10
+    assert O.round_operand(x, None) is x
+    with pytest.raises(ValueError):
+        O.round_operand(x, "bf16")
+
+
+def test_operand_rounding_covers_exactly_the_contraction_weights():
+    import synthetic as S
+    W = S.make_weights(S.MINI, 2)
+    Wr = O.cast_operand_weights(W, np.float64, "f16")
+    for name, v in W.items():
+        rounded = not np.array_equal(Wr[name], v.astype(np.float64))
+        is_gemm = name.endswith(".weight") and ("conv" in name or "proj" in name or "fc" in name
+                                                or name.startswith("ups.") or name.endswith("up.weight"))
+        is_gemm = is_gemm and not name.startswith("conv_post")
+        assert rounded == is_gemm, name
