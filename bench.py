@@ -1,6 +1,6 @@
 """Throughput of the streaming code2wav decoder on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--precision f32|f16] [--no-cpu-baseline]
 
 A step decodes one 25-frame chunk (2 s of audio) for each of 64 independent
 streams whose states were first warmed (untimed) to different positions: the
@@ -24,6 +24,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix peak
+FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak (no sparsity)
 HBM_PEAK_GBS = 8000.0
 FRAME_SECONDS = 0.08  # 12.5 Hz frames
 
@@ -36,6 +37,8 @@ def parse():
     ap.add_argument("--workload", default="qwen3_b64_chunk25")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-frames", type=int, default=100)
+    ap.add_argument("--precision", choices=["f32", "f16"], default="f32",
+                    help="matrix-product operands: f32, or fp16 with fp32 sums (the half-precision decoder)")
     # measurement helpers (each replaces the timed run)
     ap.add_argument("--counters", action="store_true",
                     help="decode exactly one batched step from fresh states, for rocprofv3 --pmc runs")
@@ -51,10 +54,11 @@ def parse():
 
 def _kernel_family(name):
     import re
-    m = re.search(r"TileCfg<(\d+), (\d+), \d+, \d+, (\d+)(?:, -?\d+)?\s*>(?:, (true|false))?", name)
+    m = re.search(r"TileCfg(H?)<(\d+), (\d+), \d+, \d+, (\d+)(?:, -?\d+)*\s*>(?:, (true|false))?", name)
     if m:
-        split = "_splitk" if m.group(4) == "true" else ""
-        return f"conv_gemm_{m.group(1)}x{m.group(2)}_bk{m.group(3)}{split}"
+        half = "f16_" if m.group(1) else ""
+        split = "_splitk" if m.group(5) == "true" else ""
+        return f"conv_gemm_{half}{m.group(2)}x{m.group(3)}_bk{m.group(4)}{split}"
     m = re.search(r"(\w+)\(", name.replace("(anonymous namespace)::", ""))
     return m.group(1) if m else name[:40]
 
@@ -165,7 +169,7 @@ def stream_latency(args, wl, torch, S, Decoder, vb):
     """Streaming latency: decode the workload's chunk schedule for its streams
     (warm-up passes untimed), timing every chunk call with HIP events on the
     caller's stream.  Prints one JSON line (not the headline metric)."""
-    model = wl["model"]
+    model = dict(wl["model"], precision=args.precision)
     sched = wl["schedule"]
     B = wl["batch"]
     W = S.make_weights(model, wl["weight_seed"])
@@ -204,7 +208,7 @@ def stream_latency(args, wl, torch, S, Decoder, vb):
                                          for n in sorted(set(sched))},
            "total_ms_median": round(float(np.median(total)), 3),
            "audio_s_per_s": round(audio / (float(np.median(total)) / 1e3), 2),
-           "dtype": "f32", "data": "synthetic"}
+           "dtype": args.precision, "data": "synthetic"}
     print(json.dumps(out), flush=True)
 
 
@@ -253,7 +257,8 @@ def main():
         return
 
     wl = S.workload(args.workload)
-    model = wl["model"]
+    model = dict(wl["model"], precision=args.precision)
+    peak = FP16_MFMA_PEAK_TFLOPS if args.precision == "f16" else FP32_MFMA_PEAK_TFLOPS
     if isinstance(wl["schedule"], list):
         stream_latency(args, wl, torch, S, Decoder, vb)
         return
@@ -309,7 +314,9 @@ def main():
                for k, v in sorted(prof.items(), key=lambda kv: -kv[1]["total_ms"])}
 
     out = {
-        "metric": "audio-seconds/sec (x real-time) for 64 x 25-frame chunks; % fp32 MFMA peak",
+        "metric": "audio-seconds/sec (x real-time) for 64 x 25-frame chunks; % fp32 MFMA peak"
+                  if args.precision == "f32" else
+                  "audio-seconds/sec (x real-time) for 64 x 25-frame chunks, fp16 operands; % fp16 MFMA peak",
         "value": round(value, 3),
         "unit": "audio-s/s",
         "n_gpus": 1,
@@ -319,15 +326,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": args.precision,
         "data": "synthetic (seeded random-init weights, uniform random codes)",
         "config": {"workload": args.workload, "streams": B, "frames_per_chunk": T,
                    "samples_per_frame": dec.hop, "warm_positions": sorted(set(warm))},
         "tflops": round(flops_step / (elapsed / args.steps) / 1e12, 3),
-        "mfma_frac": round(flops_step / (elapsed / args.steps) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4),
+        "mfma_frac": round(flops_step / (elapsed / args.steps) / 1e12 / peak, 4),
         "roofline": {"kernel": dom_name, "bound": "mfma", "achieved": round(dom_tflops, 3),
-                     "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(dom_tflops / FP32_MFMA_PEAK_TFLOPS, 4),
+                     "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(dom_tflops / peak, 4),
                      "avg_launch_ms": round(dom_ms, 4), "traffic": traffic_for(dom_name)},
         "kernels": kernels,
     }

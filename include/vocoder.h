@@ -81,7 +81,21 @@ typedef struct vocoder_config {
   int32_t post_kernel;      /* final conv kernel, C -> 1 (7) */
   int32_t max_batch;        /* largest batch a decode call may pass (sizes the workspace) */
   int32_t max_frames;       /* largest n_frames a decode call may pass (sizes the workspace) */
+  int32_t precision;        /* VOCODER_PRECISION_F32 (0) or VOCODER_PRECISION_F16 (1), see below */
 } vocoder_config;
+
+/* Arithmetic of the matrix products (every conv, transposed conv and linear
+ * except the final C -> 1 conv).  F32: fp32 operands, fp32 MFMA.  F16: both
+ * operands rounded to IEEE binary16 (ties to even) -- weights when packed,
+ * activations as they are read -- and products summed in fp32 on the fp16
+ * MFMA; everything else (embedding sum, LayerNorm, attention, GELU, Snake,
+ * residuals, biases, the final conv, all stored activations and the state)
+ * stays fp32.  The edge design page (section 1.5, quality row) allows the
+ * decoder fp16 at most; activations must stay within fp16 range (|x| < 65504).
+ * The precision is part of the state's identity: states are not
+ * interchangeable between the two. */
+#define VOCODER_PRECISION_F32 0
+#define VOCODER_PRECISION_F16 1
 
 typedef struct vocoder vocoder;
 

@@ -8,7 +8,8 @@ frames at the start and end), together with the norms of the full outputs.
     python tests/golden/make_golden.py [name ...]
 
 Names: qwen3_whole (the 250-frame whole-sequence workload, stream 0, which the
-streamed workload must also reproduce), qwen3_batched (streams 0-3 of the
+streamed workload must also reproduce), qwen3_whole_f16 (the same with every
+matrix product's operands rounded to fp16, the half-precision decoder), qwen3_batched (streams 0-3 of the
 64-stream workload: their timed 25-frame chunk after warm-up), qwen3_longform
 (stream 0 of the 16 x 1500-frame Zipf workload).
 """
@@ -32,14 +33,14 @@ def sample_index(n_samples, hop, stride):
     return np.array(sorted(idx), dtype=np.int64)
 
 
-def decode_stream(cfg, W, codes, chunk):
+def decode_stream(cfg, W, codes, chunk, operands=None):
     """Whole-sequence decode of one stream, evaluated in pieces of `chunk`
     frames to bound memory (streamed == whole is pinned by the oracle tests)."""
     st = O.new_state(cfg)
     pcm, pre = [], []
     for t0 in range(0, codes.shape[0], chunk):
         taps = {}
-        p, st = O.decode_chunk(cfg, W, codes[t0:t0 + chunk], st, np.float64, taps)
+        p, st = O.decode_chunk(cfg, W, codes[t0:t0 + chunk], st, np.float64, taps, operands)
         pcm.append(p)
         pre.append(taps["pre_tanh"])
         print(f"    frames {t0 + codes[t0:t0 + chunk].shape[0]}/{codes.shape[0]}", flush=True)
@@ -55,7 +56,16 @@ def main(names):
             W = O.cast_weights(S.make_weights(cfg, 1), np.float64)
         hop = cfg["hop"]
         out = {}
-        if name == "qwen3_whole":
+        if name == "qwen3_whole_f16":
+            # the fp16-operand decoder (matrix-product operands rounded to fp16)
+            codes = S.workload_codes("qwen3_b1_t250_whole")
+            W16 = O.cast_operand_weights(W, np.float64, "f16")
+            pcm, pre = decode_stream(cfg, W16, codes[0], 125, operands="f16")
+            idx = sample_index(pcm.size, hop, 61)
+            out.update(stream=np.array([0]), frame0=np.array([0]), frames=np.array([250]), idx=idx,
+                       pcm=pcm[idx], pre=pre[idx], pcm_norm=np.array([np.linalg.norm(pcm)]),
+                       pre_norm=np.array([np.linalg.norm(pre)]))
+        elif name == "qwen3_whole":
             codes = S.workload_codes("qwen3_b1_t250_whole")
             pcm, pre = decode_stream(cfg, W, codes[0], 125)
             idx = sample_index(pcm.size, hop, 61)

@@ -71,16 +71,17 @@ def run_schedule(dec, codes, schedule, state=None):
     return pcm, st_a
 
 
-def oracle_stream(model, W, codes_1, schedule=None, taps=None):
-    """float64 oracle of one stream; with `taps`, the taps of the last chunk."""
+def oracle_stream(model, W, codes_1, schedule=None, taps=None, operands=None):
+    """float64 oracle of one stream; with `taps`, the taps of the last chunk.
+    operands="f16" evaluates the fp16-operand decoder."""
     if schedule is None:
         schedule = [codes_1.shape[0]]
     st = O.new_state(model)
-    Wd = O.cast_weights(W, np.float64)
+    Wd = O.cast_operand_weights(W, np.float64, operands)
     out, t0 = [], 0
     for i, n in enumerate(schedule):
         tp = taps if i == len(schedule) - 1 else None
-        p, st = O.decode_chunk(model, Wd, codes_1[t0:t0 + n], st, np.float64, tp)
+        p, st = O.decode_chunk(model, Wd, codes_1[t0:t0 + n], st, np.float64, tp, operands)
         out.append(p)
         t0 += n
     return np.concatenate(out)

@@ -33,8 +33,8 @@ def test_library_exports_every_declared_function():
 
 
 def test_config_struct_matches_header_layout():
-    # 8 int32 + 2 float + 2 int32 + 4 + 3 int32 + 8 + 1 + 4 + 1 + 4 + 3 int32
-    assert ctypes.sizeof(vb.VocoderConfig) == 4 * (8 + 2 + 2 + 4 + 3 + 8 + 1 + 4 + 1 + 4 + 3)
+    # 8 int32 + 2 float + 2 int32 + 4 + 3 int32 + 8 + 1 + 4 + 1 + 4 + 4 int32
+    assert ctypes.sizeof(vb.VocoderConfig) == 4 * (8 + 2 + 2 + 4 + 3 + 8 + 1 + 4 + 1 + 4 + 4)
 
 
 @pytest.mark.parametrize("model", [S.TINY, S.MINI, S.QWEN3], ids=lambda m: m["name"])
@@ -97,3 +97,19 @@ def test_flat_weights_follow_manifest():
         n = int(np.prod(shape))
         np.testing.assert_array_equal(flat[off:off + n], W[name].ravel())
         off += n
+
+
+def test_f16_precision_halves_gemm_weight_bytes():
+    f32 = vb.make_config(S.QWEN3, 1, 1)
+    f16 = vb.make_config(dict(S.QWEN3, precision="f16"), 1, 1)
+    assert f16.precision == 1 and f32.precision == 0
+    assert vb.vocoder_raw_weights_count(f16) == vb.vocoder_raw_weights_count(f32)
+    assert vb.vocoder_state_bytes(f16) == vb.vocoder_state_bytes(f32)
+    b32, b16 = vb.vocoder_packed_weights_bytes(f32), vb.vocoder_packed_weights_bytes(f16)
+    # everything but the codebooks (67 MB) and the vectors halves
+    assert 0.5 * b32 < b16 < 0.6 * b32
+    bad = vb.make_config(S.QWEN3, 1, 1)
+    bad.precision = 2
+    assert vb.vocoder_packed_weights_bytes(bad) == 0
+    with pytest.raises(ValueError):
+        vb.make_config(dict(S.QWEN3, precision="bf16"), 1, 1)

@@ -1,0 +1,97 @@
+"""GPU parity of the fp16-operand decoder (precision = f16): every matrix
+product takes fp16-rounded operands and sums in fp32 on the fp16 MFMA.
+
+Reference: the oracle's fp16-operand mode (the same roundings, exact float64
+sums).  The two differ by fp32 summation and by the operands whose fp32 (GPU)
+and float64 (oracle) values round to neighbouring fp16 values; both are far
+below the difference to the unrounded decoder, which the tests also bound.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synthetic as S
+from oracle import decoder as O
+from tests.gpu_util import check_close, decoder, oracle_stream, run_schedule
+from tests.test_gpu_parity import _stage_names, _tap_rows
+from vocoder_rvq_codebook_amd import binding as vb
+
+pytestmark = pytest.mark.gpu
+
+# GPU fp16 decoder vs the oracle's fp16-operand mode (stage taps, pre-tanh, PCM)
+F16_VS_F16_ORACLE = 2e-3
+# fp16-operand decoder vs the unrounded float64 decoder: fp16 operand rounding
+# itself (CPU emulation of the 250-frame Qwen3-shaped decode: PCM 2.4e-2,
+# pre-tanh 1.2e-2)
+F16_VS_F64_PCM = 6e-2
+F16_VS_F64_PRE = 3e-2
+
+
+def half(model):
+    return dict(model, name=model["name"] + "_f16", precision="f16")
+
+
+@pytest.mark.parametrize("base,T", [(S.MINI, 13), (S.MINI, 1), (S.TINY, 32)], ids=["mini13", "mini1", "tiny32"])
+def test_f16_stage_by_stage(base, T):
+    model = half(base)
+    B = 2
+    dec, W = decoder(model, 5, B, 32)
+    warm = [0, 9]
+    codes = S.make_codes(model, B, max(warm) + T, 78)
+    states = dec.new_state(B)
+    for b, nw in enumerate(warm):
+        if nw:
+            _, st2 = run_schedule(dec, codes[b:b + 1, :nw], [nw], state=states[b:b + 1].clone())
+            states[b:b + 1].copy_(st2)
+    chunk = np.stack([codes[b, nw:nw + T] for b, nw in enumerate(warm)])
+    taps = {}
+    for name in _stage_names(model):
+        rows, ch = _tap_rows(model, name, T)
+        taps[name] = torch.full((B * rows * ch,), float("nan"), device="cuda")
+        dec.set_tap(name, taps[name])
+    pcm, _ = run_schedule(dec, chunk, [T], state=states)
+    assert dec.status() == vb.VOCODER_OK
+    last = len(model["rates"]) - 1
+    for b, nw in enumerate(warm):
+        ref_taps, ref64_taps = {}, {}
+        sched = [nw, T] if nw else [T]
+        ref = oracle_stream(model, W, codes[b, : nw + T], sched, taps=ref_taps, operands="f16")
+        ref64 = oracle_stream(model, W, codes[b, : nw + T], sched, taps=ref64_taps)
+        for name in _stage_names(model):
+            rows, ch = _tap_rows(model, name, T)
+            got = taps[name].view(B, rows * ch)[b].cpu().numpy()
+            r = ref_taps[name]
+            if name == f"stage{last}":
+                r = O.snake(r, W["act_post.alpha"].astype(np.float64))
+            if name == "embed":  # the gather is not a matrix product: still exact fp32
+                np.testing.assert_array_equal(got, O.rvq_embed_sum(W["codebooks"], chunk[b]).reshape(-1))
+            else:
+                check_close(got, r.reshape(-1), f"f16 stream {b} {name}", rel=F16_VS_F16_ORACLE)
+        got = pcm[b].cpu().numpy()
+        check_close(got, ref[nw * model["hop"]:], f"f16 stream {b} pcm", rel=F16_VS_F16_ORACLE)
+        check_close(got, ref64[nw * model["hop"]:], f"f16 stream {b} pcm vs float64 decoder", rel=F16_VS_F64_PCM)
+    for name in taps:
+        dec.set_tap(name, None)
+
+
+@pytest.mark.parametrize("schedule", [[1] * 5 + [7, 13, 1, 14], [20, 21]])
+def test_f16_streamed_equals_whole_bitwise(schedule):
+    model = half(S.MINI)
+    T = sum(schedule)
+    dec, _ = decoder(model, 9, 2, 41)
+    codes = S.make_codes(model, 2, T, 32)
+    whole, st_w = run_schedule(dec, codes, [T])
+    parts, st_p = run_schedule(dec, codes, schedule)
+    assert torch.equal(whole, parts)
+    assert torch.equal(st_w, st_p)
+
+
+def test_f16_state_is_not_an_f32_state():
+    f32, _ = decoder(S.MINI, 9, 1, 8)
+    f16, _ = decoder(half(S.MINI), 9, 1, 8)
+    codes = S.make_codes(S.MINI, 1, 8, 5)
+    st32 = f32.new_state(1)
+    fresh, _ = run_schedule(f16, codes, [8])
+    got, _ = run_schedule(f16, codes, [8], state=st32)
+    assert f16.status() == vb.VOCODER_ESTATE
+    assert torch.equal(got, fresh)

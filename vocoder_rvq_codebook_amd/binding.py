@@ -50,7 +50,11 @@ class VocoderConfig(ctypes.Structure):
         ("post_kernel", ctypes.c_int32),
         ("max_batch", ctypes.c_int32),
         ("max_frames", ctypes.c_int32),
+        ("precision", ctypes.c_int32),
     ]
+
+
+PRECISIONS = {"f32": 0, "f16": 1}
 
 
 class VocoderKernelStat(ctypes.Structure):
@@ -129,6 +133,10 @@ def make_config(model: dict, max_batch: int, max_frames: int) -> VocoderConfig:
             arr[i] = int(v)
     c.max_batch = int(max_batch)
     c.max_frames = int(max_frames)
+    prec = model.get("precision", "f32")
+    if prec not in PRECISIONS:
+        raise ValueError(f"precision must be one of {sorted(PRECISIONS)}")
+    c.precision = PRECISIONS[prec]
     return c
 
 

@@ -95,6 +95,9 @@ int gemm_tile_bm(int tile);
 int gemm_tile_bn(int tile);
 int gemm_tile_bk(int tile, int cin);
 hipError_t launch_conv_gemm(const ConvParams& p, int tile, hipStream_t s);
+// fp16-operand GEMM: p.w points at fp16 weights [Mpad][k][cin]; tiles 128x128, 96x128, 64x64
+hipError_t launch_conv_gemm_f16(const ConvParams& p, int tile, hipStream_t s);
+int gemm_f16_bk(int cin);
 
 hipError_t launch_begin(const void* state_in, void* state_out, long long sstride, int batch, int T,
                         uint64_t cfg_hash, const double* inv_freq, int half, float* rope_tab, int* pos,
@@ -114,10 +117,10 @@ hipError_t launch_attention(const float* qkv, const float* k_state, const float*
 hipError_t launch_conv_post(const float* x, const float* hin, long long sstride, int H, const float* w,
                             const float* bias, int C, int k, int rows, int nin, float* pcm,
                             float* pre_tanh, hipStream_t s);
-hipError_t launch_repack_conv(const float* src, float* dst, int M, int Mpad, int cin, int k,
+hipError_t launch_repack_conv(const float* src, void* dst, int M, int Mpad, int cin, int k, bool half_out,
                               hipStream_t s);
-hipError_t launch_repack_convT(const float* src, float* dst, int cin, int cout, int stride, int Mpad,
-                               hipStream_t s);
+hipError_t launch_repack_convT(const float* src, void* dst, int cin, int cout, int stride, int Mpad,
+                               bool half_out, hipStream_t s);
 hipError_t launch_expand_vec(const float* src, float* dst, int C, int phases, int Mpad, hipStream_t s);
 hipError_t launch_fill(void* dst, size_t bytes, hipStream_t s);
 hipError_t launch_reset_headers(void* state, long long sstride, int batch, uint64_t cfg_hash,

@@ -327,7 +327,246 @@ __global__ void splitk_reduce_kernel(const ConvParams p, int ngroups) {
   epilogue4(p, m, g, acc);
 }
 
-template <class C>
+// ---------------------------------------------------------------------------
+// fp16-operand variant: the same implicit GEMM with both operands rounded to
+// IEEE binary16 (ties to even) and products summed in fp32 by the fp16 MFMA.
+// Weights are packed as fp16; activation rows stay fp32 in memory and are
+// rounded as they are staged into LDS.  SLAB is the MFMA's K: 32 halves
+// (v_mfma_f32_16x16x32_f16, 8 per lane) or 16 (v_mfma_f32_16x16x16f16, 4 per
+// lane) for channel counts that are multiples of 16 only.  A K-step covers BK
+// halves; the accumulation groups (GROUP_K values) and split-K are as above.
+// ---------------------------------------------------------------------------
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int SLAB_, int IGLP_ = -1>
+struct TileCfgH {
+  static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, BK = BK_, SLAB = SLAB_,
+                       IGLP = IGLP_;
+  static constexpr int NT = WAVES_M * WAVES_N * 64;
+  static constexpr int WTM = BM / WAVES_M;
+  static constexpr int WTN = BN / WAVES_N;
+  static constexpr int FM = WTM / 16;
+  static constexpr int FN = WTN / 16;
+  static constexpr int LDK = BK + 8;      // halves; 16-byte pad per row
+  static constexpr int KC = BK / 8;       // 16-byte chunks (8 halves) per row per K-step
+  static constexpr int A_CH = BM * KC;
+  static constexpr int B_CH = BN * KC;
+  static constexpr int A_LD = (A_CH + NT - 1) / NT;
+  static constexpr int B_LD = (B_CH + NT - 1) / NT;
+  static constexpr int PER_LANE = SLAB / 4;  // halves per lane per MFMA
+  static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be a multiple of 16");
+  static_assert((SLAB == 32 || SLAB == 16) && BK % SLAB == 0 && BK % 8 == 0, "bad K-step");
+};
+
+__device__ __forceinline__ f16x8 to_half8(f32x4 lo, f32x4 hi) {
+  f16x8 r;
+  r[0] = (_Float16)lo.x; r[1] = (_Float16)lo.y; r[2] = (_Float16)lo.z; r[3] = (_Float16)lo.w;
+  r[4] = (_Float16)hi.x; r[5] = (_Float16)hi.y; r[6] = (_Float16)hi.z; r[7] = (_Float16)hi.w;
+  return r;
+}
+
+template <class C, bool SPLIT>
+__global__ __launch_bounds__(C::NT) void conv_gemm_f16_kernel(const ConvParams p) {
+  __shared__ __attribute__((aligned(16))) _Float16 As[2][C::BM * C::LDK];
+  __shared__ __attribute__((aligned(16))) _Float16 Bs[2][C::BN * C::LDK];
+  const _Float16* W = reinterpret_cast<const _Float16*>(p.w);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave % C::WAVES_M;
+  const int wn = wave / C::WAVES_M;
+
+  const int mtiles = (p.M + C::BM - 1) / C::BM;
+  int tile_id;
+  {
+    const int L = blockIdx.x, nb = gridDim.x;
+    const int xcd = L & 7, i = L >> 3;
+    const int per = nb >> 3, extra = nb & 7;
+    tile_id = xcd * per + (xcd < extra ? xcd : extra) + i;
+  }
+  int split = 0;
+  if (SPLIT) {
+    split = tile_id % p.splits;
+    tile_id /= p.splits;
+  }
+  const int mt = tile_id % mtiles;
+  const int nt = tile_id / mtiles;
+  const int m0 = mt * C::BM;
+  const int g0 = nt * C::BN;
+
+  const int cin = p.cin;
+  const int ksteps_per_tap = cin / C::BK;
+  const int nsteps_all = p.k * ksteps_per_tap;
+  constexpr int GROUP_STEPS = GROUP_K / C::BK;
+  int s_begin = 0, nsteps = nsteps_all;
+  if (SPLIT) {
+    const int ngroups = (nsteps_all + GROUP_STEPS - 1) / GROUP_STEPS;
+    const int gps = (ngroups + p.splits - 1) / p.splits;
+    s_begin = min(split * gps, ngroups) * GROUP_STEPS;
+    nsteps = min(min((split + 1) * gps, ngroups) * GROUP_STEPS, nsteps_all);
+    if (s_begin >= nsteps) return;
+  }
+
+  const _Float16* a_base[C::A_LD];
+  int a_lds[C::A_LD];
+#pragma unroll
+  for (int i = 0; i < C::A_LD; ++i) {
+    int idx = tid + i * C::NT;
+    if (C::A_CH % C::NT != 0 && idx >= C::A_CH) idx = C::A_CH - 1;
+    const int row = idx / C::KC, col = (idx % C::KC) * 8;
+    a_base[i] = W + (size_t)(m0 + row) * p.k * cin + col;
+    a_lds[i] = row * C::LDK + col;
+  }
+  const float* bx[C::B_LD];
+  const float* bh[C::B_LD];
+  int bn[C::B_LD], b_lds[C::B_LD];
+#pragma unroll
+  for (int i = 0; i < C::B_LD; ++i) {
+    int idx = tid + i * C::NT;
+    if (C::B_CH % C::NT != 0 && idx >= C::B_CH) idx = C::B_CH - 1;
+    const int row = idx / C::KC, col = (idx % C::KC) * 8;
+    const int g = min(g0 + row, p.rows - 1);
+    const int b = g / p.nin;
+    const int n = g - b * p.nin;
+    bn[i] = n;
+    bx[i] = p.x + (size_t)g * cin + col;
+    bh[i] = p.hin ? p.hin + (size_t)b * p.sstride + (ptrdiff_t)(p.hin_rows + n) * cin + col : bx[i];
+    b_lds[i] = row * C::LDK + col;
+  }
+
+  f32x4 ra[C::A_LD];
+  f32x4 rb_lo[C::B_LD], rb_hi[C::B_LD];
+
+  auto gload = [&](int s) {
+    const int tap = s / ksteps_per_tap;
+    const int c0 = (s - tap * ksteps_per_tap) * C::BK;
+    const int shift = (p.k - 1 - tap) * p.dil;
+    const ptrdiff_t aoff = (ptrdiff_t)tap * cin + c0;
+    const ptrdiff_t boff = c0 - (ptrdiff_t)shift * cin;
+#pragma unroll
+    for (int i = 0; i < C::A_LD; ++i) ra[i] = *reinterpret_cast<const f32x4*>(a_base[i] + aoff);
+#pragma unroll
+    for (int i = 0; i < C::B_LD; ++i) {
+      const float* src = (bn[i] >= shift ? bx[i] : bh[i]) + boff;
+      rb_lo[i] = ld4(src);
+      rb_hi[i] = ld4(src + 4);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < C::A_LD; ++i) *reinterpret_cast<f32x4*>(&As[buf][a_lds[i]]) = ra[i];
+#pragma unroll
+    for (int i = 0; i < C::B_LD; ++i) *reinterpret_cast<f16x8*>(&Bs[buf][b_lds[i]]) = to_half8(rb_lo[i], rb_hi[i]);
+  };
+
+  // Lane l supplies A[l%16][k] and B[k][l%16] for the PER_LANE values of k
+  // owned by lane group l/16; the group's values are consecutive in K, read
+  // as one 16- or 8-byte vector from a padded LDS row.
+  const int lr = lane & 15;
+  const int lk = (lane >> 4) * C::PER_LANE;
+
+  f32x4 acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  auto mma_step = [&](int cur, f32x4 (&part)[C::FM][C::FN], auto first) {
+    if constexpr (C::IGLP >= 0) __builtin_amdgcn_iglp_opt(C::IGLP);
+    const _Float16* Ab = As[cur];
+    const _Float16* Bb = Bs[cur];
+#pragma unroll
+    for (int kk = 0; kk < C::BK; kk += C::SLAB) {
+      if constexpr (C::SLAB == 32) {
+        f16x8 af[C::FM], bf[C::FN];
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+          af[i] = *reinterpret_cast<const f16x8*>(&Ab[(wm * C::WTM + i * 16 + lr) * C::LDK + kk + lk]);
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+          bf[j] = *reinterpret_cast<const f16x8*>(&Bb[(wn * C::WTN + j * 16 + lr) * C::LDK + kk + lk]);
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j) {
+            if (decltype(first)::value && kk == 0)
+              part[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            else
+              part[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], part[i][j], 0, 0, 0);
+          }
+      } else {
+        f16x4 af[C::FM], bf[C::FN];
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+          af[i] = *reinterpret_cast<const f16x4*>(&Ab[(wm * C::WTM + i * 16 + lr) * C::LDK + kk + lk]);
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+          bf[j] = *reinterpret_cast<const f16x4*>(&Bb[(wn * C::WTN + j * 16 + lr) * C::LDK + kk + lk]);
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j) {
+            if (decltype(first)::value && kk == 0)
+              part[i][j] = __builtin_amdgcn_mfma_f32_16x16x16f16(af[i], bf[j], (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            else
+              part[i][j] = __builtin_amdgcn_mfma_f32_16x16x16f16(af[i], bf[j], part[i][j], 0, 0, 0);
+          }
+      }
+    }
+  };
+
+  gload(s_begin);
+  lstore(s_begin & 1);
+  __syncthreads();
+  for (int gs = s_begin; gs < nsteps; gs += GROUP_STEPS) {
+    const int ge = min(gs + GROUP_STEPS, nsteps);
+    f32x4 part[C::FM][C::FN];
+    for (int s = gs; s < ge; ++s) {
+      const int cur = s & 1;
+      if (s + 1 < nsteps) gload(s + 1);
+      if (s == gs)
+        mma_step(cur, part, std::true_type{});
+      else
+        mma_step(cur, part, std::false_type{});
+      if (s + 1 < nsteps) lstore(cur ^ 1);
+      __syncthreads();
+    }
+    if (SPLIT) {
+      const size_t gbase = (size_t)(gs / GROUP_STEPS) * p.rows;
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i) {
+        const int m = m0 + wm * C::WTM + i * 16 + (lane >> 4) * 4;
+        if (m >= p.M) continue;
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+          const int g = g0 + wn * C::WTN + j * 16 + lr;
+          if (g < p.rows) st4(p.partial + (gbase + g) * p.M + m, part[i][j]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) acc[i][j] += part[i][j];
+    }
+  }
+  if (SPLIT) return;
+
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) {
+    const int m = m0 + wm * C::WTM + i * 16 + (lane >> 4) * 4;
+    if (m >= p.M) continue;
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+      const int g = g0 + wn * C::WTN + j * 16 + lr;
+      if (g < p.rows) epilogue4(p, m, g, acc[i][j]);
+    }
+  }
+}
+
+template <class C, bool HALF = false>
 hipError_t launch_cfg(const ConvParams& p, hipStream_t s) {
   const int mtiles = (p.M + C::BM - 1) / C::BM;
   const int ntiles = (p.rows + C::BN - 1) / C::BN;
@@ -335,12 +574,18 @@ hipError_t launch_cfg(const ConvParams& p, hipStream_t s) {
   if (tiles <= 0) return hipSuccess;
   if (p.splits <= 1) {
     if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((conv_gemm_kernel<C, false>), dim3((unsigned)tiles), dim3(C::NT), 0, s, p);
+    if constexpr (HALF)
+      hipLaunchKernelGGL((conv_gemm_f16_kernel<C, false>), dim3((unsigned)tiles), dim3(C::NT), 0, s, p);
+    else
+      hipLaunchKernelGGL((conv_gemm_kernel<C, false>), dim3((unsigned)tiles), dim3(C::NT), 0, s, p);
     return hipGetLastError();
   }
   const long long nb = tiles * p.splits;
   if (nb > 0x7fffffffLL || !p.partial) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((conv_gemm_kernel<C, true>), dim3((unsigned)nb), dim3(C::NT), 0, s, p);
+  if constexpr (HALF)
+    hipLaunchKernelGGL((conv_gemm_f16_kernel<C, true>), dim3((unsigned)nb), dim3(C::NT), 0, s, p);
+  else
+    hipLaunchKernelGGL((conv_gemm_kernel<C, true>), dim3((unsigned)nb), dim3(C::NT), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int ngroups = (p.k * p.cin + GROUP_K - 1) / GROUP_K;
@@ -398,5 +643,25 @@ hipError_t launch_conv_gemm(const ConvParams& p, int tile, hipStream_t s) {
     case TILE_256x128:
       return bk32 ? launch_cfg<TileCfg<256, 128, 4, 2, 32>>(p, s) : launch_cfg<TileCfg<256, 128, 4, 2, 16>>(p, s);
   }
+  return hipErrorInvalidValue;
+}
+
+int gemm_f16_bk(int cin) { return cin % 64 == 0 ? 64 : cin % 32 == 0 ? 32 : 16; }
+
+hipError_t launch_conv_gemm_f16(const ConvParams& p, int tile, hipStream_t s) {
+  if (p.cin % 16 != 0) return hipErrorInvalidValue;
+  const int bk = gemm_f16_bk(p.cin);
+  // (no interleaving hint with 16-wide slabs: iglp_opt(1) sends the compiler
+  // into unbounded memory use on that instance)
+#define VOC_F16_CASES(BM, BN, WM, WN, IG)                                                           \
+  return bk == 64 ? launch_cfg<TileCfgH<BM, BN, WM, WN, 64, 32, IG>, true>(p, s)                    \
+       : bk == 32 ? launch_cfg<TileCfgH<BM, BN, WM, WN, 32, 32, IG>, true>(p, s)                    \
+                  : launch_cfg<TileCfgH<BM, BN, WM, WN, 16, 16, -1>, true>(p, s)
+  switch (tile) {
+    case TILE_128x128: VOC_F16_CASES(128, 128, 2, 4, 1);
+    case TILE_96x128: VOC_F16_CASES(96, 128, 2, 4, 0);
+    case TILE_64x64: VOC_F16_CASES(64, 64, 2, 2, -1);
+  }
+#undef VOC_F16_CASES
   return hipErrorInvalidValue;
 }

@@ -349,8 +349,10 @@ __global__ __launch_bounds__(POST_ROWS) void conv_post_kernel(
 // ---------------------------------------------------------------------------
 // weight repacking (create time)
 // ---------------------------------------------------------------------------
-// Conv1d / Linear [M][cin][k] -> [Mpad][k][cin], zero rows past M.
-__global__ void repack_conv_kernel(const float* __restrict__ src, float* __restrict__ dst, int M, int Mpad,
+// Conv1d / Linear [M][cin][k] -> [Mpad][k][cin], zero rows past M; T is the
+// packed element type (float, or _Float16 rounded to nearest even).
+template <typename T>
+__global__ void repack_conv_kernel(const float* __restrict__ src, T* __restrict__ dst, int M, int Mpad,
                                    int cin, int k) {
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long total = (long long)Mpad * k * cin;
@@ -359,12 +361,13 @@ __global__ void repack_conv_kernel(const float* __restrict__ src, float* __restr
   const long long r = idx / cin;
   const int j = (int)(r % k);
   const int m = (int)(r / k);
-  dst[idx] = m < M ? src[((size_t)m * cin + c) * k + j] : 0.f;
+  dst[idx] = (T)(m < M ? src[((size_t)m * cin + c) * k + j] : 0.f);
 }
 
 // ConvTranspose1d [cin][cout][2s] -> [Mpad][2][cin] with row m = p*cout + o:
 // tap 0 (input row t-1) takes kernel index p + s, tap 1 (row t) takes p.
-__global__ void repack_convT_kernel(const float* __restrict__ src, float* __restrict__ dst, int cin, int cout,
+template <typename T>
+__global__ void repack_convT_kernel(const float* __restrict__ src, T* __restrict__ dst, int cin, int cout,
                                     int s, int Mpad) {
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long total = (long long)Mpad * 2 * cin;
@@ -379,7 +382,7 @@ __global__ void repack_convT_kernel(const float* __restrict__ src, float* __rest
     const int kk = j == 0 ? p + s : p;
     v = src[((size_t)c * cout + o) * (2 * s) + kk];
   }
-  dst[idx] = v;
+  dst[idx] = (T)v;
 }
 
 // per-channel vector [C] -> [Mpad] indexed by GEMM column m = p*C + c
@@ -474,16 +477,27 @@ hipError_t launch_conv_post(const float* x, const float* hin, long long sstride,
   return hipGetLastError();
 }
 
-hipError_t launch_repack_conv(const float* src, float* dst, int M, int Mpad, int cin, int k, hipStream_t s) {
+hipError_t launch_repack_conv(const float* src, void* dst, int M, int Mpad, int cin, int k, bool half_out,
+                              hipStream_t s) {
   const long long n = (long long)Mpad * k * cin;
-  hipLaunchKernelGGL(repack_conv_kernel, dim3(cdiv(n, 256)), dim3(256), 0, s, src, dst, M, Mpad, cin, k);
+  if (half_out)
+    hipLaunchKernelGGL(repack_conv_kernel<_Float16>, dim3(cdiv(n, 256)), dim3(256), 0, s, src, (_Float16*)dst, M,
+                       Mpad, cin, k);
+  else
+    hipLaunchKernelGGL(repack_conv_kernel<float>, dim3(cdiv(n, 256)), dim3(256), 0, s, src, (float*)dst, M, Mpad,
+                       cin, k);
   return hipGetLastError();
 }
 
-hipError_t launch_repack_convT(const float* src, float* dst, int cin, int cout, int stride, int Mpad,
+hipError_t launch_repack_convT(const float* src, void* dst, int cin, int cout, int stride, int Mpad, bool half_out,
                                hipStream_t s) {
   const long long n = (long long)Mpad * 2 * cin;
-  hipLaunchKernelGGL(repack_convT_kernel, dim3(cdiv(n, 256)), dim3(256), 0, s, src, dst, cin, cout, stride, Mpad);
+  if (half_out)
+    hipLaunchKernelGGL(repack_convT_kernel<_Float16>, dim3(cdiv(n, 256)), dim3(256), 0, s, src, (_Float16*)dst, cin,
+                       cout, stride, Mpad);
+  else
+    hipLaunchKernelGGL(repack_convT_kernel<float>, dim3(cdiv(n, 256)), dim3(256), 0, s, src, (float*)dst, cin, cout,
+                       stride, Mpad);
   return hipGetLastError();
 }
 

@@ -62,6 +62,7 @@ bool config_valid(const vocoder_config* c) {
     if ((long long)c->post_kernel * cl + (128LL + c->post_kernel - 1) * (cl + 1) > 16384) return false;
   }
   if (c->max_batch < 1 || c->max_frames < 1) return false;
+  if (c->precision != VOCODER_PRECISION_F32 && c->precision != VOCODER_PRECISION_F16) return false;
   // every GEMM row count must fit in int
   long long hop = 1;
   for (int i = 0; i < c->n_up; ++i) hop *= c->up_strides[i];
@@ -130,6 +131,7 @@ struct StageP {
 struct Plan {
   vocoder_config cfg{};
   int d = 0, hd = 0, half = 0, hop = 0;
+  bool f16 = false;  // fp16 GEMM operands (packed weights in fp16)
   long long raw_count = 0;
   // packed
   long long raw_codebooks = 0, codebooks = 0;
@@ -180,6 +182,7 @@ bool make_plan(const vocoder_config* cp, Plan& P) {
   P.hd = c.model_dim / c.n_heads;
   P.half = P.hd / 2;
   P.hop = hop_of(c);
+  P.f16 = c.precision == VOCODER_PRECISION_F16;
   const int d = P.d, De = c.embed_dim, F = c.ffn_dim;
 
   long long raw = 0, pk = 0;
@@ -192,7 +195,8 @@ bool make_plan(const vocoder_config* cp, Plan& P) {
     g.cin = cin;
     g.phases = phases;
     g.cout = cout;
-    g.w = K((long long)g.Mpad * k * cin);
+    const long long welems = (long long)g.Mpad * k * cin;
+    g.w = K(P.f16 ? (welems + 1) / 2 : welems);  // fp16 weights take half the floats
     g.bias = K(g.Mpad);
   };
 
@@ -491,11 +495,16 @@ int run_gemm(const Ctx& cx, const ConvParams& pin) {
   double bytes = 4.0 * ((double)p.M * K + (double)p.rows * p.cin + (double)p.nout * p.rows * p.M);
   if (p.resid) bytes += 4.0 * p.rows * p.M;
   if (p.mrf_mode == MRF_ACCUM || p.mrf_mode == MRF_LAST) bytes += 4.0 * p.rows * p.M;
+  const bool f16 = cx.v->P.f16;
+  if (f16) bytes -= 2.0 * p.M * K;  // fp16 weights
   char name[48];
-  snprintf(name, sizeof(name), "conv_gemm_%dx%d_bk%d%s", bm, gemm_tile_bn(tile), gemm_tile_bk(tile, p.cin),
-           p.splits > 1 ? "_splitk" : "");
+  snprintf(name, sizeof(name), "conv_gemm_%s%dx%d_bk%d%s", f16 ? "f16_" : "", bm, gemm_tile_bn(tile),
+           f16 ? gemm_f16_bk(p.cin) : gemm_tile_bk(tile, p.cin), p.splits > 1 ? "_splitk" : "");
   Prof pr(cx.v, cx.s, name, flops, bytes);
-  HIP_OK(launch_conv_gemm(p, tile, cx.s));
+  if (f16)
+    HIP_OK(launch_conv_gemm_f16(p, tile, cx.s));
+  else
+    HIP_OK(launch_conv_gemm(p, tile, cx.s));
   return VOCODER_OK;
 }
 
@@ -509,10 +518,10 @@ void tap(const Ctx& cx, const char* name, const float* src, long long count) {
 int repack_gemm(vocoder* v, const float* raw, const GemmW& g, bool transposed, hipStream_t s) {
   float* pk = v->packed;
   if (transposed) {
-    HIP_OK(launch_repack_convT(raw + g.raw_w, pk + g.w, g.cin, g.cout, g.phases, g.Mpad, s));
+    HIP_OK(launch_repack_convT(raw + g.raw_w, pk + g.w, g.cin, g.cout, g.phases, g.Mpad, v->P.f16, s));
     HIP_OK(launch_expand_vec(raw + g.raw_b, pk + g.bias, g.cout, g.phases, g.Mpad, s));
   } else {
-    HIP_OK(launch_repack_conv(raw + g.raw_w, pk + g.w, g.M, g.Mpad, g.cin, g.k, s));
+    HIP_OK(launch_repack_conv(raw + g.raw_w, pk + g.w, g.M, g.Mpad, g.cin, g.k, v->P.f16, s));
     HIP_OK(launch_expand_vec(raw + g.raw_b, pk + g.bias, g.M, 1, g.Mpad, s));
   }
   return VOCODER_OK;
@@ -590,8 +599,9 @@ int vocoder_create(const vocoder_config* cfg, const float* raw_weights, void* pa
     const long long raw_w[3] = {L.raw_q_w, L.raw_k_w, L.raw_v_w};
     const long long raw_b[3] = {L.raw_q_b, L.raw_k_b, L.raw_v_b};
     for (int t = 0; t < 3; ++t) {
-      if (launch_repack_conv(raw + raw_w[t], pk + L.qkv.w + (long long)t * d * d, d, d, d, 1, s) != hipSuccess)
-        return fail(VOCODER_EHIP);
+      const long long off = (long long)t * d * d;  // elements
+      void* dst = P.f16 ? (void*)(reinterpret_cast<_Float16*>(pk + L.qkv.w) + off) : (void*)(pk + L.qkv.w + off);
+      if (launch_repack_conv(raw + raw_w[t], dst, d, d, d, 1, P.f16, s) != hipSuccess) return fail(VOCODER_EHIP);
       if ((rc = copy_d2d(pk + L.qkv.bias + (long long)t * d, raw + raw_b[t], d, s))) return fail(rc);
     }
     if ((rc = repack_gemm(v, raw, L.o, false, s))) return fail(rc);
@@ -620,7 +630,7 @@ int vocoder_create(const vocoder_config* cfg, const float* raw_weights, void* pa
   const int CL = P.stages.back().c;
   if ((rc = copy_d2d(pk + P.post_alpha, raw + P.raw_post_alpha, CL, s))) return fail(rc);
   // conv_post [1][C][k] -> [k][C]
-  if (launch_repack_conv(raw + P.raw_post_w, pk + P.post_w, 1, 1, CL, c.post_kernel, s) != hipSuccess)
+  if (launch_repack_conv(raw + P.raw_post_w, pk + P.post_w, 1, 1, CL, c.post_kernel, false, s) != hipSuccess)
     return fail(VOCODER_EHIP);
   if ((rc = copy_d2d(pk + P.post_b, raw + P.raw_post_b, 1, s))) return fail(rc);
 
