@@ -1,6 +1,6 @@
 """Throughput of the streaming code2wav decoder on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--precision f32|f16] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--precision f32|f16] [--graph] [--no-cpu-baseline]
 
 A step decodes one 25-frame chunk (2 s of audio) for each of 64 independent
 streams whose states were first warmed (untimed) to different positions: the
@@ -37,6 +37,10 @@ def parse():
     ap.add_argument("--workload", default="qwen3_b64_chunk25")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-frames", type=int, default=100)
+    ap.add_argument("--profile-chunk", type=int, default=0,
+                    help="chunk-schedule workloads: add per-kernel device times of the chunks of this length")
+    ap.add_argument("--graph", action="store_true",
+                    help="chunk-schedule workloads: replay each call from a HIP graph")
     ap.add_argument("--precision", choices=["f32", "f16"], default="f32",
                     help="matrix-product operands: f32, or fp16 with fp32 sums (the half-precision decoder)")
     # measurement helpers (each replaces the timed run)
@@ -180,16 +184,19 @@ def stream_latency(args, wl, torch, S, Decoder, vb):
         chunks.append(torch.from_numpy(np.ascontiguousarray(codes[:, t0:t0 + n])).cuda())
         t0 += n
     pcm = [torch.empty((B, n * dec.hop), device="cuda") for n in sched]
-    st_a, st_b = dec.new_state(B), dec.new_state(B)
+    states = (dec.new_state(B), dec.new_state(B))
     stream = torch.cuda.current_stream()
     times = []
     for rep in range(args.warmup + args.steps):
+        # the same buffers in the same roles every repetition: with --graph the
+        # warm-up repetitions record one graph per chunk, the timed ones replay
+        st_a, st_b = states
         dec.reset(st_a)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(sched) + 1)]
         torch.cuda.synchronize()
         ev[0].record(stream)
         for i, n in enumerate(sched):
-            dec.decode(chunks[i], st_a, st_b, pcm[i])
+            dec.decode(chunks[i], st_a, st_b, pcm[i], graph=args.graph)
             st_a, st_b = st_b, st_a
             ev[i + 1].record(stream)
         torch.cuda.synchronize()
@@ -197,18 +204,44 @@ def stream_latency(args, wl, torch, S, Decoder, vb):
             times.append([ev[i].elapsed_time(ev[i + 1]) for i in range(len(sched))])
     if dec.status() != vb.VOCODER_OK:
         raise SystemExit("device reported an error")
+    kernels = None
+    if args.profile_chunk:
+        # one more eager pass, recording kernel events around the chosen chunks only
+        st_a, st_b = states
+        dec.reset(st_a)
+        agg, calls = {}, 0
+        for i, n in enumerate(sched):
+            if n == args.profile_chunk:
+                vb.vocoder_profile_begin(dec.handle)
+            dec.decode(chunks[i], st_a, st_b, pcm[i])
+            if n == args.profile_chunk:
+                calls += 1
+                for k, v in vb.vocoder_profile_end(dec.handle).items():
+                    a = agg.setdefault(k, [0, 0.0])
+                    a[0] += v["launches"]
+                    a[1] += v["total_ms"]
+            st_a, st_b = st_b, st_a
+        torch.cuda.synchronize()
+        if calls:
+            kernels = {"chunk_frames": args.profile_chunk,
+                       "sum_ms_per_call": round(sum(a[1] for a in agg.values()) / calls, 4),
+                       "launches_per_call": sum(a[0] for a in agg.values()) / calls,
+                       "by_kernel": {k: {"launches": a[0] / calls, "ms": round(a[1] / calls, 4)}
+                                     for k, a in sorted(agg.items(), key=lambda kv: -kv[1][1])}}
     t = np.array(times)  # [reps][chunks] ms
     per_chunk = np.median(t, axis=0)
     total = t.sum(axis=1)
     audio = sum(sched) * FRAME_SECONDS * B
     out = {"metric": "streaming chunk latency (ms) and audio-seconds/sec", "workload": args.workload,
-           "streams": B, "schedule": sched, "reps": args.steps,
+           "streams": B, "schedule": sched, "reps": args.steps, "graph": args.graph,
            "first_chunk_ms": round(float(per_chunk[0]), 3),
            "chunk_ms_median_by_length": {str(n): round(float(np.median(t[:, [i for i, m in enumerate(sched) if m == n]])), 3)
                                          for n in sorted(set(sched))},
            "total_ms_median": round(float(np.median(total)), 3),
            "audio_s_per_s": round(audio / (float(np.median(total)) / 1e3), 2),
            "dtype": args.precision, "data": "synthetic"}
+    if kernels:
+        out["kernels"] = kernels
     print(json.dumps(out), flush=True)
 
 

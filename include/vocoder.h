@@ -166,6 +166,29 @@ int vocoder_reset(vocoder* v, void* state, int batch, void* stream);
 int vocoder_decode_chunk(vocoder* v, const int32_t* codes, int batch, int n_frames,
                          const void* state_in, void* state_out, float* pcm, void* stream);
 
+/* Graph entries a handle keeps (least recently used evicted). */
+#define VOCODER_GRAPH_CACHE 32
+
+/* vocoder_decode_chunk replayed from a HIP graph: the server runs the decoder
+ * with one stateful graph per reachable chunk length ("Edge TTS design",
+ * section 1.3); small chunks are bound by launch overhead.  Same arguments,
+ * checks, results (bit for bit) and error reporting as vocoder_decode_chunk.
+ * The first call for a given (codes, state_in, state_out, pcm, batch,
+ * n_frames) records the call's launch sequence into a graph (nothing runs
+ * while recording), instantiates it and keeps it in the handle; later calls
+ * with the same six values only launch that graph on `stream`.  A streaming
+ * caller that ping-pongs two state buffers and reuses its code and PCM buffers
+ * therefore holds two graphs per chunk length.  Buffers named by a kept graph
+ * must stay allocated while the handle lives (or be re-used only at the same
+ * address and size).  Taps and profiling apply to eager calls only.  Graphs
+ * hold driver resources, released by vocoder_destroy.  Errors: as
+ * vocoder_decode_chunk, and VOCODER_EHIP if recording or instantiation fails. */
+int vocoder_decode_chunk_graph(vocoder* v, const int32_t* codes, int batch, int n_frames,
+                               const void* state_in, void* state_out, float* pcm, void* stream);
+
+/* Graphs the handle currently keeps (0..VOCODER_GRAPH_CACHE), -1 for NULL. */
+int vocoder_graph_cache_size(const vocoder* v);
+
 /* Samples per frame (product of up_strides and rates): 1920 for Qwen3-TTS-12Hz. */
 int vocoder_hop(const vocoder* v);
 

@@ -114,6 +114,14 @@ WORKLOADS = OrderedDict(
                                    codes="uniform", weight_seed=1, code_seed=103)),
         ("qwen3_b16_t1500_zipf", dict(model=QWEN3, batch=16, frames=1500, schedule=[25] * 60,
                                       codes="zipf", weight_seed=1, code_seed=104)),
+        # small-chunk streaming: chunks of 1, 2, 4 and 8 frames, and a 4-4-8-16-25 ramp
+        # over the 250-frame stream's codes (so it must reproduce the whole decode)
+        ("qwen3_b1_chunks_1248", dict(model=QWEN3, batch=1, frames=60,
+                                      schedule=[1] * 4 + [2] * 4 + [4] * 4 + [8] * 4,
+                                      codes="uniform", weight_seed=1, code_seed=105)),
+        ("qwen3_b1_t250_ramp", dict(model=QWEN3, batch=1, frames=250,
+                                    schedule=[4, 4, 8, 16] + [25] * 8 + [18],
+                                    codes="uniform", weight_seed=1, code_seed=101)),
     ]
 )
 

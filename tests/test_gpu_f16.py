@@ -6,6 +6,8 @@ sums).  The two differ by fp32 summation and by the operands whose fp32 (GPU)
 and float64 (oracle) values round to neighbouring fp16 values; both are far
 below the difference to the unrounded decoder, which the tests also bound.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -20,11 +22,22 @@ pytestmark = pytest.mark.gpu
 
 # GPU fp16 decoder vs the oracle's fp16-operand mode (stage taps, pre-tanh, PCM)
 F16_VS_F16_ORACLE = 2e-3
-# fp16-operand decoder vs the unrounded float64 decoder: fp16 operand rounding
-# itself (CPU emulation of the 250-frame Qwen3-shaped decode: PCM 2.4e-2,
-# pre-tanh 1.2e-2)
+# fp16-operand decoder vs the unrounded float64 decoder: the fp16 operand
+# rounding itself (the oracle's own 250-frame Qwen3-shaped decode in both modes
+# differs by PCM 2.5e-2, pre-tanh 1.2e-2)
 F16_VS_F64_PCM = 6e-2
 F16_VS_F64_PRE = 3e-2
+# Full size (250 frames of the Qwen3-shaped decoder).  Here the fp16 roundings
+# are not reproducible between two evaluations: a GPU value computed in fp32 and
+# the oracle's float64 value of the same element round to different fp16 values
+# whenever they straddle a rounding boundary, and the random-init stack (gain
+# about 10 to the pre-tanh signal) carries each such flip to the output.  Two
+# fp16-operand evaluations therefore differ by about as much as either differs
+# from the unrounded decoder, which the stored oracle values put at rel-L2
+# 1.2e-2 (pre-tanh) and 2.5e-2 (PCM).  The bound is 2.5x that, against both the
+# fp16-operand oracle and the float64 decoder.
+F16_FULL_PRE = F16_VS_F64_PRE
+F16_FULL_PCM = F16_VS_F64_PCM
 
 
 def half(model):
@@ -95,3 +108,47 @@ def test_f16_state_is_not_an_f32_state():
     got, _ = run_schedule(f16, codes, [8], state=st32)
     assert f16.status() == vb.VOCODER_ESTATE
     assert torch.equal(got, fresh)
+
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    path = os.path.join(GOLDEN, f"{name}.npz")
+    assert os.path.exists(path), f"missing {path}: run tests/golden/make_golden.py {name}"
+    return dict(np.load(path))
+
+
+@pytest.fixture(scope="module")
+def f16_whole_250():
+    print("\n[f16 full] 250-frame whole-sequence decode", flush=True)
+    model = half(S.QWEN3)
+    dec, _ = decoder(model, 1, 1, 250)
+    codes = S.workload_codes("qwen3_b1_t250_whole")
+    pre = torch.empty(250 * model["hop"], device="cuda")
+    dec.set_tap("pre_tanh", pre)
+    pcm, _ = run_schedule(dec, codes, [250])
+    dec.set_tap("pre_tanh", None)
+    assert dec.status() == vb.VOCODER_OK
+    return dec, codes, pcm[0].cpu().numpy().astype(np.float64), pre.cpu().numpy().astype(np.float64)
+
+
+def test_f16_full_size_250_frames(f16_whole_250):
+    _, _, pcm, pre = f16_whole_250
+    g16, g64 = _golden("qwen3_whole_f16"), _golden("qwen3_whole")
+    idx = g16["idx"]
+    assert np.array_equal(idx, g64["idx"])
+    check_close(pre[idx], g16["pre"], "f16 250 frames pre-tanh vs fp16-operand oracle", rel=F16_FULL_PRE)
+    check_close(pcm[idx], g16["pcm"], "f16 250 frames pcm vs fp16-operand oracle", rel=F16_FULL_PCM)
+    check_close(pre[idx], g64["pre"], "f16 250 frames pre-tanh vs float64 decoder", rel=F16_VS_F64_PRE)
+    check_close(pcm[idx], g64["pcm"], "f16 250 frames pcm vs float64 decoder", rel=F16_VS_F64_PCM)
+    assert abs(np.linalg.norm(pre) / g16["pre_norm"][0] - 1) < F16_FULL_PRE
+    assert np.all(np.abs(pcm) <= 1.0)
+
+
+def test_f16_full_size_streamed_equals_whole(f16_whole_250):
+    print("\n[f16 full] streamed 1 + 25x9 + 24", flush=True)
+    dec, codes, pcm_whole, _ = f16_whole_250
+    pcm, _ = run_schedule(dec, codes, S.workload("qwen3_b1_t250_stream")["schedule"])
+    assert dec.status() == vb.VOCODER_OK
+    assert np.array_equal(pcm[0].cpu().numpy().astype(np.float64), pcm_whole)

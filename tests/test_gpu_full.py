@@ -65,6 +65,20 @@ def test_streamed_1_then_25s_equals_whole(whole_250):
     assert np.array_equal(pcm[0].cpu().numpy().astype(np.float64), pcm_whole)
 
 
+def test_ramp_through_graphs_equals_whole(whole_250):
+    """Chunks of 4, 4, 8, 16, then 25s, each replayed from a HIP graph: bitwise
+    equal to the whole decode (small-chunk streaming at full size)."""
+    from tests.test_gpu_graph import run_graph_schedule
+
+    print("\n[full] graph ramp 4, 4, 8, 16, 25 x 8, 18", flush=True)
+    dec, codes, pcm_whole, _ = whole_250
+    sched = S.workload("qwen3_b1_t250_ramp")["schedule"]
+    assert sum(sched) == 250
+    pcm, _ = run_graph_schedule(dec, codes, sched, {})
+    assert dec.status() == 0
+    assert np.array_equal(pcm[0].cpu().numpy().astype(np.float64), pcm_whole)
+
+
 def _warm(dec, codes, warm):
     B = len(warm)
     common = min(warm)

@@ -117,3 +117,22 @@ def test_f16_operand_mode_streamed_equals_whole(mini, schedule):
     # the rounding is applied and moves the result, but only by fp16-operand error
     rel = np.linalg.norm(whole16 - whole) / np.linalg.norm(whole)
     assert 1e-6 < rel < 5e-2
+
+
+def test_stored_full_size_values_are_consistent():
+    """The stored full-size oracle values (tests/golden, written by
+    make_golden.py from the oracle alone): the same sample grid in both modes,
+    outputs within tanh's range, and the fp16-operand decode differs from the
+    float64 one by fp16 rounding error only (rel-L2 between 1e-3 and 5e-2)."""
+    import os
+
+    here = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+    g64 = np.load(os.path.join(here, "qwen3_whole.npz"))
+    g16 = np.load(os.path.join(here, "qwen3_whole_f16.npz"))
+    assert np.array_equal(g64["idx"], g16["idx"]) and g64["idx"][-1] == 250 * S.QWEN3["hop"] - 1
+    for g in (g64, g16):
+        assert np.all(np.abs(g["pcm"]) <= 1.0)
+        np.testing.assert_allclose(g["pcm"], np.tanh(g["pre"]), rtol=0, atol=1e-12)
+    for key in ("pre", "pcm"):
+        rel = np.linalg.norm(g16[key] - g64[key]) / np.linalg.norm(g64[key])
+        assert 1e-3 < rel < 5e-2, (key, rel)

@@ -95,6 +95,10 @@ def lib():
         L.vocoder_reset.restype = i32
         L.vocoder_decode_chunk.argtypes = [vp, vp, i32, i32, vp, vp, vp, vp]
         L.vocoder_decode_chunk.restype = i32
+        L.vocoder_decode_chunk_graph.argtypes = [vp, vp, i32, i32, vp, vp, vp, vp]
+        L.vocoder_decode_chunk_graph.restype = i32
+        L.vocoder_graph_cache_size.argtypes = [vp]
+        L.vocoder_graph_cache_size.restype = i32
         L.vocoder_hop.argtypes = [vp]
         L.vocoder_hop.restype = i32
         L.vocoder_left_context_frames.argtypes = [vp]
@@ -195,6 +199,15 @@ def vocoder_decode_chunk(handle, codes, batch, n_frames, state_in, state_out, pc
                                       _ptr(state_out), _ptr(pcm), _stream(stream))
 
 
+def vocoder_decode_chunk_graph(handle, codes, batch, n_frames, state_in, state_out, pcm, stream=None) -> int:
+    return lib().vocoder_decode_chunk_graph(handle, _ptr(codes), int(batch), int(n_frames), _ptr(state_in),
+                                            _ptr(state_out), _ptr(pcm), _stream(stream))
+
+
+def vocoder_graph_cache_size(handle) -> int:
+    return lib().vocoder_graph_cache_size(handle)
+
+
 def vocoder_hop(handle) -> int:
     return lib().vocoder_hop(handle)
 
@@ -284,7 +297,10 @@ class Decoder:
             raise VocoderError(rc, "vocoder_reset")
 
     def decode(self, codes: torch.Tensor, state_in: torch.Tensor, state_out: torch.Tensor,
-               pcm: torch.Tensor | None = None) -> torch.Tensor:
+               pcm: torch.Tensor | None = None, graph: bool = False) -> torch.Tensor:
+        """One chunk for codes.shape[0] streams.  graph=True replays a HIP graph
+        kept per (buffers, batch, frames): reuse the same code, state and PCM
+        tensors across calls, and keep them alive while the decoder lives."""
         B, T, Q = codes.shape
         if codes.dtype != torch.int32 or not codes.is_contiguous():
             raise ValueError("codes must be a contiguous int32 [batch][frames][codebooks] tensor")
@@ -294,9 +310,10 @@ class Decoder:
             raise ValueError("state batch too small")
         if pcm is None:
             pcm = torch.empty((B, T * self.hop), dtype=torch.float32, device=self.device)
-        rc = vocoder_decode_chunk(self.handle, codes, B, T, state_in, state_out, pcm)
+        fn = vocoder_decode_chunk_graph if graph else vocoder_decode_chunk
+        rc = fn(self.handle, codes, B, T, state_in, state_out, pcm)
         if rc != VOCODER_OK:
-            raise VocoderError(rc, "vocoder_decode_chunk")
+            raise VocoderError(rc, fn.__name__)
         return pcm
 
     def status(self) -> int:

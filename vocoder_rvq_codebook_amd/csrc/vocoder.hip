@@ -344,6 +344,24 @@ bool make_plan(const vocoder_config* cp, Plan& P) {
 // handle
 // ---------------------------------------------------------------------------
 
+struct GraphKey {
+  const void* codes;
+  const void* state_in;
+  const void* state_out;
+  const void* pcm;
+  int batch, frames;
+  bool operator==(const GraphKey& o) const {
+    return codes == o.codes && state_in == o.state_in && state_out == o.state_out && pcm == o.pcm &&
+           batch == o.batch && frames == o.frames;
+  }
+};
+
+struct GraphEntry {
+  GraphKey key;
+  hipGraphExec_t exec;
+  uint64_t last_use;
+};
+
 struct vocoder {
   Plan P;
   uint64_t hash = 0;
@@ -359,8 +377,15 @@ struct vocoder {
   std::vector<hipEvent_t> events;
   std::vector<Rec> recs;
   std::vector<std::string> prof_names;
+  // decode graphs, one per (buffers, batch, frames), least recently used evicted
+  std::vector<GraphEntry> graphs;
+  uint64_t graph_clock = 0;
+  hipStream_t capture_stream = nullptr;
+  bool capturing = false;  // recording a graph: no profiling events, no taps
   ~vocoder() {
     for (hipEvent_t e : events) (void)hipEventDestroy(e);
+    for (GraphEntry& g : graphs) (void)hipGraphExecDestroy(g.exec);
+    if (capture_stream) (void)hipStreamDestroy(capture_stream);
   }
 };
 
@@ -375,7 +400,7 @@ namespace {
 class Prof {
  public:
   Prof(vocoder* v, hipStream_t s, const std::string& name, double flops, double bytes) : v_(v), s_(s) {
-    if (!v->prof) return;
+    if (!v->prof || v->capturing) return;
     int id = -1;
     for (size_t i = 0; i < v->prof_names.size(); ++i)
       if (v->prof_names[i] == name) id = (int)i;
@@ -509,6 +534,7 @@ int run_gemm(const Ctx& cx, const ConvParams& pin) {
 }
 
 void tap(const Ctx& cx, const char* name, const float* src, long long count) {
+  if (cx.v->capturing) return;
   auto it = cx.v->taps.find(name);
   if (it == cx.v->taps.end() || !it->second.first) return;
   if ((size_t)count > it->second.second) return;
@@ -659,19 +685,31 @@ int vocoder_reset(vocoder* v, void* state, int batch, void* stream) {
   return VOCODER_OK;
 }
 
-int vocoder_decode_chunk(vocoder* v, const int32_t* codes, int batch, int n_frames, const void* state_in,
-                         void* state_out, float* pcm, void* stream) {
-  if (!v || !codes || !state_in || !state_out || !pcm) return VOCODER_EINVAL;
+}  // extern "C"
+
+namespace {
+
+// Host-side argument checks shared by the eager and the graph entry points.
+bool decode_args_ok(const vocoder* v, const int32_t* codes, int batch, int n_frames, const void* state_in,
+                    const void* state_out, const float* pcm) {
+  if (!v || !codes || !state_in || !state_out || !pcm) return false;
   const Plan& P = v->P;
   const vocoder_config& c = P.cfg;
-  if (batch < 1 || batch > c.max_batch || n_frames < 1 || n_frames > c.max_frames) return VOCODER_EINVAL;
-  if (((uintptr_t)state_in & 255) || ((uintptr_t)state_out & 255)) return VOCODER_EINVAL;
-  {
-    const char* a = (const char*)state_in;
-    const char* b = (const char*)state_out;
-    const size_t n = (size_t)batch * P.state_floats * 4;
-    if (a < b + n && b < a + n) return VOCODER_EINVAL;
-  }
+  if (batch < 1 || batch > c.max_batch || n_frames < 1 || n_frames > c.max_frames) return false;
+  if (((uintptr_t)state_in & 255) || ((uintptr_t)state_out & 255)) return false;
+  const char* a = (const char*)state_in;
+  const char* b = (const char*)state_out;
+  const size_t n = (size_t)batch * P.state_floats * 4;
+  return !(a < b + n && b < a + n);
+}
+
+// Every launch of one decode call, in order, on stream `stream`.  Launches
+// only: no host synchronisation, allocation or memset, so the sequence can
+// be recorded into a HIP graph as it stands.
+int decode_launches(vocoder* v, const int32_t* codes, int batch, int n_frames, const void* state_in,
+                    void* state_out, float* pcm, void* stream) {
+  const Plan& P = v->P;
+  const vocoder_config& c = P.cfg;
   Ctx cx;
   cx.v = v;
   cx.s = (hipStream_t)stream;
@@ -895,6 +933,58 @@ int vocoder_decode_chunk(vocoder* v, const int32_t* codes, int batch, int n_fram
   }
   return VOCODER_OK;
 }
+
+}  // namespace
+
+extern "C" {
+
+int vocoder_decode_chunk(vocoder* v, const int32_t* codes, int batch, int n_frames, const void* state_in,
+                         void* state_out, float* pcm, void* stream) {
+  if (!decode_args_ok(v, codes, batch, n_frames, state_in, state_out, pcm)) return VOCODER_EINVAL;
+  return decode_launches(v, codes, batch, n_frames, state_in, state_out, pcm, stream);
+}
+
+int vocoder_decode_chunk_graph(vocoder* v, const int32_t* codes, int batch, int n_frames, const void* state_in,
+                               void* state_out, float* pcm, void* stream) {
+  if (!decode_args_ok(v, codes, batch, n_frames, state_in, state_out, pcm)) return VOCODER_EINVAL;
+  const GraphKey key{codes, state_in, state_out, pcm, batch, n_frames};
+  ++v->graph_clock;
+  for (GraphEntry& e : v->graphs)
+    if (e.key == key) {
+      e.last_use = v->graph_clock;
+      HIP_OK(hipGraphLaunch(e.exec, (hipStream_t)stream));
+      return VOCODER_OK;
+    }
+  // record the launch sequence on the library's own capture stream (nothing
+  // runs while recording), then instantiate and launch on the caller's stream
+  if (!v->capture_stream) HIP_OK(hipStreamCreateWithFlags(&v->capture_stream, hipStreamNonBlocking));
+  HIP_OK(hipStreamBeginCapture(v->capture_stream, hipStreamCaptureModeThreadLocal));
+  v->capturing = true;
+  const int rc = decode_launches(v, codes, batch, n_frames, state_in, state_out, pcm, v->capture_stream);
+  v->capturing = false;
+  hipGraph_t graph = nullptr;
+  const hipError_t ec = hipStreamEndCapture(v->capture_stream, &graph);
+  if (rc != VOCODER_OK || ec != hipSuccess || !graph) {
+    if (graph) (void)hipGraphDestroy(graph);
+    return rc != VOCODER_OK ? rc : VOCODER_EHIP;
+  }
+  hipGraphExec_t exec = nullptr;
+  const hipError_t ei = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(graph);
+  if (ei != hipSuccess) return VOCODER_EHIP;
+  if ((int)v->graphs.size() >= VOCODER_GRAPH_CACHE) {
+    size_t lru = 0;
+    for (size_t i = 1; i < v->graphs.size(); ++i)
+      if (v->graphs[i].last_use < v->graphs[lru].last_use) lru = i;
+    (void)hipGraphExecDestroy(v->graphs[lru].exec);
+    v->graphs.erase(v->graphs.begin() + lru);
+  }
+  v->graphs.push_back({key, exec, v->graph_clock});
+  HIP_OK(hipGraphLaunch(exec, (hipStream_t)stream));
+  return VOCODER_OK;
+}
+
+int vocoder_graph_cache_size(const vocoder* v) { return v ? (int)v->graphs.size() : -1; }
 
 int vocoder_profile_begin(vocoder* v) {
   if (!v) return VOCODER_EINVAL;
