@@ -189,6 +189,24 @@ int vocoder_decode_chunk_graph(vocoder* v, const int32_t* codes, int batch, int 
 /* Graphs the handle currently keeps (0..VOCODER_GRAPH_CACHE), -1 for NULL. */
 int vocoder_graph_cache_size(const vocoder* v);
 
+/* Reference prefix: decode `codes` into the state without emitting audio.
+ * The decoder's cross-chunk state includes a cache of the voice-clone
+ * reference prefix ("Edge TTS design", section 1.3): the reference's codes are
+ * run through the decoder before the utterance so that its window and conv
+ * context start from them.  state_out is bit for bit the state_out of
+ * vocoder_decode_chunk on the same arguments; no PCM is written.  The
+ * transformer runs over all n_frames frames (its window of keys and values is
+ * carried); the stack after it runs over the last
+ * vocoder_prefill_tail_frames frames only, which determine every carried row
+ * of that stack.  A prefix longer than max_frames is fed in several calls.
+ * Arguments and errors as vocoder_decode_chunk without `pcm`. */
+int vocoder_prefill(vocoder* v, const int32_t* codes, int batch, int n_frames, const void* state_in,
+                    void* state_out, void* stream);
+
+/* Frames at the end of a prefill call that go through the upsampling stack
+ * (9 for the Qwen3-TTS-12Hz shape); 0 for NULL. */
+int vocoder_prefill_tail_frames(const vocoder* v);
+
 /* Samples per frame (product of up_strides and rates): 1920 for Qwen3-TTS-12Hz. */
 int vocoder_hop(const vocoder* v);
 

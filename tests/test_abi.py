@@ -81,6 +81,8 @@ def test_null_arguments_rejected_before_any_device_call():
     assert L.vocoder_decode_chunk(None, 256, 1, 1, 256, 512, 256, None) == vb.VOCODER_EINVAL
     assert L.vocoder_decode_chunk_graph(None, 256, 1, 1, 256, 512, 256, None) == vb.VOCODER_EINVAL
     assert L.vocoder_graph_cache_size(None) == -1
+    assert L.vocoder_prefill(None, 256, 1, 1, 256, 512, None) == vb.VOCODER_EINVAL
+    assert L.vocoder_prefill_tail_frames(None) == 0
     assert L.vocoder_reset(None, 256, 1, None) == vb.VOCODER_EINVAL
     assert L.vocoder_get_status(None, None) == vb.VOCODER_EINVAL
     assert L.vocoder_hop(None) == 0

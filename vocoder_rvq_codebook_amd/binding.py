@@ -99,6 +99,10 @@ def lib():
         L.vocoder_decode_chunk_graph.restype = i32
         L.vocoder_graph_cache_size.argtypes = [vp]
         L.vocoder_graph_cache_size.restype = i32
+        L.vocoder_prefill.argtypes = [vp, vp, i32, i32, vp, vp, vp]
+        L.vocoder_prefill.restype = i32
+        L.vocoder_prefill_tail_frames.argtypes = [vp]
+        L.vocoder_prefill_tail_frames.restype = i32
         L.vocoder_hop.argtypes = [vp]
         L.vocoder_hop.restype = i32
         L.vocoder_left_context_frames.argtypes = [vp]
@@ -208,6 +212,15 @@ def vocoder_graph_cache_size(handle) -> int:
     return lib().vocoder_graph_cache_size(handle)
 
 
+def vocoder_prefill(handle, codes, batch, n_frames, state_in, state_out, stream=None) -> int:
+    return lib().vocoder_prefill(handle, _ptr(codes), int(batch), int(n_frames), _ptr(state_in), _ptr(state_out),
+                                 _stream(stream))
+
+
+def vocoder_prefill_tail_frames(handle) -> int:
+    return lib().vocoder_prefill_tail_frames(handle)
+
+
 def vocoder_hop(handle) -> int:
     return lib().vocoder_hop(handle)
 
@@ -315,6 +328,19 @@ class Decoder:
         if rc != VOCODER_OK:
             raise VocoderError(rc, fn.__name__)
         return pcm
+
+    def prefill(self, codes: torch.Tensor, state_in: torch.Tensor, state_out: torch.Tensor) -> None:
+        """Decode a reference prefix into state_out without producing audio."""
+        B, T, Q = codes.shape
+        if codes.dtype != torch.int32 or not codes.is_contiguous():
+            raise ValueError("codes must be a contiguous int32 [batch][frames][codebooks] tensor")
+        if Q != self.cfg.n_codebooks:
+            raise ValueError(f"expected {self.cfg.n_codebooks} codebooks, got {Q}")
+        if state_in.shape[0] < B or state_out.shape[0] < B:
+            raise ValueError("state batch too small")
+        rc = vocoder_prefill(self.handle, codes, B, T, state_in, state_out)
+        if rc != VOCODER_OK:
+            raise VocoderError(rc, "vocoder_prefill")
 
     def status(self) -> int:
         return vocoder_get_status(self.handle)

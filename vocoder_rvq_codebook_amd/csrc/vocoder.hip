@@ -160,6 +160,9 @@ struct Plan {
   long long ws_partial = 0, partial_floats = 0;  // split-K group partials
   std::vector<long long> ws_A;
   long long ws_floats = 0;
+  // frames at the end of a chunk that determine every carried row after the
+  // transformer (prefill decodes only these through the upsampling stack)
+  int tail_frames = 0;
 };
 
 int add_slot(Plan& P, int H, int C, long long rate) {
@@ -335,6 +338,28 @@ bool make_plan(const vocoder_config* cp, Plan& P) {
   P.partial_floats = 32LL << 20;
   P.ws_partial = Wk(P.partial_floats);
   P.ws_floats = ws;
+  {
+    // Walk back from conv_post's carried rows: a causal conv of kernel k and
+    // dilation d reaches (k-1)*d input rows further back, an AMP block the sum
+    // over its dilations of both convs, a stage's blocks the longest of them;
+    // m trailing output rows of a transposed conv of stride s need the last
+    // ceil(m/s)+1 input rows.  The count at the transformer output, in frames,
+    // covers every carried row of the stack.
+    long long need = c.post_kernel - 1;
+    for (int si = c.n_stages - 1; si >= 0; --si) {
+      long long look = 0;
+      for (int j = 0; j < c.n_res; ++j) {
+        long long lj = 0;
+        for (int i = 0; i < c.n_dil; ++i) lj += (long long)(c.res_kernels[j] - 1) * (c.dilations[i] + 1);
+        look = std::max(look, lj);
+      }
+      need += look;
+      need = (need + c.rates[si] - 1) / c.rates[si] + 1;
+    }
+    need += c.conv_pre_kernel - 1;
+    for (int i = c.n_up - 1; i >= 0; --i) need = (need + c.up_strides[i] - 1) / c.up_strides[i] + 1;
+    P.tail_frames = (int)std::min<long long>(need, 1 << 30);
+  }
   return true;
 }
 
@@ -444,6 +469,7 @@ struct Ctx {
   float* sout;
   long long sstride;
   int B, T;
+  bool quiet = false;  // no taps
 };
 
 ConvParams base_params(const Ctx& cx, const GemmW& g, const float* x, int rows, int nin, int dil,
@@ -534,7 +560,7 @@ int run_gemm(const Ctx& cx, const ConvParams& pin) {
 }
 
 void tap(const Ctx& cx, const char* name, const float* src, long long count) {
-  if (cx.v->capturing) return;
+  if (cx.v->capturing || cx.quiet) return;
   auto it = cx.v->taps.find(name);
   if (it == cx.v->taps.end() || !it->second.first) return;
   if ((size_t)count > it->second.second) return;
@@ -691,8 +717,8 @@ namespace {
 
 // Host-side argument checks shared by the eager and the graph entry points.
 bool decode_args_ok(const vocoder* v, const int32_t* codes, int batch, int n_frames, const void* state_in,
-                    const void* state_out, const float* pcm) {
-  if (!v || !codes || !state_in || !state_out || !pcm) return false;
+                    const void* state_out, const float* pcm, bool need_pcm = true) {
+  if (!v || !codes || !state_in || !state_out || (need_pcm && !pcm)) return false;
   const Plan& P = v->P;
   const vocoder_config& c = P.cfg;
   if (batch < 1 || batch > c.max_batch || n_frames < 1 || n_frames > c.max_frames) return false;
@@ -704,13 +730,16 @@ bool decode_args_ok(const vocoder* v, const int32_t* codes, int batch, int n_fra
 }
 
 // Every launch of one decode call, in order, on stream `stream`.  Launches
-// only: no host synchronisation, allocation or memset, so the sequence can
-// be recorded into a HIP graph as it stands.
+// and device-to-device copies only: no host synchronisation, allocation or
+// memset, so the sequence can be recorded into a HIP graph as it stands.
+// prefill: produce state_out only (no PCM, no taps), taking the stack after
+// the transformer through the chunk's last tail_frames frames alone.
 int decode_launches(vocoder* v, const int32_t* codes, int batch, int n_frames, const void* state_in,
-                    void* state_out, float* pcm, void* stream) {
+                    void* state_out, float* pcm, void* stream, bool prefill = false) {
   const Plan& P = v->P;
   const vocoder_config& c = P.cfg;
   Ctx cx;
+  cx.quiet = prefill;
   cx.v = v;
   cx.s = (hipStream_t)stream;
   cx.sin_ = (const float*)state_in;
@@ -821,9 +850,23 @@ int decode_launches(vocoder* v, const int32_t* codes, int batch, int n_frames, c
   }
   tap(cx, "final_ln", u, (long long)R * d);
 
-  // 2x2 upsampling: transposed convs as phase-stacked 2-tap GEMMs
+  // Prefill: every carried row from here on depends only on the last
+  // tail_frames frames (each row's value is computed by the same operations
+  // whatever rows precede it), so run the rest on those frames alone; the
+  // rows they would have read from earlier frames never reach a carried row.
+  const int F = prefill ? std::min(T, P.tail_frames) : T;
   const float* x = u;
-  long long nin = T;
+  if (F < T) {
+    // the residual stream h is dead after the final LayerNorm: gather the
+    // tail rows [B][F][d] there
+    HIP_OK(hipMemcpy2DAsync(h, (size_t)F * d * sizeof(float), u + (size_t)(T - F) * d,
+                            (size_t)T * d * sizeof(float), (size_t)F * d * sizeof(float), B,
+                            hipMemcpyDeviceToDevice, cx.s));
+    x = h;
+  }
+
+  // 2x2 upsampling: transposed convs as phase-stacked 2-tap GEMMs
+  long long nin = F;
   for (int i = 0; i < c.n_up; ++i) {
     const GemmW& g = P.ups[i];
     float* y = ws + P.ws_up[i];
@@ -920,12 +963,13 @@ int decode_launches(vocoder* v, const int32_t* codes, int batch, int n_frames, c
     S_in = S_out;
   }
   // final Snake is already applied: conv_post + tanh
-  {
+  if (!prefill) {
     const Slot& sp = P.slots[P.slot_post];
     auto it = v->taps.find("pre_tanh");
     float* pre = nullptr;
     const long long rows = B * nin;
-    if (it != v->taps.end() && it->second.first && (size_t)rows <= it->second.second) pre = it->second.first;
+    if (!v->capturing && it != v->taps.end() && it->second.first && (size_t)rows <= it->second.second)
+      pre = it->second.first;
     const double C = P.stages.back().c;
     Prof pr(v, cx.s, "conv_post", 2.0 * rows * C * c.post_kernel, 4.0 * rows * (C + 1 + (pre ? 1 : 0)));
     HIP_OK(launch_conv_post(S_in, cx.sin_ + sp.off, cx.sstride, sp.H, pk + P.post_w, pk + P.post_b,
@@ -985,6 +1029,14 @@ int vocoder_decode_chunk_graph(vocoder* v, const int32_t* codes, int batch, int 
 }
 
 int vocoder_graph_cache_size(const vocoder* v) { return v ? (int)v->graphs.size() : -1; }
+
+int vocoder_prefill(vocoder* v, const int32_t* codes, int batch, int n_frames, const void* state_in,
+                    void* state_out, void* stream) {
+  if (!decode_args_ok(v, codes, batch, n_frames, state_in, state_out, nullptr, false)) return VOCODER_EINVAL;
+  return decode_launches(v, codes, batch, n_frames, state_in, state_out, nullptr, stream, true);
+}
+
+int vocoder_prefill_tail_frames(const vocoder* v) { return v ? v->P.tail_frames : 0; }
 
 int vocoder_profile_begin(vocoder* v) {
   if (!v) return VOCODER_EINVAL;
