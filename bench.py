@@ -179,19 +179,49 @@ def stream_latency(args, wl, torch, S, Decoder, vb):
     W = S.make_weights(model, wl["weight_seed"])
     codes = S.workload_codes(args.workload)
     dec = Decoder(model, torch.from_numpy(S.flatten_weights(model, W)), B, max(sched))
-    chunks, t0 = [], 0
+    prefix = wl.get("prefix", 0)
+    pre_chunks, t0 = [], 0
+    while t0 < prefix:
+        n = min(max(sched), prefix - t0)
+        pre_chunks.append(torch.from_numpy(np.ascontiguousarray(codes[:, t0:t0 + n])).cuda())
+        t0 += n
+    chunks = []
     for n in sched:
         chunks.append(torch.from_numpy(np.ascontiguousarray(codes[:, t0:t0 + n])).cuda())
         t0 += n
     pcm = [torch.empty((B, n * dec.hop), device="cuda") for n in sched]
     states = (dec.new_state(B), dec.new_state(B))
     stream = torch.cuda.current_stream()
-    times = []
+    times, pre_times, pre_dec_times = [], [], []
+
+    def run_prefix(st_a, st_b, decode):
+        # the reference prefix into the state: prefill (no audio), or, for
+        # comparison, ordinary decode calls whose audio is discarded
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for c in pre_chunks:
+            if decode:
+                dec.decode(c, st_a, st_b)
+            else:
+                dec.prefill(c, st_a, st_b)
+            st_a, st_b = st_b, st_a
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return st_a, st_b, ev[0].elapsed_time(ev[1])
+
     for rep in range(args.warmup + args.steps):
         # the same buffers in the same roles every repetition: with --graph the
         # warm-up repetitions record one graph per chunk, the timed ones replay
         st_a, st_b = states
         dec.reset(st_a)
+        if pre_chunks:
+            _, _, ms = run_prefix(st_a, st_b, True)
+            dec.reset(st_a)
+            st_a, st_b, ms_pre = run_prefix(st_a, st_b, False)
+            if rep >= args.warmup:
+                pre_dec_times.append(ms)
+                pre_times.append(ms_pre)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(sched) + 1)]
         torch.cuda.synchronize()
         ev[0].record(stream)
@@ -240,6 +270,10 @@ def stream_latency(args, wl, torch, S, Decoder, vb):
            "total_ms_median": round(float(np.median(total)), 3),
            "audio_s_per_s": round(audio / (float(np.median(total)) / 1e3), 2),
            "dtype": args.precision, "data": "synthetic"}
+    if pre_chunks:
+        out["prefix_frames"] = prefix
+        out["prefill_ms_median"] = round(float(np.median(pre_times)), 3)
+        out["prefix_as_decode_ms_median"] = round(float(np.median(pre_dec_times)), 3)
     if kernels:
         out["kernels"] = kernels
     print(json.dumps(out), flush=True)

@@ -122,6 +122,11 @@ WORKLOADS = OrderedDict(
         ("qwen3_b1_t250_ramp", dict(model=QWEN3, batch=1, frames=250,
                                     schedule=[4, 4, 8, 16] + [25] * 8 + [18],
                                     codes="uniform", weight_seed=1, code_seed=101)),
+        # voice-clone reference: a 75-frame (6 s) prefix decoded into the state
+        # without audio, then the utterance streamed 1 + 25 x 3
+        ("qwen3_b1_prefix75_stream", dict(model=QWEN3, batch=1, frames=76, prefix=75,
+                                          schedule=[1] + [25] * 3,
+                                          codes="uniform", weight_seed=1, code_seed=106)),
     ]
 )
 
@@ -272,7 +277,7 @@ def make_codes(cfg, batch: int, frames: int, seed: int, dist: str = "uniform") -
 
 
 def workload_codes(i_or_name) -> np.ndarray:
-    """Codes of a workload.  For the 64-stream batched workload the array holds
+    """Codes of a workload (a reference prefix, if any, first).  For the 64-stream batched workload the array holds
     each stream's warm-up frames followed by its timed 25-frame chunk, padded to
     the longest stream (stream b uses its first batched_warmup_frames(b) + 25 rows)."""
     w = workload(i_or_name)
@@ -280,4 +285,4 @@ def workload_codes(i_or_name) -> np.ndarray:
     if w["schedule"] == "warm_then_25":
         total = max(batched_warmup_frames(b) for b in range(w["batch"])) + w["frames"]
         return make_codes(cfg, w["batch"], total, w["code_seed"], w["codes"])
-    return make_codes(cfg, w["batch"], w["frames"], w["code_seed"], w["codes"])
+    return make_codes(cfg, w["batch"], w.get("prefix", 0) + w["frames"], w["code_seed"], w["codes"])

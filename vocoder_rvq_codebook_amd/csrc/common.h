@@ -90,14 +90,18 @@ struct Slot {
 // ---------------------------------------------------------------------------
 
 // tile configuration ids for the implicit-GEMM kernel
-enum GemmTile { TILE_128x128 = 0, TILE_96x256 = 1, TILE_192x128 = 2, TILE_64x64 = 3, TILE_96x128 = 4, TILE_256x128 = 5, TILE_COUNT = 6 };
+// TILE_S64x16 / TILE_S64x32: skinny tiles for launches of a few rows (small
+// chunks), 128-deep K-steps so that few load round trips cover a group.
+enum GemmTile {
+  TILE_128x128 = 0, TILE_96x256 = 1, TILE_192x128 = 2, TILE_64x64 = 3, TILE_96x128 = 4, TILE_256x128 = 5,
+  TILE_S64x16 = 6, TILE_S64x32 = 7, TILE_COUNT = 8
+};
 int gemm_tile_bm(int tile);
 int gemm_tile_bn(int tile);
-int gemm_tile_bk(int tile, int cin);
+int gemm_tile_bk(int tile, int cin, bool half);
 hipError_t launch_conv_gemm(const ConvParams& p, int tile, hipStream_t s);
 // fp16-operand GEMM: p.w points at fp16 weights [Mpad][k][cin]; tiles 128x128, 96x128, 64x64
 hipError_t launch_conv_gemm_f16(const ConvParams& p, int tile, hipStream_t s);
-int gemm_f16_bk(int cin);
 
 hipError_t launch_begin(const void* state_in, void* state_out, long long sstride, int batch, int T,
                         uint64_t cfg_hash, const double* inv_freq, int half, float* rope_tab, int* pos,

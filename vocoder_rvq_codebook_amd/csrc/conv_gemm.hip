@@ -110,6 +110,24 @@ __device__ __forceinline__ void epilogue4(const ConvParams& p, int m, int g, f32
 // below); split-K splits only at group boundaries.
 constexpr int GROUP_K = VOC_GROUP_K;
 
+// Sum of the group partials of output elements m..m+3 of row g, in group
+// order from zero; loads issued 8 at a time.
+__device__ __forceinline__ f32x4 fold_groups(const ConvParams& p, int m, int g, int ngroups) {
+  const size_t stride = (size_t)p.rows * p.M;
+  const float* src = p.partial + (size_t)g * p.M + m;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  int j = 0;
+  for (; j + 8 <= ngroups; j += 8) {
+    f32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = ld4(src + (size_t)(j + u) * stride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += v[u];
+  }
+  for (; j < ngroups; ++j) acc += ld4(src + (size_t)j * stride);
+  return acc;
+}
+
 // SPLIT = false: one block computes a whole output tile and runs the epilogue.
 // SPLIT = true: blocks are (tile, split) pairs; a split owns a contiguous,
 // non-empty range of accumulation groups and stores each group's partial sum,
@@ -320,11 +338,7 @@ __global__ void splitk_reduce_kernel(const ConvParams p, int ngroups) {
   if (idx >= (long long)p.rows * M4) return;
   const int g = (int)(idx / M4);
   const int m = (int)(idx - (long long)g * M4) * 4;
-  const size_t stride = (size_t)p.rows * p.M;
-  const float* src = p.partial + (size_t)g * p.M + m;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < ngroups; ++j) acc += ld4(src + j * stride);
-  epilogue4(p, m, g, acc);
+  epilogue4(p, m, g, fold_groups(p, m, g, ngroups));
 }
 
 // ---------------------------------------------------------------------------
@@ -604,6 +618,8 @@ int gemm_tile_bm(int tile) {
     case TILE_64x64: return 64;
     case TILE_96x128: return 96;
     case TILE_256x128: return 256;
+    case TILE_S64x16: return 64;
+    case TILE_S64x32: return 64;
   }
   return 0;
 }
@@ -616,11 +632,22 @@ int gemm_tile_bn(int tile) {
     case TILE_64x64: return 64;
     case TILE_96x128: return 128;
     case TILE_256x128: return 128;
+    case TILE_S64x16: return 16;
+    case TILE_S64x32: return 32;
   }
   return 0;
 }
 
-int gemm_tile_bk(int tile, int cin) { return tile == TILE_128x128 || cin % 32 != 0 ? 16 : 32; }
+namespace {
+int skinny_bk(int cin) { return cin % 128 == 0 ? 128 : cin % 64 == 0 ? 64 : cin % 32 == 0 ? 32 : 16; }
+int half_bk(int cin) { return cin % 64 == 0 ? 64 : cin % 32 == 0 ? 32 : 16; }
+}  // namespace
+
+int gemm_tile_bk(int tile, int cin, bool half) {
+  if (tile == TILE_S64x16 || tile == TILE_S64x32) return skinny_bk(cin);
+  if (half) return half_bk(cin);
+  return tile == TILE_128x128 || cin % 32 != 0 ? 16 : 32;
+}
 
 hipError_t launch_conv_gemm(const ConvParams& p, int tile, hipStream_t s) {
   const bool bk32 = (p.cin % 32) == 0;
@@ -642,15 +669,27 @@ hipError_t launch_conv_gemm(const ConvParams& p, int tile, hipStream_t s) {
       return bk32 ? launch_cfg<TileCfg<96, 128, 2, 4, 32, 0>>(p, s) : launch_cfg<TileCfg<96, 128, 2, 4, 16, 0>>(p, s);
     case TILE_256x128:
       return bk32 ? launch_cfg<TileCfg<256, 128, 4, 2, 32>>(p, s) : launch_cfg<TileCfg<256, 128, 4, 2, 16>>(p, s);
+    case TILE_S64x16:
+    case TILE_S64x32: {
+      // skinny: 4 waves stacked along M, one 16- or 32-row column block; a
+      // K-step moves 32 KB of weights, so a 256-deep group takes two round trips
+      const int bk = skinny_bk(p.cin);
+#define VOC_SKINNY(BN, WM, WN)                                                               \
+  return bk == 128 ? launch_cfg<TileCfg<64, BN, WM, WN, 128>>(p, s)                        \
+       : bk == 64  ? launch_cfg<TileCfg<64, BN, WM, WN, 64>>(p, s)                         \
+       : bk == 32  ? launch_cfg<TileCfg<64, BN, WM, WN, 32>>(p, s)                         \
+                   : launch_cfg<TileCfg<64, BN, WM, WN, 16>>(p, s)
+      if (tile == TILE_S64x16) VOC_SKINNY(16, 4, 1);
+      VOC_SKINNY(32, 4, 1);
+#undef VOC_SKINNY
+    }
   }
   return hipErrorInvalidValue;
 }
 
-int gemm_f16_bk(int cin) { return cin % 64 == 0 ? 64 : cin % 32 == 0 ? 32 : 16; }
-
 hipError_t launch_conv_gemm_f16(const ConvParams& p, int tile, hipStream_t s) {
   if (p.cin % 16 != 0) return hipErrorInvalidValue;
-  const int bk = gemm_f16_bk(p.cin);
+  const int bk = half_bk(p.cin);
   // (no interleaving hint with 16-wide slabs: iglp_opt(1) sends the compiler
   // into unbounded memory use on that instance)
 #define VOC_F16_CASES(BM, BN, WM, WN, IG)                                                           \
@@ -661,6 +700,19 @@ hipError_t launch_conv_gemm_f16(const ConvParams& p, int tile, hipStream_t s) {
     case TILE_128x128: VOC_F16_CASES(128, 128, 2, 4, 1);
     case TILE_96x128: VOC_F16_CASES(96, 128, 2, 4, 0);
     case TILE_64x64: VOC_F16_CASES(64, 64, 2, 2, -1);
+    case TILE_S64x16:
+    case TILE_S64x32: {
+      // the MFMA K (SLAB) follows the channel count exactly as above
+      const int sk = skinny_bk(p.cin);
+#define VOC_F16_SKINNY(BN, WM, WN)                                                           \
+  return sk == 128 ? launch_cfg<TileCfgH<64, BN, WM, WN, 128, 32>, true>(p, s)            \
+       : sk == 64  ? launch_cfg<TileCfgH<64, BN, WM, WN, 64, 32>, true>(p, s)             \
+       : sk == 32  ? launch_cfg<TileCfgH<64, BN, WM, WN, 32, 32>, true>(p, s)             \
+                   : launch_cfg<TileCfgH<64, BN, WM, WN, 16, 16, -1>, true>(p, s)
+      if (tile == TILE_S64x16) VOC_F16_SKINNY(16, 4, 1);
+      VOC_F16_SKINNY(32, 4, 1);
+#undef VOC_F16_SKINNY
+    }
   }
 #undef VOC_F16_CASES
   return hipErrorInvalidValue;

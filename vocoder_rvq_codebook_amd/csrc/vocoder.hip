@@ -453,10 +453,15 @@ class Prof {
   long long idx_ = -1;
 };
 
-// Tile per GEMM shape: 64x64 up to 2048 rows (transformer linears, the first
-// stages of short chunks), 96x128 when M is 96, 192 or 288 (BigVGAN stages
-// 3-4), 128x128 otherwise.  Launches with few tiles are split along K.
+// Tile per GEMM shape: skinny 64x16 / 64x32 tiles up to 32 rows (the
+// transformer and first stages of one- and two-frame chunks: weight streaming),
+// 64x64 up to 2048 rows (transformer linears, the first stages of short
+// chunks), 96x128 when M is 96, 192 or 288 (BigVGAN stages 3-4), 128x128
+// otherwise.  Launches with few tiles are split along K.  Every tile reduces
+// each output in the same order, so the choice never changes a bit.
 int pick_tile(int M, long long rows) {
+  if (rows <= 16) return TILE_S64x16;
+  if (rows <= 32) return TILE_S64x32;
   if (rows <= 2048) return TILE_64x64;
   if (M % 96 == 0 && M <= 288) return TILE_96x128;
   return TILE_128x128;
@@ -550,7 +555,7 @@ int run_gemm(const Ctx& cx, const ConvParams& pin) {
   if (f16) bytes -= 2.0 * p.M * K;  // fp16 weights
   char name[48];
   snprintf(name, sizeof(name), "conv_gemm_%s%dx%d_bk%d%s", f16 ? "f16_" : "", bm, gemm_tile_bn(tile),
-           f16 ? gemm_f16_bk(p.cin) : gemm_tile_bk(tile, p.cin), p.splits > 1 ? "_splitk" : "");
+           gemm_tile_bk(tile, p.cin, f16), p.splits > 1 ? "_splitk" : "");
   Prof pr(cx.v, cx.s, name, flops, bytes);
   if (f16)
     HIP_OK(launch_conv_gemm_f16(p, tile, cx.s));
