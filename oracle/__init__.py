@@ -14,6 +14,10 @@ from .decoder import (  # noqa: F401
     conv_transpose1d_causal,
     decode_chunk,
     decode_whole,
+    dequantize_rows_int8,
+    int8_eligible,
+    quantize_rows_int8,
+    quantize_weights_int8,
     gelu,
     layer_norm,
     new_state,

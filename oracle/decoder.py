@@ -40,6 +40,8 @@ routines torch.nn.functional.conv1d / conv_transpose1d / layer_norm / gelu /
 scaled_dot_product_attention on the CPU in float64, the zero-insertion +
 flipped-kernel identity, closed-form special values of Snake, RoPE's relative
 position invariance, and streamed == whole for several chunk schedules.  The
+int8 weight quantizer: a hand-worked group, ties to even, the half-step error
+bound, and the group layout.  The
 decoder as a whole against the real Qwen3-TTS checkpoint is parity unpinned:
 no trained weights or reference audio exist here.
 """
@@ -282,6 +284,89 @@ def transformer_layer(h, W, l, cache, positions, cfg, operands=None):
     h = h + linear(r(f), W[p + "fc2.weight"], W[p + "fc2.bias"])
     keep = min(Wn, K.shape[0])
     return h, (K[K.shape[0] - keep:].copy(), V[V.shape[0] - keep:].copy())
+
+
+# ---------------------------------------------------------------------------
+# int8 weights ("blixt/phonon", section Weights)
+# ---------------------------------------------------------------------------
+
+# A weight tensor of at least this many values is stored as int8 ...
+INT8_MIN_VALUES = 16384
+# ... with one fp16 scale per this many consecutive values of a row.
+INT8_GROUP = 32
+
+
+def quantize_rows_int8(rows):
+    """int8 values and fp16 scales of a [n][K] matrix, one scale per 32
+    consecutive values of a row (K a multiple of 32), as the phonon page's
+    weight converter does: round the values to fp16; the scale is the largest
+    magnitude of the 32 rounded values over 127, rounded to fp16; each value is
+    the nearest integer to value / scale, ties to even.  The scale and the
+    quotients are computed in fp32, the arithmetic the page's shaders use
+    (where floating point decides an integer, both implementations decide in
+    the same precision); a group of zeros gets scale 0 and values 0.
+
+    Returns (q int8 [n][K], scale float16 [n][K/32])."""
+    v = np.asarray(rows, dtype=np.float32).astype(np.float16).astype(np.float32)
+    n, K = v.shape
+    if K % INT8_GROUP:
+        raise ValueError("row length must be a multiple of 32")
+    g = v.reshape(n, K // INT8_GROUP, INT8_GROUP)
+    amax = np.abs(g).max(axis=2)
+    scale = (amax / np.float32(127)).astype(np.float16)
+    s = scale.astype(np.float32)[:, :, None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(s > 0, np.rint(g / np.where(s > 0, s, np.float32(1))), np.float32(0))
+    return q.astype(np.int8).reshape(n, K), scale
+
+
+def dequantize_rows_int8(q, scale):
+    """q * scale per group, in float64 (exact: 8-bit integer times fp16)."""
+    n, K = q.shape
+    out = q.astype(np.float64).reshape(n, K // INT8_GROUP, INT8_GROUP) * scale.astype(np.float64)[:, :, None]
+    return out.reshape(n, K)
+
+
+def _is_transposed_conv(name):
+    return name.startswith("ups.") or name.endswith(".up.weight")
+
+
+def int8_eligible(name, shape):
+    """Whether a weight is stored as int8: a matrix-product weight of at least
+    INT8_MIN_VALUES values whose rows (one output channel at one tap, along the
+    input channels) split into whole groups of 32."""
+    if not _is_contraction_weight(name) or int(np.prod(shape)) < INT8_MIN_VALUES:
+        return False
+    cin = shape[0] if _is_transposed_conv(name) else shape[1]
+    return cin % INT8_GROUP == 0
+
+
+def _rows_of(name, w):
+    """The weight as [rows][in]: Linear [out][in] as is; Conv1d [out][in][k]
+    and ConvTranspose1d [in][out][k] as [out][k][in] flattened to rows."""
+    if w.ndim == 2:
+        return w, lambda r: r
+    if _is_transposed_conv(name):
+        cin, cout, k = w.shape
+        return (np.ascontiguousarray(w.transpose(1, 2, 0)).reshape(cout * k, cin),
+                lambda r: r.reshape(cout, k, cin).transpose(2, 0, 1))
+    cout, cin, k = w.shape
+    return (np.ascontiguousarray(w.transpose(0, 2, 1)).reshape(cout * k, cin),
+            lambda r: r.reshape(cout, k, cin).transpose(0, 2, 1))
+
+
+def quantize_weights_int8(weights):
+    """The weights with every int8-eligible tensor replaced by its dequantized
+    values q * scale (float64, same shape); the others unchanged."""
+    out = {}
+    for name, w in weights.items():
+        w = np.asarray(w)
+        if int8_eligible(name, w.shape):
+            rows, back = _rows_of(name, w)
+            out[name] = np.ascontiguousarray(back(dequantize_rows_int8(*quantize_rows_int8(rows))))
+        else:
+            out[name] = w
+    return out
 
 
 def cast_operand_weights(weights, dtype, operands):

@@ -9,7 +9,9 @@ frames at the start and end), together with the norms of the full outputs.
 
 Names: qwen3_whole (the 250-frame whole-sequence workload, stream 0, which the
 streamed workload must also reproduce), qwen3_whole_f16 (the same with every
-matrix product's operands rounded to fp16, the half-precision decoder), qwen3_batched (streams 0-3 of the
+matrix product's operands rounded to fp16, the half-precision decoder),
+qwen3_whole_int8 (the same with the matrix weights stored as int8 with one
+fp16 scale per 32 values), qwen3_batched (streams 0-3 of the
 64-stream workload: their timed 25-frame chunk after warm-up), qwen3_longform
 (stream 0 of the 16 x 1500-frame Zipf workload).
 """
@@ -61,6 +63,15 @@ def main(names):
             codes = S.workload_codes("qwen3_b1_t250_whole")
             W16 = O.cast_operand_weights(W, np.float64, "f16")
             pcm, pre = decode_stream(cfg, W16, codes[0], 125, operands="f16")
+            idx = sample_index(pcm.size, hop, 61)
+            out.update(stream=np.array([0]), frame0=np.array([0]), frames=np.array([250]), idx=idx,
+                       pcm=pcm[idx], pre=pre[idx], pcm_norm=np.array([np.linalg.norm(pcm)]),
+                       pre_norm=np.array([np.linalg.norm(pre)]))
+        elif name == "qwen3_whole_int8":
+            # int8 weights (one fp16 scale per 32 values), arithmetic unrounded
+            codes = S.workload_codes("qwen3_b1_t250_whole")
+            W8 = O.quantize_weights_int8(W)
+            pcm, pre = decode_stream(cfg, W8, codes[0], 125)
             idx = sample_index(pcm.size, hop, 61)
             out.update(stream=np.array([0]), frame0=np.array([0]), frames=np.array([250]), idx=idx,
                        pcm=pcm[idx], pre=pre[idx], pcm_norm=np.array([np.linalg.norm(pcm)]),

@@ -136,3 +136,15 @@ def test_stored_full_size_values_are_consistent():
     for key in ("pre", "pcm"):
         rel = np.linalg.norm(g16[key] - g64[key]) / np.linalg.norm(g64[key])
         assert 1e-3 < rel < 5e-2, (key, rel)
+
+
+@pytest.mark.parametrize("schedule", [[1] * 12 + [28], [13, 27]])
+def test_int8_weights_streamed_equals_whole(mini, schedule):
+    cfg, W, codes, whole = mini
+    W8 = O.quantize_weights_int8(W)
+    whole8 = O.decode_whole(cfg, W8, codes)
+    got, _ = O.decode_schedule(cfg, W8, codes, schedule)
+    np.testing.assert_allclose(got, whole8, rtol=0, atol=1e-12)
+    # quantization moves the output, by int8 step error only
+    rel = np.linalg.norm(whole8 - whole) / np.linalg.norm(whole)
+    assert 1e-5 < rel < 5e-2

@@ -11,6 +11,7 @@ import pytest
 import torch
 import torch.nn.functional as F
 
+import synthetic as S
 from oracle import decoder as O
 
 RNG = np.random.default_rng(1234)
@@ -373,3 +374,117 @@ def test_operand_rounding_covers_exactly_the_contraction_weights():
                                                 or name.startswith("ups.") or name.endswith("up.weight"))
         is_gemm = is_gemm and not name.startswith("conv_post")
         assert rounded == is_gemm, name
+
+
+# ---------------------------------------------------------------------------
+# int8 weights (blixt/phonon, section Weights)
+# ---------------------------------------------------------------------------
+
+
+def test_int8_hand_worked_group():
+    """Largest magnitude 127/256: the scale is exactly 1/256, so every multiple
+    of 1/256 quantizes to its integer; halves go to the even neighbour."""
+    vals = np.array([127, -127, 0, 1, -1, 5, 63.5, 62.5, -2.5, 3.5, 0.5, -0.5, 1.5, 100, -64, 2]
+                    + [0] * 16, dtype=np.float64) / 256
+    q, s = O.quantize_rows_int8(vals[None, :])
+    assert s.dtype == np.float16 and s.shape == (1, 1) and float(s[0, 0]) == 1 / 256
+    expect = [127, -127, 0, 1, -1, 5, 64, 62, -2, 4, 0, 0, 2, 100, -64, 2] + [0] * 16
+    assert q.dtype == np.int8 and q[0].tolist() == expect
+    np.testing.assert_array_equal(O.dequantize_rows_int8(q, s)[0], np.array(expect) / 256)
+
+
+def test_int8_values_round_to_fp16_first():
+    """The scale comes from the fp16-rounded values: 1 + 2^-12 rounds to 1 in
+    fp16, so a group whose largest value is 1 + 2^-12 gets scale fp16(1/127)."""
+    g = np.zeros(32)
+    g[0] = 1 + 2.0 ** -12
+    q, s = O.quantize_rows_int8(g[None, :])
+    assert float(s[0, 0]) == float(np.float16(np.float32(1) / np.float32(127)))
+    assert q[0, 0] == 127
+
+
+def test_int8_error_bound_and_range():
+    rng = np.random.default_rng(5)
+    w = rng.normal(0, 0.02, size=(40, 256)) * rng.uniform(0.01, 10, size=(40, 1))
+    w[3, 32:64] = 0  # an all-zero group
+    q, s = O.quantize_rows_int8(w)
+    v16 = w.astype(np.float16).astype(np.float64)
+    deq = O.dequantize_rows_int8(q, s)
+    step = np.repeat(s.astype(np.float64), 32, axis=1)
+    # every value within half a step of its fp16 value, the largest of each group at +-127
+    assert np.all(np.abs(deq - v16) <= step / 2 * (1 + 1e-6))
+    gmax = np.abs(q.astype(np.int64)).reshape(40, 8, 32).max(axis=2)
+    assert np.all((gmax == 127) | (s == 0))
+    assert s[3, 1] == 0 and np.all(q[3, 32:64] == 0)
+    # the scale is the group maximum over 127 to fp16 precision (normal fp16
+    # scales; a scale below 2^-14 is subnormal and coarser, as fp16 is)
+    amax = np.abs(v16).reshape(40, 8, 32).max(axis=2)
+    normal = s.astype(np.float64) >= 2.0 ** -14
+    assert normal.sum() > 200
+    assert np.all(np.abs(s.astype(np.float64)[normal] * 127 / amax[normal] - 1) <= 2.0 ** -11)
+
+
+def test_int8_ties_to_even_against_brute_force():
+    """Brute force: for each value, the integer nearest to v/s by exhaustive
+    search over -127..127 (ties broken to the even integer)."""
+    rng = np.random.default_rng(6)
+    w = rng.normal(0, 1, size=(6, 64)).astype(np.float32)
+    w[:, 5] = np.float32(127.0) * 0.25  # group max fixes scale 0.25 ...
+    w[:, 0] = 0.25 * np.array([0.5, 1.5, 2.5, -0.5, -1.5, -3.5])  # ... and ties at exact halves
+    w[:, 1:5] = w[:, 6:10] = np.clip(w[:, 1:5], -30, 30)
+    w[:, 32:] = np.clip(w[:, 32:], -30, 30)
+    q, s = O.quantize_rows_int8(w)
+    cand = np.arange(-127, 128)
+    for r in range(w.shape[0]):
+        for k in range(w.shape[1]):
+            sc = np.float32(s[r, k // 32])
+            x = np.float32(np.float16(w[r, k])) / sc
+            d = np.abs(cand - np.float64(x))
+            best = cand[d == d.min()]
+            want = best[0] if len(best) == 1 else best[best % 2 == 0][0]
+            assert q[r, k] == want, (r, k, x)
+    assert q[:, 0].tolist() == [0, 2, 2, 0, -2, -4]
+
+
+def test_int8_groups_are_input_channels_at_one_output_and_tap():
+    """A single nonzero weight gives a nonzero scale to exactly its own group:
+    32 consecutive input channels of one output channel at one tap."""
+    cases = [("stages.0.blocks.0.0.conv1.weight", (8, 64, 3), (5, 40, 2)),   # Conv1d [out][in][k]
+             ("stages.0.up.weight", (64, 6, 4), (50, 3, 1)),                  # ConvTranspose1d [in][out][k]
+             ("layers.0.fc1.weight", (8, 64), (2, 33))]                        # Linear [out][in]
+    for name, shape, pos in cases:
+        w = np.zeros(shape)
+        w[pos] = 127 / 256  # scale exactly 1/256: the value dequantizes exactly
+        big = np.zeros((shape[0] * 4096,) + shape[1:])  # make it large enough to quantize
+        big[: shape[0]] = w
+        if O._is_transposed_conv(name):
+            big = np.zeros((shape[0], shape[1] * 64, shape[2]))
+            big[:, : shape[1]] = w
+        assert O.int8_eligible(name, big.shape)
+        out = O.quantize_weights_int8({name: big})[name]
+        np.testing.assert_array_equal(out, big)
+        rows, _ = O._rows_of(name, big)
+        _, s = O.quantize_rows_int8(rows)
+        assert np.count_nonzero(s) == 1
+        r, grp = np.argwhere(s)[0]
+        if len(shape) == 2:
+            assert (r, grp) == (pos[0], pos[1] // 32)
+        elif O._is_transposed_conv(name):
+            cin, cout, k = big.shape
+            assert (r, grp) == (pos[1] * k + pos[2], pos[0] // 32)
+        else:
+            cout, cin, k = big.shape
+            assert (r, grp) == (pos[0] * k + pos[2], pos[1] // 32)
+
+
+def test_int8_eligibility():
+    el = {n for n, sh, _ in S.manifest(S.QWEN3) if O.int8_eligible(n, sh)}
+    contraction = {n for n, sh, _ in S.manifest(S.QWEN3) if n.endswith(".weight") and len(sh) > 1
+                   and not n.startswith("conv_post")}
+    assert el == contraction and len(el) == 128
+    assert not O.int8_eligible("conv_post.weight", (1, 96, 7))
+    assert not O.int8_eligible("codebooks", (16, 2048, 512))
+    mini = {n for n, sh, _ in S.manifest(S.MINI) if O.int8_eligible(n, sh)}
+    assert "stages.1.blocks.0.0.conv1.weight" not in mini  # 64 x 64 x 3 = 12288 values
+    assert "stages.1.blocks.1.0.conv1.weight" in mini      # 64 x 64 x 7
+    assert "layers.0.q_proj.weight" not in mini            # 64 x 64
