@@ -1,6 +1,6 @@
 """Throughput of the streaming code2wav decoder on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--precision f32|f16] [--graph] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--precision f32|f16] [--weights float|int8] [--graph] [--no-cpu-baseline]
 
 A step decodes one 25-frame chunk (2 s of audio) for each of 64 independent
 streams whose states were first warmed (untimed) to different positions: the
@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--cpu-frames", type=int, default=100)
     ap.add_argument("--profile-chunk", type=int, default=0,
                     help="chunk-schedule workloads: add per-kernel device times of the chunks of this length")
+    ap.add_argument("--weights", choices=["float", "int8"], default="float",
+                    help="matrix weights stored as float, or int8 with one fp16 scale per 32 values")
     ap.add_argument("--graph", action="store_true",
                     help="chunk-schedule workloads: replay each call from a HIP graph")
     ap.add_argument("--precision", choices=["f32", "f16"], default="f32",
@@ -58,11 +60,13 @@ def parse():
 
 def _kernel_family(name):
     import re
-    m = re.search(r"TileCfg(H?)<(\d+), (\d+), \d+, \d+, (\d+)(?:, -?\d+)*\s*>(?:, (true|false))?", name)
+    m = re.search(r"TileCfg(H?)<(\d+), (\d+), \d+, \d+, (\d+)(?:, -?\d+)*\s*>(?:, (true|false))?"
+                  r"(?:, (true|false))?", name)
     if m:
         half = "f16_" if m.group(1) else ""
+        q8 = "q8_" if m.group(6) == "true" else ""
         split = "_splitk" if m.group(5) == "true" else ""
-        return f"conv_gemm_{half}{m.group(2)}x{m.group(3)}_bk{m.group(4)}{split}"
+        return f"conv_gemm_{half}{q8}{m.group(2)}x{m.group(3)}_bk{m.group(4)}{split}"
     m = re.search(r"(\w+)\(", name.replace("(anonymous namespace)::", ""))
     return m.group(1) if m else name[:40]
 
@@ -173,7 +177,7 @@ def stream_latency(args, wl, torch, S, Decoder, vb):
     """Streaming latency: decode the workload's chunk schedule for its streams
     (warm-up passes untimed), timing every chunk call with HIP events on the
     caller's stream.  Prints one JSON line (not the headline metric)."""
-    model = dict(wl["model"], precision=args.precision)
+    model = dict(wl["model"], precision=args.precision, weights=args.weights)
     sched = wl["schedule"]
     B = wl["batch"]
     W = S.make_weights(model, wl["weight_seed"])
@@ -263,7 +267,7 @@ def stream_latency(args, wl, torch, S, Decoder, vb):
     total = t.sum(axis=1)
     audio = sum(sched) * FRAME_SECONDS * B
     out = {"metric": "streaming chunk latency (ms) and audio-seconds/sec", "workload": args.workload,
-           "streams": B, "schedule": sched, "reps": args.steps, "graph": args.graph,
+           "streams": B, "schedule": sched, "reps": args.steps, "graph": args.graph, "weights": args.weights,
            "first_chunk_ms": round(float(per_chunk[0]), 3),
            "chunk_ms_median_by_length": {str(n): round(float(np.median(t[:, [i for i, m in enumerate(sched) if m == n]])), 3)
                                          for n in sorted(set(sched))},
@@ -324,7 +328,7 @@ def main():
         return
 
     wl = S.workload(args.workload)
-    model = dict(wl["model"], precision=args.precision)
+    model = dict(wl["model"], precision=args.precision, weights=args.weights)
     peak = FP16_MFMA_PEAK_TFLOPS if args.precision == "f16" else FP32_MFMA_PEAK_TFLOPS
     if isinstance(wl["schedule"], list):
         stream_latency(args, wl, torch, S, Decoder, vb)
@@ -395,7 +399,7 @@ def main():
         "vs_baseline": None,
         "dtype": args.precision,
         "data": "synthetic (seeded random-init weights, uniform random codes)",
-        "config": {"workload": args.workload, "streams": B, "frames_per_chunk": T,
+        "config": {"workload": args.workload, "streams": B, "frames_per_chunk": T, "weights": args.weights,
                    "samples_per_frame": dec.hop, "warm_positions": sorted(set(warm))},
         "tflops": round(flops_step / (elapsed / args.steps) / 1e12, 3),
         "mfma_frac": round(flops_step / (elapsed / args.steps) / 1e12 / peak, 4),

@@ -82,6 +82,7 @@ typedef struct vocoder_config {
   int32_t max_batch;        /* largest batch a decode call may pass (sizes the workspace) */
   int32_t max_frames;       /* largest n_frames a decode call may pass (sizes the workspace) */
   int32_t precision;        /* VOCODER_PRECISION_F32 (0) or VOCODER_PRECISION_F16 (1), see below */
+  int32_t weight_format;    /* VOCODER_WEIGHTS_FLOAT (0) or VOCODER_WEIGHTS_INT8 (1), see below */
 } vocoder_config;
 
 /* Arithmetic of the matrix products (every conv, transposed conv and linear
@@ -96,6 +97,22 @@ typedef struct vocoder_config {
  * interchangeable between the two. */
 #define VOCODER_PRECISION_F32 0
 #define VOCODER_PRECISION_F16 1
+
+/* Storage of the matrix-product weights.  FLOAT: fp32 (precision F32) or
+ * fp16 (F16).  INT8: the blixt/phonon page's weight format (section Weights):
+ * a weight tensor of 16,384 values or more becomes int8 with one fp16 scale per
+ * 32 values along its rows, the scale being max |value| / 127 of the 32 values
+ * after rounding them to fp16, and each value round(v / scale), ties to even;
+ * all arithmetic stays as `precision` says, on the dequantized value q * scale
+ * (exact in fp32; rounded to fp16 for F16).  Here a row is one output channel
+ * at one tap, its values the input channels, so the tensors quantized are the
+ * conv, transposed-conv and linear weights of at least 16,384 values whose
+ * input channel count is a multiple of 32 (all of them at the Qwen3-TTS-12Hz
+ * shape); the others, the codebooks, the vectors and the final C -> 1 conv
+ * keep their float storage.  Every such weight is read as 1.0625 bytes per
+ * value.  Weights must lie within the fp16 range. */
+#define VOCODER_WEIGHTS_FLOAT 0
+#define VOCODER_WEIGHTS_INT8 1
 
 typedef struct vocoder vocoder;
 
@@ -185,6 +202,13 @@ int vocoder_decode_chunk(vocoder* v, const int32_t* codes, int batch, int n_fram
  * vocoder_decode_chunk, and VOCODER_EHIP if recording or instantiation fails. */
 int vocoder_decode_chunk_graph(vocoder* v, const int32_t* codes, int batch, int n_frames,
                                const void* state_in, void* state_out, float* pcm, void* stream);
+
+/* The int8 weight quantizer vocoder_create applies (see VOCODER_WEIGHTS_INT8),
+ * on a caller's matrix: src fp32 [rows][K] (device, K a multiple of 32) ->
+ * q int8 [rows][K] and scale fp16 [rows][K/32] (device, IEEE binary16 bits),
+ * one scale per 32 consecutive values of a row.  Errors: VOCODER_EINVAL (null
+ * pointer, K not a positive multiple of 32, rows < 0), VOCODER_EHIP. */
+int vocoder_quantize_int8(const float* src, long long rows, int K, int8_t* q, uint16_t* scale, void* stream);
 
 /* Graphs the handle currently keeps (0..VOCODER_GRAPH_CACHE), -1 for NULL. */
 int vocoder_graph_cache_size(const vocoder* v);

@@ -33,8 +33,8 @@ def test_library_exports_every_declared_function():
 
 
 def test_config_struct_matches_header_layout():
-    # 8 int32 + 2 float + 2 int32 + 4 + 3 int32 + 8 + 1 + 4 + 1 + 4 + 4 int32
-    assert ctypes.sizeof(vb.VocoderConfig) == 4 * (8 + 2 + 2 + 4 + 3 + 8 + 1 + 4 + 1 + 4 + 4)
+    # 8 int32 + 2 float + 2 int32 + 4 + 3 int32 + 8 + 1 + 4 + 1 + 4 + 5 int32
+    assert ctypes.sizeof(vb.VocoderConfig) == 4 * (8 + 2 + 2 + 4 + 3 + 8 + 1 + 4 + 1 + 4 + 5)
 
 
 @pytest.mark.parametrize("model", [S.TINY, S.MINI, S.QWEN3], ids=lambda m: m["name"])
@@ -83,6 +83,8 @@ def test_null_arguments_rejected_before_any_device_call():
     assert L.vocoder_graph_cache_size(None) == -1
     assert L.vocoder_prefill(None, 256, 1, 1, 256, 512, None) == vb.VOCODER_EINVAL
     assert L.vocoder_prefill_tail_frames(None) == 0
+    assert L.vocoder_quantize_int8(None, 1, 32, 256, 256, None) == vb.VOCODER_EINVAL
+    assert L.vocoder_quantize_int8(256, 1, 48, 256, 256, None) == vb.VOCODER_EINVAL
     assert L.vocoder_reset(None, 256, 1, None) == vb.VOCODER_EINVAL
     assert L.vocoder_get_status(None, None) == vb.VOCODER_EINVAL
     assert L.vocoder_hop(None) == 0
@@ -117,3 +119,19 @@ def test_f16_precision_halves_gemm_weight_bytes():
     assert vb.vocoder_packed_weights_bytes(bad) == 0
     with pytest.raises(ValueError):
         vb.make_config(dict(S.QWEN3, precision="bf16"), 1, 1)
+
+
+def test_int8_weights_shrink_the_packed_weights():
+    f32 = vb.make_config(S.QWEN3, 1, 1)
+    q8 = vb.make_config(dict(S.QWEN3, weights="int8"), 1, 1)
+    q8h = vb.make_config(dict(S.QWEN3, weights="int8", precision="f16"), 1, 1)
+    assert q8.weight_format == 1 and f32.weight_format == 0
+    b32, b8, b8h = (vb.vocoder_packed_weights_bytes(c) for c in (f32, q8, q8h))
+    # 1.0625 bytes per matrix weight value instead of 4; the codebooks (67 MB) stay fp32
+    assert b8 == b8h and 0.3 * b32 < b8 < 0.35 * b32
+    assert vb.vocoder_state_bytes(q8) == vb.vocoder_state_bytes(f32)
+    bad = vb.make_config(S.QWEN3, 1, 1)
+    bad.weight_format = 2
+    assert vb.vocoder_packed_weights_bytes(bad) == 0
+    with pytest.raises(ValueError):
+        vb.make_config(dict(S.QWEN3, weights="int4"), 1, 1)

@@ -51,10 +51,12 @@ class VocoderConfig(ctypes.Structure):
         ("max_batch", ctypes.c_int32),
         ("max_frames", ctypes.c_int32),
         ("precision", ctypes.c_int32),
+        ("weight_format", ctypes.c_int32),
     ]
 
 
 PRECISIONS = {"f32": 0, "f16": 1}
+WEIGHT_FORMATS = {"float": 0, "int8": 1}
 
 
 class VocoderKernelStat(ctypes.Structure):
@@ -99,6 +101,8 @@ def lib():
         L.vocoder_decode_chunk_graph.restype = i32
         L.vocoder_graph_cache_size.argtypes = [vp]
         L.vocoder_graph_cache_size.restype = i32
+        L.vocoder_quantize_int8.argtypes = [vp, ctypes.c_longlong, i32, vp, vp, vp]
+        L.vocoder_quantize_int8.restype = i32
         L.vocoder_prefill.argtypes = [vp, vp, i32, i32, vp, vp, vp]
         L.vocoder_prefill.restype = i32
         L.vocoder_prefill_tail_frames.argtypes = [vp]
@@ -145,6 +149,10 @@ def make_config(model: dict, max_batch: int, max_frames: int) -> VocoderConfig:
     if prec not in PRECISIONS:
         raise ValueError(f"precision must be one of {sorted(PRECISIONS)}")
     c.precision = PRECISIONS[prec]
+    wf = model.get("weights", "float")
+    if wf not in WEIGHT_FORMATS:
+        raise ValueError(f"weights must be one of {sorted(WEIGHT_FORMATS)}")
+    c.weight_format = WEIGHT_FORMATS[wf]
     return c
 
 
@@ -210,6 +218,10 @@ def vocoder_decode_chunk_graph(handle, codes, batch, n_frames, state_in, state_o
 
 def vocoder_graph_cache_size(handle) -> int:
     return lib().vocoder_graph_cache_size(handle)
+
+
+def vocoder_quantize_int8(src, rows, K, q, scale, stream=None) -> int:
+    return lib().vocoder_quantize_int8(_ptr(src), int(rows), int(K), _ptr(q), _ptr(scale), _stream(stream))
 
 
 def vocoder_prefill(handle, codes, batch, n_frames, state_in, state_out, stream=None) -> int:

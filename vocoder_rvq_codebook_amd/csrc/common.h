@@ -26,7 +26,8 @@ enum { MRF_NONE = 0, MRF_FIRST = 1, MRF_ACCUM = 2, MRF_LAST = 3, MRF_ONLY = 4 };
 enum { ACT_NONE = 0, ACT_GELU = 1 };
 
 struct ConvParams {
-  const float* w;       // packed [Mpad][k][cin]
+  const float* w;       // packed [Mpad][k][cin] (fp32, fp16, or int8 when wscale is set)
+  const void* wscale;   // int8 weights: fp16 scales [Mpad][k*cin/32], else nullptr
   int M;                // GEMM columns (= phases * cout)
   int k, cin, dil;
   const float* x;       // [rows][cin]
@@ -92,10 +93,7 @@ struct Slot {
 // tile configuration ids for the implicit-GEMM kernel
 // TILE_S64x16 / TILE_S64x32: skinny tiles for launches of a few rows (small
 // chunks), 128-deep K-steps so that few load round trips cover a group.
-enum GemmTile {
-  TILE_128x128 = 0, TILE_96x256 = 1, TILE_192x128 = 2, TILE_64x64 = 3, TILE_96x128 = 4, TILE_256x128 = 5,
-  TILE_S64x16 = 6, TILE_S64x32 = 7, TILE_COUNT = 8
-};
+enum GemmTile { TILE_128x128 = 0, TILE_64x64 = 1, TILE_96x128 = 2, TILE_S64x16 = 3, TILE_S64x32 = 4, TILE_COUNT = 5 };
 int gemm_tile_bm(int tile);
 int gemm_tile_bn(int tile);
 int gemm_tile_bk(int tile, int cin, bool half);
@@ -126,6 +124,8 @@ hipError_t launch_repack_conv(const float* src, void* dst, int M, int Mpad, int 
 hipError_t launch_repack_convT(const float* src, void* dst, int cin, int cout, int stride, int Mpad,
                                bool half_out, hipStream_t s);
 hipError_t launch_expand_vec(const float* src, float* dst, int C, int phases, int Mpad, hipStream_t s);
+// int8 with one fp16 scale per 32 values of each row of a [rows][K] fp32 matrix
+hipError_t launch_quantize_rows(const float* src, long long rows, int K, void* q, void* scale, hipStream_t s);
 hipError_t launch_fill(void* dst, size_t bytes, hipStream_t s);
 hipError_t launch_reset_headers(void* state, long long sstride, int batch, uint64_t cfg_hash,
                                 hipStream_t s);

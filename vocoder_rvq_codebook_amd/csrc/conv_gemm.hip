@@ -44,6 +44,13 @@ struct TileCfg {
   static_assert(BK % 16 == 0, "BK must be a multiple of 16");
 };
 
+// 4 int8 weights (one 32-bit word) times their group's scale, in fp32 (exact:
+// an 8-bit integer times an fp16 value).
+__device__ __forceinline__ f32x4 dequant4(int w, float sc) {
+  return (f32x4){(float)((w << 24) >> 24) * sc, (float)((w << 16) >> 24) * sc, (float)((w << 8) >> 24) * sc,
+                 (float)(w >> 24) * sc};
+}
+
 // Snake x + sin^2(a x)/a.  The sine is the hardware instruction (argument in
 // revolutions) applied to the angle reduced to [-1/2, 1/2] revolution: the
 // subtraction of the nearest integer is exact, so the only angle error is the
@@ -134,7 +141,7 @@ __device__ __forceinline__ f32x4 fold_groups(const ConvParams& p, int m, int g, 
 // unreduced, to p.partial[group][row][M]; splitk_reduce_kernel then folds the
 // groups in order and runs the same epilogue.  Every group's partial is the
 // same MFMA chain in both modes, so both modes give the same bits.
-template <class C, bool SPLIT>
+template <class C, bool SPLIT, bool Q8>
 __global__ __launch_bounds__(C::NT) void conv_gemm_kernel(const ConvParams p) {
   __shared__ __attribute__((aligned(16))) float As[2][C::BM * C::LDK];
   __shared__ __attribute__((aligned(16))) float Bs[2][C::BN * C::LDK];
@@ -186,14 +193,23 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_kernel(const ConvParams p) {
   // before the chunk reads the stream's history slot instead: both bases are
   // kept and selected per step, without branches.  Rows past the end clamp to
   // the last row (their outputs are never stored).
+  // int8 weights use the same slots: 4 values (one word) and their scale
   const float* a_base[C::A_LD];
-  int a_lds[C::A_LD];
+  const int8_t* q_base[C::A_LD];
+  const _Float16* s_base[C::A_LD];
+  int a_lds[C::A_LD], q_col[C::A_LD];
+  const size_t ktot = (size_t)p.k * cin;
 #pragma unroll
   for (int i = 0; i < C::A_LD; ++i) {
     int idx = tid + i * C::NT;
     if (C::A_F4 % C::NT != 0 && idx >= C::A_F4) idx = C::A_F4 - 1;  // duplicate load, same value
     const int row = idx / C::KV, col = (idx % C::KV) * 4;
-    a_base[i] = p.w + (size_t)(m0 + row) * p.k * cin + col;
+    a_base[i] = p.w + (size_t)(m0 + row) * ktot + col;
+    if constexpr (Q8) {
+      q_base[i] = reinterpret_cast<const int8_t*>(p.w) + (size_t)(m0 + row) * ktot + col;
+      s_base[i] = reinterpret_cast<const _Float16*>(p.wscale) + (size_t)(m0 + row) * (ktot / 32);
+    }
+    q_col[i] = col;
     a_lds[i] = row * C::LDK + col;
   }
   const float* bx[C::B_LD];
@@ -214,6 +230,8 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_kernel(const ConvParams p) {
   }
 
   f32x4 ra[C::A_LD], rb[C::B_LD];
+  int rq[C::A_LD];
+  float rs[C::A_LD];
 
   auto gload = [&](int s) {
     const int tap = s / ksteps_per_tap;
@@ -221,14 +239,27 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_kernel(const ConvParams p) {
     const int shift = (p.k - 1 - tap) * p.dil;
     const ptrdiff_t aoff = (ptrdiff_t)tap * cin + c0;
     const ptrdiff_t boff = c0 - (ptrdiff_t)shift * cin;
+    if constexpr (Q8) {
 #pragma unroll
-    for (int i = 0; i < C::A_LD; ++i) ra[i] = ld4(a_base[i] + aoff);
+      for (int i = 0; i < C::A_LD; ++i) {
+        rq[i] = *reinterpret_cast<const int*>(q_base[i] + aoff);
+        rs[i] = (float)s_base[i][(aoff + q_col[i]) >> 5];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::A_LD; ++i) ra[i] = ld4(a_base[i] + aoff);
+    }
 #pragma unroll
     for (int i = 0; i < C::B_LD; ++i) rb[i] = ld4((bn[i] >= shift ? bx[i] : bh[i]) + boff);
   };
   auto lstore = [&](int buf) {
+    if constexpr (Q8) {
 #pragma unroll
-    for (int i = 0; i < C::A_LD; ++i) st4(&As[buf][a_lds[i]], ra[i]);
+      for (int i = 0; i < C::A_LD; ++i) st4(&As[buf][a_lds[i]], dequant4(rq[i], rs[i]));
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::A_LD; ++i) st4(&As[buf][a_lds[i]], ra[i]);
+    }
 #pragma unroll
     for (int i = 0; i < C::B_LD; ++i) st4(&Bs[buf][b_lds[i]], rb[i]);
   };
@@ -380,7 +411,7 @@ __device__ __forceinline__ f16x8 to_half8(f32x4 lo, f32x4 hi) {
   return r;
 }
 
-template <class C, bool SPLIT>
+template <class C, bool SPLIT, bool Q8>
 __global__ __launch_bounds__(C::NT) void conv_gemm_f16_kernel(const ConvParams p) {
   __shared__ __attribute__((aligned(16))) _Float16 As[2][C::BM * C::LDK];
   __shared__ __attribute__((aligned(16))) _Float16 Bs[2][C::BN * C::LDK];
@@ -423,14 +454,23 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_f16_kernel(const ConvParams p
     if (s_begin >= nsteps) return;
   }
 
+  // int8 weights use the same slots: 8 values (two words) and their scale
   const _Float16* a_base[C::A_LD];
-  int a_lds[C::A_LD];
+  const int8_t* q_base[C::A_LD];
+  const _Float16* s_base[C::A_LD];
+  int a_lds[C::A_LD], q_col[C::A_LD];
+  const size_t ktot = (size_t)p.k * cin;
 #pragma unroll
   for (int i = 0; i < C::A_LD; ++i) {
     int idx = tid + i * C::NT;
     if (C::A_CH % C::NT != 0 && idx >= C::A_CH) idx = C::A_CH - 1;
     const int row = idx / C::KC, col = (idx % C::KC) * 8;
-    a_base[i] = W + (size_t)(m0 + row) * p.k * cin + col;
+    a_base[i] = W + (size_t)(m0 + row) * ktot + col;
+    if constexpr (Q8) {
+      q_base[i] = reinterpret_cast<const int8_t*>(p.w) + (size_t)(m0 + row) * ktot + col;
+      s_base[i] = reinterpret_cast<const _Float16*>(p.wscale) + (size_t)(m0 + row) * (ktot / 32);
+    }
+    q_col[i] = col;
     a_lds[i] = row * C::LDK + col;
   }
   const float* bx[C::B_LD];
@@ -452,6 +492,8 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_f16_kernel(const ConvParams p
 
   f32x4 ra[C::A_LD];
   f32x4 rb_lo[C::B_LD], rb_hi[C::B_LD];
+  int2 rq[C::A_LD];
+  float rs[C::A_LD];
 
   auto gload = [&](int s) {
     const int tap = s / ksteps_per_tap;
@@ -459,8 +501,16 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_f16_kernel(const ConvParams p
     const int shift = (p.k - 1 - tap) * p.dil;
     const ptrdiff_t aoff = (ptrdiff_t)tap * cin + c0;
     const ptrdiff_t boff = c0 - (ptrdiff_t)shift * cin;
+    if constexpr (Q8) {
 #pragma unroll
-    for (int i = 0; i < C::A_LD; ++i) ra[i] = *reinterpret_cast<const f32x4*>(a_base[i] + aoff);
+      for (int i = 0; i < C::A_LD; ++i) {
+        rq[i] = *reinterpret_cast<const int2*>(q_base[i] + aoff);
+        rs[i] = (float)s_base[i][(aoff + q_col[i]) >> 5];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::A_LD; ++i) ra[i] = *reinterpret_cast<const f32x4*>(a_base[i] + aoff);
+    }
 #pragma unroll
     for (int i = 0; i < C::B_LD; ++i) {
       const float* src = (bn[i] >= shift ? bx[i] : bh[i]) + boff;
@@ -469,8 +519,16 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_f16_kernel(const ConvParams p
     }
   };
   auto lstore = [&](int buf) {
+    if constexpr (Q8) {
+      // q * scale is exact in fp32; one rounding to fp16 as for float weights
 #pragma unroll
-    for (int i = 0; i < C::A_LD; ++i) *reinterpret_cast<f32x4*>(&As[buf][a_lds[i]]) = ra[i];
+      for (int i = 0; i < C::A_LD; ++i)
+        *reinterpret_cast<f16x8*>(&As[buf][a_lds[i]]) =
+            to_half8(dequant4(rq[i].x, rs[i]), dequant4(rq[i].y, rs[i]));
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::A_LD; ++i) *reinterpret_cast<f32x4*>(&As[buf][a_lds[i]]) = ra[i];
+    }
 #pragma unroll
     for (int i = 0; i < C::B_LD; ++i) *reinterpret_cast<f16x8*>(&Bs[buf][b_lds[i]]) = to_half8(rb_lo[i], rb_hi[i]);
   };
@@ -580,8 +638,8 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_f16_kernel(const ConvParams p
   }
 }
 
-template <class C, bool HALF = false>
-hipError_t launch_cfg(const ConvParams& p, hipStream_t s) {
+template <class C, bool HALF, bool Q8>
+hipError_t launch_cfg_q(const ConvParams& p, hipStream_t s) {
   const int mtiles = (p.M + C::BM - 1) / C::BM;
   const int ntiles = (p.rows + C::BN - 1) / C::BN;
   const long long tiles = (long long)mtiles * ntiles;
@@ -589,17 +647,17 @@ hipError_t launch_cfg(const ConvParams& p, hipStream_t s) {
   if (p.splits <= 1) {
     if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
     if constexpr (HALF)
-      hipLaunchKernelGGL((conv_gemm_f16_kernel<C, false>), dim3((unsigned)tiles), dim3(C::NT), 0, s, p);
+      hipLaunchKernelGGL((conv_gemm_f16_kernel<C, false, Q8>), dim3((unsigned)tiles), dim3(C::NT), 0, s, p);
     else
-      hipLaunchKernelGGL((conv_gemm_kernel<C, false>), dim3((unsigned)tiles), dim3(C::NT), 0, s, p);
+      hipLaunchKernelGGL((conv_gemm_kernel<C, false, Q8>), dim3((unsigned)tiles), dim3(C::NT), 0, s, p);
     return hipGetLastError();
   }
   const long long nb = tiles * p.splits;
   if (nb > 0x7fffffffLL || !p.partial) return hipErrorInvalidValue;
   if constexpr (HALF)
-    hipLaunchKernelGGL((conv_gemm_f16_kernel<C, true>), dim3((unsigned)nb), dim3(C::NT), 0, s, p);
+    hipLaunchKernelGGL((conv_gemm_f16_kernel<C, true, Q8>), dim3((unsigned)nb), dim3(C::NT), 0, s, p);
   else
-    hipLaunchKernelGGL((conv_gemm_kernel<C, true>), dim3((unsigned)nb), dim3(C::NT), 0, s, p);
+    hipLaunchKernelGGL((conv_gemm_kernel<C, true, Q8>), dim3((unsigned)nb), dim3(C::NT), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int ngroups = (p.k * p.cin + GROUP_K - 1) / GROUP_K;
@@ -608,16 +666,20 @@ hipError_t launch_cfg(const ConvParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// int8 weights (p.wscale set) or float weights
+template <class C, bool HALF = false>
+hipError_t launch_cfg(const ConvParams& p, hipStream_t s) {
+  if (p.wscale) return launch_cfg_q<C, HALF, true>(p, s);
+  return launch_cfg_q<C, HALF, false>(p, s);
+}
+
 }  // namespace
 
 int gemm_tile_bm(int tile) {
   switch (tile) {
     case TILE_128x128: return 128;
-    case TILE_96x256: return 96;
-    case TILE_192x128: return 192;
     case TILE_64x64: return 64;
     case TILE_96x128: return 96;
-    case TILE_256x128: return 256;
     case TILE_S64x16: return 64;
     case TILE_S64x32: return 64;
   }
@@ -627,11 +689,8 @@ int gemm_tile_bm(int tile) {
 int gemm_tile_bn(int tile) {
   switch (tile) {
     case TILE_128x128: return 128;
-    case TILE_96x256: return 256;
-    case TILE_192x128: return 128;
     case TILE_64x64: return 64;
     case TILE_96x128: return 128;
-    case TILE_256x128: return 128;
     case TILE_S64x16: return 16;
     case TILE_S64x32: return 32;
   }
@@ -658,17 +717,11 @@ hipError_t launch_conv_gemm(const ConvParams& p, int tile, hipStream_t s) {
       // TFLOP/s; 4 waves of 64x64 at BK = 32 fit one wave per SIMD and reach
       // 101).  The reduction order does not depend on BK or the wave layout.
       return launch_cfg<TileCfg<128, 128, 2, 4, 16, 1>>(p, s);
-    case TILE_96x256:
-      return bk32 ? launch_cfg<TileCfg<96, 256, 1, 4, 32>>(p, s) : launch_cfg<TileCfg<96, 256, 1, 4, 16>>(p, s);
-    case TILE_192x128:
-      return bk32 ? launch_cfg<TileCfg<192, 128, 2, 2, 32>>(p, s) : launch_cfg<TileCfg<192, 128, 2, 2, 16>>(p, s);
     case TILE_64x64:
       return bk32 ? launch_cfg<TileCfg<64, 64, 2, 2, 32>>(p, s) : launch_cfg<TileCfg<64, 64, 2, 2, 16>>(p, s);
     case TILE_96x128:
       // 8 waves of 48x32: four waves per SIMD
       return bk32 ? launch_cfg<TileCfg<96, 128, 2, 4, 32, 0>>(p, s) : launch_cfg<TileCfg<96, 128, 2, 4, 16, 0>>(p, s);
-    case TILE_256x128:
-      return bk32 ? launch_cfg<TileCfg<256, 128, 4, 2, 32>>(p, s) : launch_cfg<TileCfg<256, 128, 4, 2, 16>>(p, s);
     case TILE_S64x16:
     case TILE_S64x32: {
       // skinny: 4 waves stacked along M, one 16- or 32-row column block; a

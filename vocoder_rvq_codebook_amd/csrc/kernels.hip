@@ -385,6 +385,41 @@ __global__ void repack_convT_kernel(const float* __restrict__ src, T* __restrict
   dst[idx] = (T)v;
 }
 
+// int8 quantization of one group of 32 consecutive values of a row ("blixt/
+// phonon", section Weights): the values rounded to fp16, scale = fp16(max |v| /
+// 127), each value rint(v / scale) (ties to even); divisions correctly rounded
+// in fp32; a zero group keeps scale 0 and values 0.  One thread per group.
+__global__ void quantize_rows_kernel(const float* __restrict__ src, long long groups, int8_t* __restrict__ q,
+                                     _Float16* __restrict__ scale) {
+  const long long gi = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gi >= groups) return;
+  const float* x = src + gi * 32;
+  float v[32];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    v[i] = (float)(_Float16)x[i];
+    amax = fmaxf(amax, fabsf(v[i]));
+  }
+  const _Float16 sh = (_Float16)__fdiv_rn(amax, 127.0f);
+  const float sc = (float)sh;
+  uint32_t words[8];
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    uint32_t packed = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int qi = sc > 0.f ? (int)rintf(__fdiv_rn(v[4 * w + b], sc)) : 0;
+      packed |= (uint32_t)(qi & 0xff) << (8 * b);
+    }
+    words[w] = packed;
+  }
+  uint4* qd = reinterpret_cast<uint4*>(q + gi * 32);
+  qd[0] = make_uint4(words[0], words[1], words[2], words[3]);
+  qd[1] = make_uint4(words[4], words[5], words[6], words[7]);
+  scale[gi] = sh;
+}
+
 // per-channel vector [C] -> [Mpad] indexed by GEMM column m = p*C + c
 __global__ void expand_vec_kernel(const float* __restrict__ src, float* __restrict__ dst, int C, int phases,
                                   int Mpad) {
@@ -498,6 +533,15 @@ hipError_t launch_repack_convT(const float* src, void* dst, int cin, int cout, i
   else
     hipLaunchKernelGGL(repack_convT_kernel<float>, dim3(cdiv(n, 256)), dim3(256), 0, s, src, (float*)dst, cin, cout,
                        stride, Mpad);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_rows(const float* src, long long rows, int K, void* q, void* scale, hipStream_t s) {
+  if (K <= 0 || K % 32 != 0 || rows < 0) return hipErrorInvalidValue;
+  const long long groups = rows * (K / 32);
+  if (groups == 0) return hipSuccess;
+  hipLaunchKernelGGL(quantize_rows_kernel, dim3((unsigned)cdiv(groups, 256)), dim3(256), 0, s, src, groups,
+                     (int8_t*)q, (_Float16*)scale);
   return hipGetLastError();
 }
 

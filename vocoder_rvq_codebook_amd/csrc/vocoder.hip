@@ -63,6 +63,7 @@ bool config_valid(const vocoder_config* c) {
   }
   if (c->max_batch < 1 || c->max_frames < 1) return false;
   if (c->precision != VOCODER_PRECISION_F32 && c->precision != VOCODER_PRECISION_F16) return false;
+  if (c->weight_format != VOCODER_WEIGHTS_FLOAT && c->weight_format != VOCODER_WEIGHTS_INT8) return false;
   // every GEMM row count must fit in int
   long long hop = 1;
   for (int i = 0; i < c->n_up; ++i) hop *= c->up_strides[i];
@@ -100,9 +101,15 @@ int hop_of(const vocoder_config& c) {
 
 struct GemmW {
   long long w = -1, bias = -1;  // packed float offsets
+  long long scale = -1;         // int8 weights: fp16 scales (packed float offset)
   long long raw_w = -1, raw_b = -1;
   int M = 0, Mpad = 0, k = 1, cin = 0, phases = 1, cout = 0;
+  bool q8 = false;              // weights stored as int8 with one fp16 scale per 32
 };
+
+// Tensors of at least this many values whose input channel count is a
+// multiple of 32 are stored as int8 ("blixt/phonon", section Weights).
+constexpr long long INT8_MIN_VALUES = 16384;
 
 struct LayerP {
   long long ln1_g, ln1_b, ln2_g, ln2_b;         // packed
@@ -132,6 +139,7 @@ struct Plan {
   vocoder_config cfg{};
   int d = 0, hd = 0, half = 0, hop = 0;
   bool f16 = false;  // fp16 GEMM operands (packed weights in fp16)
+  long long max_gemm_values = 0;  // largest packed GEMM weight (values)
   long long raw_count = 0;
   // packed
   long long raw_codebooks = 0, codebooks = 0;
@@ -191,7 +199,9 @@ bool make_plan(const vocoder_config* cp, Plan& P) {
   long long raw = 0, pk = 0;
   auto R = [&](long long n) { long long o = raw; raw += n; return o; };
   auto K = [&](long long n) { long long o = pk; pk += align_up(n); return o; };
-  auto gemm = [&](GemmW& g, int M, int k, int cin, int phases, int cout) {
+  // tensor_values: values of the source tensor (one of q, k, v for the stacked
+  // projection), which decides int8 storage
+  auto gemm = [&](GemmW& g, int M, int k, int cin, int phases, int cout, long long tensor_values) {
     g.M = M;
     g.Mpad = round_up_i(M, 128);
     g.k = k;
@@ -199,8 +209,15 @@ bool make_plan(const vocoder_config* cp, Plan& P) {
     g.phases = phases;
     g.cout = cout;
     const long long welems = (long long)g.Mpad * k * cin;
-    g.w = K(P.f16 ? (welems + 1) / 2 : welems);  // fp16 weights take half the floats
+    g.q8 = c.weight_format == VOCODER_WEIGHTS_INT8 && tensor_values >= INT8_MIN_VALUES && cin % 32 == 0;
+    if (g.q8) {
+      g.w = K((welems + 3) / 4);          // int8 values
+      g.scale = K((welems / 32 + 1) / 2);  // fp16 scales, one per 32 values
+    } else {
+      g.w = K(P.f16 ? (welems + 1) / 2 : welems);  // fp16 weights take half the floats
+    }
     g.bias = K(g.Mpad);
+    P.max_gemm_values = std::max(P.max_gemm_values, welems);
   };
 
   P.state_floats = VOC_STATE_HEADER_FLOATS;
@@ -208,7 +225,7 @@ bool make_plan(const vocoder_config* cp, Plan& P) {
   // codebooks and pre-conv
   P.raw_codebooks = R((long long)c.n_codebooks * c.codebook_size * De);
   P.codebooks = K((long long)c.n_codebooks * c.codebook_size * De);
-  gemm(P.pre, d, c.pre_kernel, De, 1, d);
+  gemm(P.pre, d, c.pre_kernel, De, 1, d, (long long)d * De * c.pre_kernel);
   P.pre.raw_w = R((long long)d * De * c.pre_kernel);
   P.pre.raw_b = R(d);
   P.slot_pre = add_slot(P, c.pre_kernel - 1, De, 1);
@@ -221,14 +238,14 @@ bool make_plan(const vocoder_config* cp, Plan& P) {
     L.raw_q_w = R((long long)d * d); L.raw_q_b = R(d);
     L.raw_k_w = R((long long)d * d); L.raw_k_b = R(d);
     L.raw_v_w = R((long long)d * d); L.raw_v_b = R(d);
-    gemm(L.o, d, 1, d, 1, d);
+    gemm(L.o, d, 1, d, 1, d, (long long)d * d);
     L.o.raw_w = R((long long)d * d); L.o.raw_b = R(d);
     L.raw_ln2_g = R(d); L.raw_ln2_b = R(d);
-    gemm(L.fc1, F, 1, d, 1, F);
+    gemm(L.fc1, F, 1, d, 1, F, (long long)F * d);
     L.fc1.raw_w = R((long long)F * d); L.fc1.raw_b = R(F);
-    gemm(L.fc2, d, 1, F, 1, d);
+    gemm(L.fc2, d, 1, F, 1, d, (long long)d * F);
     L.fc2.raw_w = R((long long)d * F); L.fc2.raw_b = R(d);
-    gemm(L.qkv, 3 * d, 1, d, 1, 3 * d);
+    gemm(L.qkv, 3 * d, 1, d, 1, 3 * d, (long long)d * d);
     L.ln1_g = K(d); L.ln1_b = K(d); L.ln2_g = K(d); L.ln2_b = K(d);
     L.slot_k = add_slot(P, c.window, d, 1);
     L.slot_v = add_slot(P, c.window, d, 1);
@@ -243,7 +260,7 @@ bool make_plan(const vocoder_config* cp, Plan& P) {
   P.ups.resize(c.n_up);
   for (int i = 0; i < c.n_up; ++i) {
     const int s = c.up_strides[i];
-    gemm(P.ups[i], s * d, 2, d, s, d);
+    gemm(P.ups[i], s * d, 2, d, s, d, (long long)d * d * 2 * s);
     P.ups[i].raw_w = R((long long)d * d * 2 * s);
     P.ups[i].raw_b = R(d);
     P.slot_ups.push_back(add_slot(P, 1, d, rate));
@@ -251,7 +268,7 @@ bool make_plan(const vocoder_config* cp, Plan& P) {
   }
   // conv_pre
   const int C0 = c.voc_ch0;
-  gemm(P.conv_pre, C0, c.conv_pre_kernel, d, 1, C0);
+  gemm(P.conv_pre, C0, c.conv_pre_kernel, d, 1, C0, (long long)C0 * d * c.conv_pre_kernel);
   P.conv_pre.raw_w = R((long long)C0 * d * c.conv_pre_kernel);
   P.conv_pre.raw_b = R(C0);
   P.slot_conv_pre = add_slot(P, c.conv_pre_kernel - 1, d, rate);
@@ -265,7 +282,7 @@ bool make_plan(const vocoder_config* cp, Plan& P) {
     S.cin = cin;
     S.c = co;
     S.r = r;
-    gemm(S.up, r * co, 2, cin, r, co);
+    gemm(S.up, r * co, 2, cin, r, co, (long long)cin * co * 2 * r);
     S.up.raw_w = R((long long)cin * co * 2 * r);
     S.up.raw_b = R(co);
     S.slot_up = add_slot(P, 1, cin, rate);
@@ -277,11 +294,11 @@ bool make_plan(const vocoder_config* cp, Plan& P) {
       for (int i = 0; i < c.n_dil; ++i) {
         AmpP& A = S.amp[(size_t)j * c.n_dil + i];
         A.raw_act1 = R(co);
-        gemm(A.conv1, co, k, co, 1, co);
+        gemm(A.conv1, co, k, co, 1, co, (long long)co * co * k);
         A.conv1.raw_w = R((long long)co * co * k);
         A.conv1.raw_b = R(co);
         A.raw_act2 = R(co);
-        gemm(A.conv2, co, k, co, 1, co);
+        gemm(A.conv2, co, k, co, 1, co, (long long)co * co * k);
         A.conv2.raw_w = R((long long)co * co * k);
         A.conv2.raw_b = R(co);
         A.act1 = K(co);
@@ -338,6 +355,9 @@ bool make_plan(const vocoder_config* cp, Plan& P) {
   P.partial_floats = 32LL << 20;
   P.ws_partial = Wk(P.partial_floats);
   P.ws_floats = ws;
+  // int8 weights are quantized at create time from a float repack staged in
+  // the workspace
+  if (c.weight_format == VOCODER_WEIGHTS_INT8) P.ws_floats = std::max(P.ws_floats, align_up(P.max_gemm_values));
   {
     // Walk back from conv_post's carried rows: a causal conv of kernel k and
     // dilation d reaches (k-1)*d input rows further back, an AMP block the sum
@@ -482,6 +502,7 @@ ConvParams base_params(const Ctx& cx, const GemmW& g, const float* x, int rows, 
   const Plan& P = cx.v->P;
   ConvParams p{};
   p.w = cx.v->packed + g.w;
+  p.wscale = g.q8 ? (const void*)(cx.v->packed + g.scale) : nullptr;
   p.M = g.M;
   p.k = g.k;
   p.cin = g.cin;
@@ -552,9 +573,11 @@ int run_gemm(const Ctx& cx, const ConvParams& pin) {
   if (p.resid) bytes += 4.0 * p.rows * p.M;
   if (p.mrf_mode == MRF_ACCUM || p.mrf_mode == MRF_LAST) bytes += 4.0 * p.rows * p.M;
   const bool f16 = cx.v->P.f16;
-  if (f16) bytes -= 2.0 * p.M * K;  // fp16 weights
+  if (p.wscale) bytes -= (4.0 - 1.0625) * p.M * K;  // int8 weights and their scales
+  else if (f16) bytes -= 2.0 * p.M * K;             // fp16 weights
   char name[48];
-  snprintf(name, sizeof(name), "conv_gemm_%s%dx%d_bk%d%s", f16 ? "f16_" : "", bm, gemm_tile_bn(tile),
+  snprintf(name, sizeof(name), "conv_gemm_%s%s%dx%d_bk%d%s", f16 ? "f16_" : "", p.wscale ? "q8_" : "", bm,
+           gemm_tile_bn(tile),
            gemm_tile_bk(tile, p.cin, f16), p.splits > 1 ? "_splitk" : "");
   Prof pr(cx.v, cx.s, name, flops, bytes);
   if (f16)
@@ -572,15 +595,25 @@ void tap(const Ctx& cx, const char* name, const float* src, long long count) {
   (void)hipMemcpyAsync(it->second.first, src, (size_t)count * sizeof(float), hipMemcpyDeviceToDevice, cx.s);
 }
 
+// int8 weights: the float repack goes to the (still unused) workspace, then
+// each [Mpad][k*cin] row is quantized per 32 values into the packed region.
+int quantize_packed(vocoder* v, const GemmW& g, hipStream_t s) {
+  HIP_OK(launch_quantize_rows(v->ws, g.Mpad, g.k * g.cin, v->packed + g.w, v->packed + g.scale, s));
+  return VOCODER_OK;
+}
+
 int repack_gemm(vocoder* v, const float* raw, const GemmW& g, bool transposed, hipStream_t s) {
   float* pk = v->packed;
+  void* dst = g.q8 ? (void*)v->ws : (void*)(pk + g.w);
+  const bool half = v->P.f16 && !g.q8;
   if (transposed) {
-    HIP_OK(launch_repack_convT(raw + g.raw_w, pk + g.w, g.cin, g.cout, g.phases, g.Mpad, v->P.f16, s));
+    HIP_OK(launch_repack_convT(raw + g.raw_w, dst, g.cin, g.cout, g.phases, g.Mpad, half, s));
     HIP_OK(launch_expand_vec(raw + g.raw_b, pk + g.bias, g.cout, g.phases, g.Mpad, s));
   } else {
-    HIP_OK(launch_repack_conv(raw + g.raw_w, pk + g.w, g.M, g.Mpad, g.cin, g.k, v->P.f16, s));
+    HIP_OK(launch_repack_conv(raw + g.raw_w, dst, g.M, g.Mpad, g.cin, g.k, half, s));
     HIP_OK(launch_expand_vec(raw + g.raw_b, pk + g.bias, g.M, 1, g.Mpad, s));
   }
+  if (g.q8) return quantize_packed(v, g, s);
   return VOCODER_OK;
 }
 
@@ -657,9 +690,19 @@ int vocoder_create(const vocoder_config* cfg, const float* raw_weights, void* pa
     const long long raw_b[3] = {L.raw_q_b, L.raw_k_b, L.raw_v_b};
     for (int t = 0; t < 3; ++t) {
       const long long off = (long long)t * d * d;  // elements
-      void* dst = P.f16 ? (void*)(reinterpret_cast<_Float16*>(pk + L.qkv.w) + off) : (void*)(pk + L.qkv.w + off);
-      if (launch_repack_conv(raw + raw_w[t], dst, d, d, d, 1, P.f16, s) != hipSuccess) return fail(VOCODER_EHIP);
+      void* dst = L.qkv.q8 ? (void*)(v->ws + off)
+                  : P.f16  ? (void*)(reinterpret_cast<_Float16*>(pk + L.qkv.w) + off)
+                           : (void*)(pk + L.qkv.w + off);
+      if (launch_repack_conv(raw + raw_w[t], dst, d, d, d, 1, P.f16 && !L.qkv.q8, s) != hipSuccess)
+        return fail(VOCODER_EHIP);
       if ((rc = copy_d2d(pk + L.qkv.bias + (long long)t * d, raw + raw_b[t], d, s))) return fail(rc);
+    }
+    if (L.qkv.q8) {
+      // rows past the three stacked projections are padding: zero
+      const long long used = 3LL * d * d, all = (long long)L.qkv.Mpad * d;
+      if (all > used && launch_fill(v->ws + used, (size_t)(all - used) * 4, s) != hipSuccess)
+        return fail(VOCODER_EHIP);
+      if ((rc = quantize_packed(v, L.qkv, s))) return fail(rc);
     }
     if ((rc = repack_gemm(v, raw, L.o, false, s))) return fail(rc);
     if ((rc = repack_gemm(v, raw, L.fc1, false, s))) return fail(rc);
@@ -1030,6 +1073,12 @@ int vocoder_decode_chunk_graph(vocoder* v, const int32_t* codes, int batch, int 
   }
   v->graphs.push_back({key, exec, v->graph_clock});
   HIP_OK(hipGraphLaunch(exec, (hipStream_t)stream));
+  return VOCODER_OK;
+}
+
+int vocoder_quantize_int8(const float* src, long long rows, int K, int8_t* q, uint16_t* scale, void* stream) {
+  if (!src || !q || !scale || rows < 0 || K <= 0 || K % 32 != 0) return VOCODER_EINVAL;
+  HIP_OK(launch_quantize_rows(src, rows, K, q, scale, (hipStream_t)stream));
   return VOCODER_OK;
 }
 
