@@ -1,0 +1,135 @@
+"""GPU parity of int8 weights (weight_format = int8): the device quantizer
+against the oracle's bit for bit, then decodes with int8 weights against the
+oracle run on the dequantized weights (the same model, exactly representable),
+at small shapes stage by stage and at full size against stored values."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import synthetic as S
+from oracle import decoder as O
+from tests.gpu_util import PCM_MAX_ABS, REL_L2, check_close, decoder, run_schedule, weights
+from tests.test_gpu_parity import _stage_names, _tap_rows
+from vocoder_rvq_codebook_amd import binding as vb
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+F16_BAR = 2e-3  # fp16 operands: as for float weights in fp16 mode
+
+
+def q8(model, precision="f32"):
+    return dict(model, name=f"{model['name']}_q8_{precision}", weights="int8", precision=precision)
+
+
+def _gpu_quantize(x):
+    rows, K = x.shape
+    src = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+    q = torch.empty((rows, K), dtype=torch.int8, device="cuda")
+    sc = torch.empty((rows, K // 32), dtype=torch.int16, device="cuda")
+    assert vb.vocoder_quantize_int8(src, rows, K, q, sc) == vb.VOCODER_OK
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), sc.cpu().numpy().view(np.float16)
+
+
+def test_device_quantizer_equals_oracle_bitwise():
+    rng = np.random.default_rng(12)
+    x = rng.normal(0, 0.02, size=(300, 512)) * rng.uniform(1e-3, 50, size=(300, 1))
+    x[7, 64:96] = 0                              # zero group
+    x[8, :32] = 127 / 256 * np.array([1] + [0.5 / 127, 1.5 / 127, 2.5 / 127, -2.5 / 127] + [0] * 27)  # ties
+    x[9, :] = rng.normal(0, 1e-7, size=512)      # subnormal fp16 scales
+    q, s = _gpu_quantize(x)
+    q0, s0 = O.quantize_rows_int8(x)
+    np.testing.assert_array_equal(s.view(np.uint16), s0.view(np.uint16))
+    np.testing.assert_array_equal(q, q0)
+    assert q[8, :5].tolist() == [127, 0, 2, 2, -2]
+
+
+def test_device_quantizer_on_weights():
+    """The decoder's own weight tensors (as [rows][in]) quantize identically."""
+    W = weights(S.MINI, 3)[0]
+    for name in ("stages.0.up.weight", "conv_pre.weight", "stages.0.blocks.2.1.conv2.weight"):
+        rows, _ = O._rows_of(name, W[name])
+        q, s = _gpu_quantize(rows)
+        q0, s0 = O.quantize_rows_int8(rows)
+        np.testing.assert_array_equal(q, q0)
+        np.testing.assert_array_equal(s.view(np.uint16), s0.view(np.uint16))
+
+
+@pytest.mark.parametrize("precision", ["f32", "f16"])
+@pytest.mark.parametrize("T", [13, 1])
+def test_int8_stage_by_stage(precision, T):
+    model = q8(S.MINI, precision)
+    operands = "f16" if precision == "f16" else None
+    bar = F16_BAR if operands else REL_L2
+    B = 2
+    dec, W = decoder(model, 5, B, 32)
+    W8 = O.quantize_weights_int8(O.cast_weights(W, np.float64))
+    warm = [0, 9]
+    codes = S.make_codes(model, B, max(warm) + T, 79)
+    states = dec.new_state(B)
+    for b, nw in enumerate(warm):
+        if nw:
+            _, st2 = run_schedule(dec, codes[b:b + 1, :nw], [nw], state=states[b:b + 1].clone())
+            states[b:b + 1].copy_(st2)
+    chunk = np.stack([codes[b, nw:nw + T] for b, nw in enumerate(warm)])
+    taps = {}
+    for name in _stage_names(model):
+        rows, ch = _tap_rows(model, name, T)
+        taps[name] = torch.full((B * rows * ch,), float("nan"), device="cuda")
+        dec.set_tap(name, taps[name])
+    pcm, _ = run_schedule(dec, chunk, [T], state=states)
+    assert dec.status() == vb.VOCODER_OK
+    last = len(model["rates"]) - 1
+    Wop = O.cast_operand_weights(W8, np.float64, operands)
+    for b, nw in enumerate(warm):
+        ref_taps = {}
+        st = O.new_state(model)
+        if nw:
+            _, st = O.decode_chunk(model, Wop, codes[b, :nw], st, np.float64, None, operands)
+        ref, _ = O.decode_chunk(model, Wop, codes[b, nw:nw + T], st, np.float64, ref_taps, operands)
+        for name in _stage_names(model):
+            rows, ch = _tap_rows(model, name, T)
+            got = taps[name].view(B, rows * ch)[b].cpu().numpy()
+            r = ref_taps[name]
+            if name == f"stage{last}":
+                r = O.snake(r, W["act_post.alpha"].astype(np.float64))
+            check_close(got, r.reshape(-1), f"int8 {precision} stream {b} {name}", rel=bar)
+        check_close(pcm[b].cpu().numpy(), ref, f"int8 {precision} stream {b} pcm", rel=bar,
+                    max_abs=None if operands else PCM_MAX_ABS)
+    for name in taps:
+        dec.set_tap(name, None)
+
+
+def test_int8_streamed_equals_whole_bitwise():
+    model = q8(S.MINI)
+    dec, _ = decoder(model, 9, 2, 41)
+    codes = S.make_codes(model, 2, 41, 33)
+    whole, st_w = run_schedule(dec, codes, [41])
+    parts, st_p = run_schedule(dec, codes, [1, 1, 2, 4, 8, 25])
+    assert torch.equal(whole, parts) and torch.equal(st_w, st_p)
+
+
+def test_int8_full_size_250_frames():
+    """fp32 arithmetic on int8 weights: the spec bar against the oracle
+    run on the same dequantized weights."""
+    print("\n[int8 full] 250-frame whole-sequence decode", flush=True)
+    path = os.path.join(GOLDEN, "qwen3_whole_int8.npz")
+    assert os.path.exists(path), f"missing {path}: run tests/golden/make_golden.py qwen3_whole_int8"
+    g = dict(np.load(path))
+    model = q8(S.QWEN3)
+    dec, _ = decoder(model, 1, 1, 250)
+    codes = S.workload_codes("qwen3_b1_t250_whole")
+    pre = torch.empty(250 * model["hop"], device="cuda")
+    dec.set_tap("pre_tanh", pre)
+    pcm, _ = run_schedule(dec, codes, [250])
+    dec.set_tap("pre_tanh", None)
+    assert dec.status() == vb.VOCODER_OK
+    pcm = pcm[0].cpu().numpy().astype(np.float64)
+    pre = pre.cpu().numpy().astype(np.float64)
+    idx = g["idx"]
+    check_close(pcm[idx], g["pcm"], "int8 250 frames pcm", rel=REL_L2, max_abs=PCM_MAX_ABS)
+    check_close(pre[idx], g["pre"], "int8 250 frames pre-tanh", rel=REL_L2)
+    assert abs(np.linalg.norm(pre) / g["pre_norm"][0] - 1) < 1e-5
