@@ -20,6 +20,7 @@ struct EpiOut {
   float* hist;          // state_out slot of stream 0 ([H][cout]) or nullptr
   int H;                // slot rows
   int src;              // 0: the conv value v, 1: the multi-receptive-field value s
+  int half;             // store dst as fp16 (a tensor read only as an fp16 GEMM operand)
 };
 
 enum { MRF_NONE = 0, MRF_FIRST = 1, MRF_ACCUM = 2, MRF_LAST = 3, MRF_ONLY = 4 };
@@ -30,7 +31,8 @@ struct ConvParams {
   const void* wscale;   // int8 weights: fp16 scales [Mpad][k*cin/32], else nullptr
   int M;                // GEMM columns (= phases * cout)
   int k, cin, dil;
-  const float* x;       // [rows][cin]
+  const float* x;       // [rows][cin], fp32 or (x_half) fp16
+  int x_half;           // x holds fp16 values (fp16-operand kernel only); history rows stay fp32
   const float* hin;     // state_in slot of stream 0 ([hin_rows][cin])
   long long sstride;    // state floats per stream
   int hin_rows;         // (k-1)*dil history rows

@@ -24,6 +24,9 @@
 
 namespace {
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
 // IGLP_: the compiler's MFMA/LDS interleaving strategy for the K-step body
 // (__builtin_amdgcn_iglp_opt), or -1 for none; chosen per tile by measurement.
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int IGLP_ = -1>
@@ -106,7 +109,13 @@ __device__ __forceinline__ void epilogue4(const ConvParams& p, int m, int g, f32
       val.x = snake1(val.x, a.x); val.y = snake1(val.y, a.y);
       val.z = snake1(val.z, a.z); val.w = snake1(val.w, a.w);
     }
-    if (eo.dst) st4(eo.dst + oidx, val);
+    if (eo.dst) {
+      if (eo.half)
+        *reinterpret_cast<f16x4*>(reinterpret_cast<_Float16*>(eo.dst) + oidx) =
+            (f16x4){(_Float16)val.x, (_Float16)val.y, (_Float16)val.z, (_Float16)val.w};
+      else
+        st4(eo.dst + oidx, val);
+    }
     if (eo.hist && no >= nout_rows - eo.H) {
       st4(eo.hist + (size_t)b * p.sstride + (size_t)(eo.H - nout_rows + no) * p.cout + c, val);
     }
@@ -174,6 +183,7 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_kernel(const ConvParams p) {
   const int g0 = nt * C::BN;
 
   const int cin = p.cin;
+  const int ktaps = p.k, dil = p.dil;  // (lambdas below read locals, not the by-value argument)
   const int ksteps_per_tap = cin / C::BK;
   const int nsteps_all = p.k * ksteps_per_tap;
   constexpr int GROUP_STEPS = GROUP_K / C::BK;
@@ -236,7 +246,7 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_kernel(const ConvParams p) {
   auto gload = [&](int s) {
     const int tap = s / ksteps_per_tap;
     const int c0 = (s - tap * ksteps_per_tap) * C::BK;
-    const int shift = (p.k - 1 - tap) * p.dil;
+    const int shift = (ktaps - 1 - tap) * dil;
     const ptrdiff_t aoff = (ptrdiff_t)tap * cin + c0;
     const ptrdiff_t boff = c0 - (ptrdiff_t)shift * cin;
     if constexpr (Q8) {
@@ -381,8 +391,6 @@ __global__ void splitk_reduce_kernel(const ConvParams p, int ngroups) {
 // lane) for channel counts that are multiples of 16 only.  A K-step covers BK
 // halves; the accumulation groups (GROUP_K values) and split-K are as above.
 // ---------------------------------------------------------------------------
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int SLAB_, int IGLP_ = -1>
 struct TileCfgH {
@@ -442,6 +450,7 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_f16_kernel(const ConvParams p
   const int g0 = nt * C::BN;
 
   const int cin = p.cin;
+  const int ktaps = p.k, dil = p.dil;  // (lambdas below read locals, not the by-value argument)
   const int ksteps_per_tap = cin / C::BK;
   const int nsteps_all = p.k * ksteps_per_tap;
   constexpr int GROUP_STEPS = GROUP_K / C::BK;
@@ -473,8 +482,10 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_f16_kernel(const ConvParams p
     q_col[i] = col;
     a_lds[i] = row * C::LDK + col;
   }
-  const float* bx[C::B_LD];
+  const char* bxb[C::B_LD];  // row of x (fp32 or fp16 elements), as bytes
   const float* bh[C::B_LD];
+  const bool x_half = p.x_half != 0;
+  const int x_esz = x_half ? 2 : 4;
   int bn[C::B_LD], b_lds[C::B_LD];
 #pragma unroll
   for (int i = 0; i < C::B_LD; ++i) {
@@ -485,20 +496,24 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_f16_kernel(const ConvParams p
     const int b = g / p.nin;
     const int n = g - b * p.nin;
     bn[i] = n;
-    bx[i] = p.x + (size_t)g * cin + col;
-    bh[i] = p.hin ? p.hin + (size_t)b * p.sstride + (ptrdiff_t)(p.hin_rows + n) * cin + col : bx[i];
+    bxb[i] = reinterpret_cast<const char*>(p.x) + ((size_t)g * cin + col) * x_esz;
+    bh[i] = p.hin ? p.hin + (size_t)b * p.sstride + (ptrdiff_t)(p.hin_rows + n) * cin + col
+                  : reinterpret_cast<const float*>(bxb[i]);
     b_lds[i] = row * C::LDK + col;
   }
 
   f32x4 ra[C::A_LD];
+  // B: 8 fp32 values (rb_lo, rb_hi) or, for an fp16 input row, the 8 halves'
+  // bits in rb_lo (bhalf set); rounded / stored as fp16 at the LDS store
   f32x4 rb_lo[C::B_LD], rb_hi[C::B_LD];
+  int b_shift = 0;  // tap shift of the staged step
   int2 rq[C::A_LD];
   float rs[C::A_LD];
 
   auto gload = [&](int s) {
     const int tap = s / ksteps_per_tap;
     const int c0 = (s - tap * ksteps_per_tap) * C::BK;
-    const int shift = (p.k - 1 - tap) * p.dil;
+    const int shift = (ktaps - 1 - tap) * dil;
     const ptrdiff_t aoff = (ptrdiff_t)tap * cin + c0;
     const ptrdiff_t boff = c0 - (ptrdiff_t)shift * cin;
     if constexpr (Q8) {
@@ -511,11 +526,18 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_f16_kernel(const ConvParams p
 #pragma unroll
       for (int i = 0; i < C::A_LD; ++i) ra[i] = *reinterpret_cast<const f32x4*>(a_base[i] + aoff);
     }
+    b_shift = shift;
 #pragma unroll
     for (int i = 0; i < C::B_LD; ++i) {
-      const float* src = (bn[i] >= shift ? bx[i] : bh[i]) + boff;
-      rb_lo[i] = ld4(src);
-      rb_hi[i] = ld4(src + 4);
+      // branch-free: an fp16 row needs one 16-byte load (its second load
+      // repeats the first address), an fp32 row two
+      const bool fromx = bn[i] >= shift;
+      const bool hx = x_half && fromx;
+      const char* src = hx      ? bxb[i] + boff * 2
+                        : fromx ? bxb[i] + boff * 4
+                                : reinterpret_cast<const char*>(bh[i] + boff);
+      rb_lo[i] = *reinterpret_cast<const f32x4*>(src);
+      rb_hi[i] = *reinterpret_cast<const f32x4*>(hx ? src : src + 16);
     }
   };
   auto lstore = [&](int buf) {
@@ -530,7 +552,10 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_f16_kernel(const ConvParams p
       for (int i = 0; i < C::A_LD; ++i) *reinterpret_cast<f32x4*>(&As[buf][a_lds[i]]) = ra[i];
     }
 #pragma unroll
-    for (int i = 0; i < C::B_LD; ++i) *reinterpret_cast<f16x8*>(&Bs[buf][b_lds[i]]) = to_half8(rb_lo[i], rb_hi[i]);
+    for (int i = 0; i < C::B_LD; ++i)
+      *reinterpret_cast<f16x8*>(&Bs[buf][b_lds[i]]) = (x_half && bn[i] >= b_shift)
+                                                          ? __builtin_bit_cast(f16x8, rb_lo[i])
+                                                          : to_half8(rb_lo[i], rb_hi[i]);
   };
 
   // Lane l supplies A[l%16][k] and B[k][l%16] for the PER_LANE values of k

@@ -527,11 +527,13 @@ ConvParams base_params(const Ctx& cx, const GemmW& g, const float* x, int rows, 
   return p;
 }
 
-void add_out(const Ctx& cx, ConvParams& p, float* dst, const float* alpha, int hslot, int src = 0) {
+void add_out(const Ctx& cx, ConvParams& p, float* dst, const float* alpha, int hslot, int src = 0,
+             bool half = false) {
   EpiOut& o = p.out[p.nout++];
   o.dst = dst;
   o.alpha = alpha;
   o.src = src;
+  o.half = half ? 1 : 0;
   if (hslot >= 0) {
     o.hist = cx.sout + cx.v->P.slots[hslot].off;
     o.H = cx.v->P.slots[hslot].H;
@@ -569,7 +571,9 @@ int run_gemm(const Ctx& cx, const ConvParams& pin) {
   if (p.hin_rows < (p.k - 1) * p.dil) return VOCODER_EINVAL;
   const double K = (double)p.k * p.cin;
   const double flops = 2.0 * p.M * K * p.rows;
-  double bytes = 4.0 * ((double)p.M * K + (double)p.rows * p.cin + (double)p.nout * p.rows * p.M);
+  double bytes = 4.0 * (double)p.M * K + (p.x_half ? 2.0 : 4.0) * (double)p.rows * p.cin;
+  for (int o = 0; o < p.nout; ++o)
+    if (p.out[o].dst) bytes += (p.out[o].half ? 2.0 : 4.0) * (double)p.rows * p.M;
   if (p.resid) bytes += 4.0 * p.rows * p.M;
   if (p.mrf_mode == MRF_ACCUM || p.mrf_mode == MRF_LAST) bytes += 4.0 * p.rows * p.M;
   const bool f16 = cx.v->P.f16;
@@ -951,8 +955,9 @@ int decode_launches(vocoder* v, const int32_t* codes, int batch, int n_frames, c
     {
       ConvParams p = base_params(cx, S.up, S_in, (int)(B * nin), (int)nin, 1, S.slot_up);
       add_out(cx, p, X0, nullptr, -1);
+      // Snake outputs are read only as GEMM operands: fp16 in fp16 mode
       for (int j = 0; j < c.n_res; ++j)
-        add_out(cx, p, ws + P.ws_A[j], pk + S.up_alpha[j], S.amp[(size_t)j * c.n_dil].slot1);
+        add_out(cx, p, ws + P.ws_A[j], pk + S.up_alpha[j], S.amp[(size_t)j * c.n_dil].slot1, 0, P.f16);
       CHECK(run_gemm(cx, p));
     }
     nin *= S.r;
@@ -970,17 +975,19 @@ int decode_launches(vocoder* v, const int32_t* codes, int batch, int n_frames, c
         // conv(k, d) of Snake_1(x), then Snake_2
         {
           ConvParams p = base_params(cx, A.conv1, a_in, rows, (int)nin, c.dilations[i], A.slot1);
-          add_out(cx, p, Tb, pk + A.act2, A.slot2);
+          p.x_half = P.f16;
+          add_out(cx, p, Tb, pk + A.act2, A.slot2, 0, P.f16);
           CHECK(run_gemm(cx, p));
         }
         // conv(k, 1) + residual
         {
           ConvParams p = base_params(cx, A.conv2, Tb, rows, (int)nin, 1, A.slot2);
+          p.x_half = P.f16;
           p.resid = i == 0 ? X0 : Xr;
           if (i + 1 < c.n_dil) {
             const AmpP& An1 = S.amp[(size_t)j * c.n_dil + i + 1];
             add_out(cx, p, Xr, nullptr, -1);
-            add_out(cx, p, An, pk + An1.act1, An1.slot1);
+            add_out(cx, p, An, pk + An1.act1, An1.slot1, 0, P.f16);
           } else {
             p.mrf = S_out;
             p.mrf_div = (float)c.n_res;
