@@ -392,10 +392,12 @@ __global__ void splitk_reduce_kernel(const ConvParams p, int ngroups) {
 // halves; the accumulation groups (GROUP_K values) and split-K are as above.
 // ---------------------------------------------------------------------------
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int SLAB_, int IGLP_ = -1>
+// WPE_: minimum waves per SIMD the register allocation must allow (1 = no
+// constraint), chosen per tile by measurement.
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int SLAB_, int IGLP_ = -1, int WPE_ = 1>
 struct TileCfgH {
   static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, BK = BK_, SLAB = SLAB_,
-                       IGLP = IGLP_;
+                       IGLP = IGLP_, WPE = WPE_;
   static constexpr int NT = WAVES_M * WAVES_N * 64;
   static constexpr int WTM = BM / WAVES_M;
   static constexpr int WTN = BN / WAVES_N;
@@ -420,7 +422,8 @@ __device__ __forceinline__ f16x8 to_half8(f32x4 lo, f32x4 hi) {
 }
 
 template <class C, bool SPLIT, bool Q8>
-__global__ __launch_bounds__(C::NT) void conv_gemm_f16_kernel(const ConvParams p) {
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE))) void conv_gemm_f16_kernel(
+    const ConvParams p) {
   __shared__ __attribute__((aligned(16))) _Float16 As[2][C::BM * C::LDK];
   __shared__ __attribute__((aligned(16))) _Float16 Bs[2][C::BN * C::LDK];
   const _Float16* W = reinterpret_cast<const _Float16*>(p.w);
@@ -729,7 +732,7 @@ int half_bk(int cin) { return cin % 64 == 0 ? 64 : cin % 32 == 0 ? 32 : 16; }
 
 int gemm_tile_bk(int tile, int cin, bool half) {
   if (tile == TILE_S64x16 || tile == TILE_S64x32) return skinny_bk(cin);
-  if (half) return half_bk(cin);
+  if (half) return tile == TILE_128x128 ? std::min(half_bk(cin), 32) : half_bk(cin);
   return tile == TILE_128x128 || cin % 32 != 0 ? 16 : 32;
 }
 
@@ -775,8 +778,15 @@ hipError_t launch_conv_gemm_f16(const ConvParams& p, int tile, hipStream_t s) {
        : bk == 32 ? launch_cfg<TileCfgH<BM, BN, WM, WN, 32, 32, IG>, true>(p, s)                    \
                   : launch_cfg<TileCfgH<BM, BN, WM, WN, 16, 16, -1>, true>(p, s)
   switch (tile) {
-    case TILE_128x128: VOC_F16_CASES(128, 128, 2, 4, 1);
-    case TILE_96x128: VOC_F16_CASES(96, 128, 2, 4, 0);
+    case TILE_128x128:
+      // at most 32-deep K-steps: fewer staging registers, two blocks per CU
+      return bk >= 32 ? launch_cfg<TileCfgH<128, 128, 2, 4, 32, 32, 1>, true>(p, s)
+                      : launch_cfg<TileCfgH<128, 128, 2, 4, 16, 16, -1>, true>(p, s);
+    case TILE_96x128:
+      // 64-deep K-steps with registers allocated for four waves per SIMD
+      return bk == 64 ? launch_cfg<TileCfgH<96, 128, 2, 4, 64, 32, 0, 4>, true>(p, s)
+           : bk == 32 ? launch_cfg<TileCfgH<96, 128, 2, 4, 32, 32, 0>, true>(p, s)
+                      : launch_cfg<TileCfgH<96, 128, 2, 4, 16, 16, -1>, true>(p, s);
     case TILE_64x64: VOC_F16_CASES(64, 64, 2, 2, -1);
     case TILE_S64x16:
     case TILE_S64x32: {
