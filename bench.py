@@ -98,13 +98,15 @@ def traffic_summary(gemm_fetch, gemm_write, copy_fetch, copy_write, copy_bytes):
     `copy_bytes` reads and writes exactly that many bytes."""
     import csv
 
-    def per_kernel(path, counter):
+    def per_kernel(paths, counter):
+        # paths: one CSV, or several joined by commas (e.g. an fp32 and an fp16 run)
         out = {}
-        for r in csv.DictReader(open(path)):
-            if r["Counter_Name"] != counter:
-                continue
-            k = _kernel_family(r["Kernel_Name"])
-            out.setdefault(k, []).append(float(r["Counter_Value"]) * 1024.0)
+        for path in paths.split(","):
+            for r in csv.DictReader(open(path)):
+                if r["Counter_Name"] != counter:
+                    continue
+                k = _kernel_family(r["Kernel_Name"])
+                out.setdefault(k, []).append(float(r["Counter_Value"]) * 1024.0)
         return out
 
     cf = per_kernel(copy_fetch, "FETCH_SIZE")
