@@ -387,9 +387,9 @@ def main():
                for k, v in sorted(prof.items(), key=lambda kv: -kv[1]["total_ms"])}
 
     out = {
-        "metric": "audio-seconds/sec (x real-time) for 64 x 25-frame chunks; % fp32 MFMA peak"
+        "metric": "audio-seconds/sec (\u00d7real-time) for 64\u00d725-frame chunks; % fp32 MFMA peak"
                   if args.precision == "f32" else
-                  "audio-seconds/sec (x real-time) for 64 x 25-frame chunks, fp16 operands; % fp16 MFMA peak",
+                  "audio-seconds/sec (\u00d7real-time) for 64\u00d725-frame chunks, fp16 operands; % fp16 MFMA peak",
         "value": round(value, 3),
         "unit": "audio-s/s",
         "n_gpus": 1,

@@ -346,6 +346,74 @@ __global__ __launch_bounds__(POST_ROWS) void conv_post_kernel(
   pcm[g] = tanhf(acc);
 }
 
+// The same conv for a kernel size known at compile time, reading every input
+// row from HBM once: thread t of a block sums its own input row against all K
+// taps (K dot products over the channels, each a fused multiply-add chain in
+// channel order), the block exchanges the tap sums through LDS, and output
+// sample g adds bias + sum over taps j of the sum of row g-(K-1)+j, in tap
+// order -- the operations and order of conv_post_kernel, so the same bits.
+// A block covers POST_T input rows and emits the POST_T-(K-1) samples whose
+// rows it holds; a tap reaching before the stream's chunk is summed from the
+// history slot in place.
+constexpr int POST_T = 256;
+
+template <int K>
+__global__ __launch_bounds__(POST_T) void conv_post_rows_kernel(
+    const float* __restrict__ x, const float* __restrict__ hin, long long sstride, int H,
+    const float* __restrict__ w, const float* __restrict__ bias, int C, int rows, int nin,
+    float* __restrict__ pcm, float* __restrict__ pre) {
+  extern __shared__ float sm[];
+  float* ws = sm;          // [K][C]
+  float* ys = sm + K * C;  // [POST_T][K]: tap sums of each row
+  constexpr int OUT = POST_T - (K - 1);
+  const int t = threadIdx.x;
+  const int g_out0 = blockIdx.x * OUT;
+  for (int i = t; i < K * C; i += POST_T) ws[i] = w[i];
+  __syncthreads();
+  const int gr = g_out0 - (K - 1) + t;  // input row of this thread
+  if (gr >= 0 && gr < rows) {
+    float dot[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) dot[j] = 0.f;
+    const float* xr = x + (size_t)gr * C;
+#pragma unroll 4
+    for (int c = 0; c < C; c += 4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(xr + c);
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        const f32x4 wv = *reinterpret_cast<const f32x4*>(ws + j * C + c);
+        dot[j] = fmaf(wv.x, v.x, dot[j]);
+        dot[j] = fmaf(wv.y, v.y, dot[j]);
+        dot[j] = fmaf(wv.z, v.z, dot[j]);
+        dot[j] = fmaf(wv.w, v.w, dot[j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < K; ++j) ys[t * K + j] = dot[j];
+  }
+  __syncthreads();
+  if (t < K - 1) return;
+  const int g = g_out0 + (t - (K - 1));
+  if (g >= rows) return;
+  const int b = g / nin, n = g - b * nin;
+  float acc = bias[0];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const int n2 = n - (K - 1 - j);
+    if (n2 >= 0) {
+      acc += ys[(t - (K - 1) + j) * K + j];
+    } else {
+      const float* wj = ws + j * C;
+      const float* hr = hin + (size_t)b * sstride + (size_t)(H + n2) * C;
+      float dot = 0.f;
+      for (int c = 0; c < C; ++c) dot = fmaf(wj[c], hr[c], dot);
+      acc += dot;
+    }
+  }
+  if (pre) pre[g] = acc;
+  pcm[g] = tanhf(acc);
+}
+
 // ---------------------------------------------------------------------------
 // weight repacking (create time)
 // ---------------------------------------------------------------------------
@@ -505,6 +573,13 @@ hipError_t launch_attention(const float* qkv, const float* k_state, const float*
 hipError_t launch_conv_post(const float* x, const float* hin, long long sstride, int H, const float* w,
                             const float* bias, int C, int k, int rows, int nin, float* pcm, float* pre_tanh,
                             hipStream_t s) {
+  if (k == 7 && C % 4 == 0) {
+    const size_t smem7 = ((size_t)7 * C + (size_t)POST_T * 7) * sizeof(float);
+    if (smem7 > 64 * 1024) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(conv_post_rows_kernel<7>, dim3(cdiv(rows, POST_T - 6)), dim3(POST_T), smem7, s, x, hin,
+                       sstride, H, w, bias, C, rows, nin, pcm, pre_tanh);
+    return hipGetLastError();
+  }
   const size_t smem = ((size_t)k * C + (size_t)(POST_ROWS + k - 1) * (C + 1)) * sizeof(float);
   if (smem > 64 * 1024) return hipErrorInvalidValue;
   hipLaunchKernelGGL(conv_post_kernel, dim3(cdiv(rows, POST_ROWS)), dim3(POST_ROWS), smem, s, x, hin, sstride, H, w,
