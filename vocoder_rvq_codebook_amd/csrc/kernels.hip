@@ -219,27 +219,33 @@ __global__ __launch_bounds__(ATT_THREADS) void attention_kernel(
   float* Vs = Ks + (ATT_QT + W) * ldk;    // [(QT + W)][hd]
   float* Qs = Vs + (ATT_QT + W) * hd;     // [QT][hd]
   const int tid = threadIdx.x;
-  for (int idx = tid; idx < nk * hd; idx += ATT_THREADS) {
-    const int r = idx / hd, c = idx - r * hd;
+  // staged with 16-byte loads (hd is a multiple of 4)
+  const int hd4 = hd / 4;
+  for (int idx = tid; idx < nk * hd4; idx += ATT_THREADS) {
+    const int r = idx / hd4, c = (idx - r * hd4) * 4;
     const int j = t0 + r;  // concat index: j < W state row, else new frame j - W
-    float kv = 0.f, vv = 0.f;
+    f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
     if (j < W) {
       if (p0 - W + j >= 0) {
         const size_t o = (size_t)b * sstride + (size_t)j * d + h * hd + c;
-        kv = ks[o];
-        vv = vs[o];
+        kv = *reinterpret_cast<const f32x4*>(ks + o);
+        vv = *reinterpret_cast<const f32x4*>(vs + o);
       }
     } else if (j - W < T) {
       const float* row = qkv + ((size_t)b * T + (j - W)) * 3 * d;
-      kv = row[d + h * hd + c];
-      vv = row[2 * d + h * hd + c];
+      kv = *reinterpret_cast<const f32x4*>(row + d + h * hd + c);
+      vv = *reinterpret_cast<const f32x4*>(row + 2 * d + h * hd + c);
     }
-    Ks[r * ldk + c] = kv;
-    Vs[r * hd + c] = vv;
+    float* kd = Ks + r * ldk + c;
+    kd[0] = kv.x; kd[1] = kv.y; kd[2] = kv.z; kd[3] = kv.w;
+    float* vd = Vs + r * hd + c;
+    vd[0] = vv.x; vd[1] = vv.y; vd[2] = vv.z; vd[3] = vv.w;
   }
-  for (int idx = tid; idx < nq * hd; idx += ATT_THREADS) {
-    const int r = idx / hd, c = idx - r * hd;
-    Qs[r * hd + c] = qkv[((size_t)b * T + t0 + r) * 3 * d + h * hd + c];
+  for (int idx = tid; idx < nq * hd4; idx += ATT_THREADS) {
+    const int r = idx / hd4, c = (idx - r * hd4) * 4;
+    const f32x4 qv = *reinterpret_cast<const f32x4*>(qkv + ((size_t)b * T + t0 + r) * 3 * d + h * hd + c);
+    float* qd = Qs + r * hd + c;
+    qd[0] = qv.x; qd[1] = qv.y; qd[2] = qv.z; qd[3] = qv.w;
   }
   __syncthreads();
   const int lane = tid & 63, wave = tid >> 6;

@@ -36,7 +36,7 @@ bool config_valid(const vocoder_config* c) {
   if (!m16(c->embed_dim) || !m16(c->model_dim) || !m16(c->ffn_dim)) return false;
   if (c->n_layers < 0 || c->n_layers > 64 || c->n_heads < 1 || c->model_dim % c->n_heads) return false;
   const int hd = c->model_dim / c->n_heads;
-  if (hd % 2 || hd > 256) return false;
+  if (hd % 4 || hd > 256) return false;  // rotate-half pairs; attention stages 16-byte rows
   if (c->window < 0 || c->window > 255) return false;
   // the attention kernel stages (16 + window) keys and values plus 16 queries in 64 KB of LDS
   if ((16LL + c->window) * (2LL * hd + 1) + 16LL * hd > 16384) return false;
