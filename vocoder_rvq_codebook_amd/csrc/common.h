@@ -46,6 +46,7 @@ struct ConvParams {
   int mrf_mode;
   float mrf_div;        // divisor of the MRF mean
   float* mrf;           // running MRF sum [rows_out][cout] (read in ACCUM/LAST)
+  const float* mrf2;    // LAST only, or nullptr: a second block's output, added after mrf
   int nout;
   EpiOut out[4];
   // split-K: splits > 1 stores per-group partials to `partial`
@@ -56,6 +57,9 @@ struct ConvParams {
 
 // reduction values per split-K group (and per accumulation group)
 #define VOC_GROUP_K 256
+// chunks of at most this many frames (over the batch) run a stage's AMP
+// blocks concurrently
+#define VOC_CONC_FRAMES 16
 
 // ---------------------------------------------------------------------------
 // state layout

@@ -93,7 +93,10 @@ __device__ __forceinline__ void epilogue4(const ConvParams& p, int m, int g, f32
   } else if (p.mrf_mode == MRF_ACCUM) {
     sm = ld4(p.mrf + oidx) + v;
   } else if (p.mrf_mode == MRF_LAST) {
-    sm = (ld4(p.mrf + oidx) + v) / p.mrf_div;
+    // ((block 0 + block 1) + this block): the order of the running sum
+    f32x4 acc = ld4(p.mrf + oidx);
+    if (p.mrf2) acc = acc + ld4(p.mrf2 + oidx);
+    sm = (acc + v) / p.mrf_div;
   } else if (p.mrf_mode == MRF_ONLY) {
     sm = v / p.mrf_div;
   }

@@ -166,6 +166,12 @@ struct Plan {
   std::vector<long long> ws_up;
   long long ws_X0 = 0, ws_T = 0, ws_Xr = 0, ws_An = 0, ws_S[2] = {0, 0};
   long long ws_partial = 0, partial_floats = 0;  // split-K group partials
+  // concurrent AMP blocks (chunks of at most conc_frames frames over the
+  // batch): per extra block its own inner buffers and split-K partials, and
+  // the middle block's output
+  long long conc_frames = 0;
+  long long ws_conc_T[2] = {0, 0}, ws_conc_Xr[2] = {0, 0}, ws_conc_An[2] = {0, 0}, ws_conc_B1 = 0;
+  long long ws_partial_aux[2] = {0, 0}, partial_aux_floats = 0;
   std::vector<long long> ws_A;
   long long ws_floats = 0;
   // frames at the end of a chunk that determine every carried row after the
@@ -354,6 +360,19 @@ bool make_plan(const vocoder_config* cp, Plan& P) {
   // small; 32 M floats (128 MB) bounds the split factor of the rest
   P.partial_floats = 32LL << 20;
   P.ws_partial = Wk(P.partial_floats);
+  if (c.n_res >= 2 && c.n_res <= 3) {
+    P.conc_frames = std::min<long long>(Rr, VOC_CONC_FRAMES);
+    long long bigc = 0;
+    for (const StageP& S : P.stages) bigc = std::max(bigc, P.conc_frames * S.rate * S.c);
+    for (int j = 0; j < 2; ++j) {
+      P.ws_conc_T[j] = Wk(bigc);
+      P.ws_conc_Xr[j] = Wk(bigc);
+      P.ws_conc_An[j] = Wk(bigc);
+    }
+    P.ws_conc_B1 = Wk(bigc);
+    P.partial_aux_floats = 8LL << 20;
+    for (int j = 0; j < 2; ++j) P.ws_partial_aux[j] = Wk(P.partial_aux_floats);
+  }
   P.ws_floats = ws;
   // int8 weights are quantized at create time from a float repack staged in
   // the workspace
@@ -427,10 +446,18 @@ struct vocoder {
   uint64_t graph_clock = 0;
   hipStream_t capture_stream = nullptr;
   bool capturing = false;  // recording a graph: no profiling events, no taps
+  // side streams (default priority) for concurrent AMP blocks, fork/join events
+  hipStream_t aux[2] = {nullptr, nullptr};
+  hipEvent_t ev_fork = nullptr, ev_join[2] = {nullptr, nullptr};
   ~vocoder() {
     for (hipEvent_t e : events) (void)hipEventDestroy(e);
     for (GraphEntry& g : graphs) (void)hipGraphExecDestroy(g.exec);
     if (capture_stream) (void)hipStreamDestroy(capture_stream);
+    for (hipStream_t a : aux)
+      if (a) (void)hipStreamDestroy(a);
+    if (ev_fork) (void)hipEventDestroy(ev_fork);
+    for (hipEvent_t e : ev_join)
+      if (e) (void)hipEventDestroy(e);
   }
 };
 
@@ -495,6 +522,8 @@ struct Ctx {
   long long sstride;
   int B, T;
   bool quiet = false;  // no taps
+  float* partial = nullptr;       // split-K partials of launches on this stream
+  long long partial_floats = 0;
 };
 
 ConvParams base_params(const Ctx& cx, const GemmW& g, const float* x, int rows, int nin, int dil,
@@ -546,12 +575,12 @@ void add_out(const Ctx& cx, ConvParams& p, float* dst, const float* alpha, int h
 // Split a launch along K (at accumulation-group boundaries) when it has too
 // few output tiles to fill the GPU: up to ~1024 blocks, if the group partials
 // fit the workspace.  The result is bitwise the same either way.
-int pick_splits(const Plan& P, int tile, int M, long long rows, int k, int cin) {
+int pick_splits(long long partial_floats, int tile, int M, long long rows, int k, int cin) {
   const long long tiles = (long long)((M + gemm_tile_bm(tile) - 1) / gemm_tile_bm(tile)) *
                           ((rows + gemm_tile_bn(tile) - 1) / gemm_tile_bn(tile));
   const long long ngroups = ((long long)k * cin + VOC_GROUP_K - 1) / VOC_GROUP_K;
   if (tiles >= 256 || ngroups < 2) return 1;
-  if (ngroups * rows * M > P.partial_floats) return 1;
+  if (ngroups * rows * M > partial_floats) return 1;
   long long splits = std::min<long long>(ngroups, (1024 + tiles - 1) / tiles);
   // every split owns at least one group
   const long long gps = (ngroups + splits - 1) / splits;
@@ -564,8 +593,8 @@ int run_gemm(const Ctx& cx, const ConvParams& pin) {
   const int tile = pick_tile(p.M, p.rows);
   const int bm = gemm_tile_bm(tile);
   const int mt = (p.M + bm - 1) / bm;
-  p.splits = pick_splits(cx.v->P, tile, p.M, p.rows, p.k, p.cin);
-  p.partial = p.splits > 1 ? cx.v->ws + cx.v->P.ws_partial : nullptr;
+  p.splits = pick_splits(cx.partial_floats, tile, p.M, p.rows, p.k, p.cin);
+  p.partial = p.splits > 1 ? cx.partial : nullptr;
   // A-tile rows read must lie inside the packed (zero-padded) weight rows
   if ((long long)mt * bm > round_up_i(p.M, 128)) return VOCODER_EINVAL;
   if (p.hin_rows < (p.k - 1) * p.dil) return VOCODER_EINVAL;
@@ -750,6 +779,13 @@ int vocoder_create(const vocoder_config* cfg, const float* raw_weights, void* pa
   // the host vectors above are released on return: wait for the copies
   if (hipStreamSynchronize(s) != hipSuccess) return fail(VOCODER_EHIP);
   if (launch_fill(v->ws + P.ws_status, 256, s) != hipSuccess) return fail(VOCODER_EHIP);
+  if (P.conc_frames > 0) {
+    bool ok = hipEventCreateWithFlags(&v->ev_fork, hipEventDisableTiming) == hipSuccess;
+    for (int j = 0; j < 2 && ok; ++j)
+      ok = hipStreamCreateWithFlags(&v->aux[j], hipStreamNonBlocking) == hipSuccess &&
+           hipEventCreateWithFlags(&v->ev_join[j], hipEventDisableTiming) == hipSuccess;
+    if (!ok) return fail(VOCODER_EHIP);
+  }
   *out = v;
   return VOCODER_OK;
 }
@@ -792,6 +828,8 @@ int decode_launches(vocoder* v, const int32_t* codes, int batch, int n_frames, c
   const vocoder_config& c = P.cfg;
   Ctx cx;
   cx.quiet = prefill;
+  cx.partial = v->ws + P.ws_partial;
+  cx.partial_floats = P.partial_floats;
   cx.v = v;
   cx.s = (hipStream_t)stream;
   cx.sin_ = (const float*)state_in;
@@ -967,46 +1005,76 @@ int decode_launches(vocoder* v, const int32_t* codes, int batch, int n_frames, c
       snprintf(nm, sizeof(nm), "stage%d.up", si);
       tap(cx, nm, X0, (long long)rows * S.c);
     }
+    // AMP blocks.  A short chunk (at most conc_frames frames over the batch)
+    // runs them concurrently: every block but the last on a side stream, each
+    // with its own intermediates and split-K partials, the last on the
+    // caller's stream, which waits for the others before its final conv and
+    // sums the multi-receptive-field mean in the sequential order, ((block 0
+    // + block 1) + block 2) / 3.  Longer chunks fill the GPU one block at a
+    // time and run the blocks in order.
+    const bool conc = P.conc_frames > 0 && (long long)B * T <= P.conc_frames && v->aux[0] && v->aux[1];
+    if (conc) {
+      HIP_OK(hipEventRecord(v->ev_fork, cx.s));
+      for (int j = 0; j + 1 < c.n_res; ++j) HIP_OK(hipStreamWaitEvent(v->aux[j], v->ev_fork, 0));
+    }
     for (int j = 0; j < c.n_res; ++j) {
-      const int k = c.res_kernels[j];
+      const bool side = conc && j + 1 < c.n_res;
+      Ctx bc = cx;
+      float* tb = Tb;
+      float* xr = Xr;
+      float* an = An;
+      if (side) {
+        bc.s = v->aux[j];
+        bc.partial = ws + P.ws_partial_aux[j];
+        bc.partial_floats = P.partial_aux_floats;
+        tb = ws + P.ws_conc_T[j];
+        xr = ws + P.ws_conc_Xr[j];
+        an = ws + P.ws_conc_An[j];
+      }
       for (int i = 0; i < c.n_dil; ++i) {
         const AmpP& A = S.amp[(size_t)j * c.n_dil + i];
-        const float* a_in = i == 0 ? ws + P.ws_A[j] : An;
+        const float* a_in = i == 0 ? ws + P.ws_A[j] : an;
         // conv(k, d) of Snake_1(x), then Snake_2
         {
-          ConvParams p = base_params(cx, A.conv1, a_in, rows, (int)nin, c.dilations[i], A.slot1);
+          ConvParams p = base_params(bc, A.conv1, a_in, rows, (int)nin, c.dilations[i], A.slot1);
           p.x_half = P.f16;
-          add_out(cx, p, Tb, pk + A.act2, A.slot2, 0, P.f16);
-          CHECK(run_gemm(cx, p));
+          add_out(bc, p, tb, pk + A.act2, A.slot2, 0, P.f16);
+          CHECK(run_gemm(bc, p));
         }
         // conv(k, 1) + residual
         {
-          ConvParams p = base_params(cx, A.conv2, Tb, rows, (int)nin, 1, A.slot2);
+          ConvParams p = base_params(bc, A.conv2, tb, rows, (int)nin, 1, A.slot2);
           p.x_half = P.f16;
-          p.resid = i == 0 ? X0 : Xr;
+          p.resid = i == 0 ? X0 : xr;
           if (i + 1 < c.n_dil) {
             const AmpP& An1 = S.amp[(size_t)j * c.n_dil + i + 1];
-            add_out(cx, p, Xr, nullptr, -1);
-            add_out(cx, p, An, pk + An1.act1, An1.slot1, 0, P.f16);
+            add_out(bc, p, xr, nullptr, -1);
+            add_out(bc, p, an, pk + An1.act1, An1.slot1, 0, P.f16);
           } else {
             p.mrf = S_out;
             p.mrf_div = (float)c.n_res;
             if (c.n_res == 1) p.mrf_mode = MRF_ONLY;
-            else if (j == 0) p.mrf_mode = MRF_FIRST;
             else if (j + 1 == c.n_res) p.mrf_mode = MRF_LAST;
+            else if (j == 0 || conc) p.mrf_mode = MRF_FIRST;
             else p.mrf_mode = MRF_ACCUM;
             const bool fin = p.mrf_mode == MRF_LAST || p.mrf_mode == MRF_ONLY;
             if (!fin) {
-              add_out(cx, p, S_out, nullptr, -1, 1);
-            } else if (!last_stage) {
-              add_out(cx, p, S_out, nullptr, P.stages[si + 1].slot_up, 1);
+              // concurrent: block 0 into S_out, block 1 into its own buffer
+              add_out(bc, p, side && j == 1 ? ws + P.ws_conc_B1 : S_out, nullptr, -1, 1);
             } else {
-              add_out(cx, p, S_out, pk + P.post_alpha, P.slot_post, 1);
+              if (conc) {
+                for (int jj = 0; jj + 1 < c.n_res; ++jj) HIP_OK(hipStreamWaitEvent(cx.s, v->ev_join[jj], 0));
+                if (c.n_res == 3) p.mrf2 = ws + P.ws_conc_B1;
+              }
+              if (!last_stage)
+                add_out(bc, p, S_out, nullptr, P.stages[si + 1].slot_up, 1);
+              else
+                add_out(bc, p, S_out, pk + P.post_alpha, P.slot_post, 1);
             }
           }
-          CHECK(run_gemm(cx, p));
+          CHECK(run_gemm(bc, p));
+          if (side && i + 1 == c.n_dil) HIP_OK(hipEventRecord(v->ev_join[j], bc.s));
         }
-        (void)k;
       }
     }
     {
