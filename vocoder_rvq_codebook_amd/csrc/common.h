@@ -59,7 +59,7 @@ struct ConvParams {
 #define VOC_GROUP_K 256
 // chunks of at most this many frames (over the batch) run a stage's AMP
 // blocks concurrently
-#define VOC_CONC_FRAMES 16
+#define VOC_CONC_FRAMES 64
 
 // ---------------------------------------------------------------------------
 // state layout
