@@ -67,7 +67,7 @@ def _kernel_family(name):
         q8 = "q8_" if m.group(6) == "true" else ""
         split = "_splitk" if m.group(5) == "true" else ""
         return f"conv_gemm_{half}{q8}{m.group(2)}x{m.group(3)}_bk{m.group(4)}{split}"
-    m = re.search(r"(\w+)\(", name.replace("(anonymous namespace)::", ""))
+    m = re.search(r"(\w+)(?:<[^<>]*>)?\(", name.replace("(anonymous namespace)::", ""))
     return m.group(1) if m else name[:40]
 
 
