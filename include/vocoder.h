@@ -19,7 +19,11 @@
  *  - Every data pointer is a DEVICE pointer on the current HIP device, except
  *    the vocoder_config pointer (host).  `stream` is a hipStream_t (NULL = the
  *    null stream).  Calls enqueue work on `stream` and never synchronise it,
- *    except vocoder_get_status.
+ *    except vocoder_get_status.  A decode of a short chunk (at most 64 frames
+ *    over the batch) also runs part of its work on two streams the handle
+ *    owns, forked from `stream` and joined back into it by events: every
+ *    call's work still starts after earlier work on `stream` and ends before
+ *    later work on it.
  *  - The caller owns every device buffer (raw and packed weights, workspace,
  *    states, codes, PCM).  The library allocates no device memory; it owns only
  *    its host-side handle.
