@@ -25,8 +25,10 @@
  *    call's work still starts after earlier work on `stream` and ends before
  *    later work on it.
  *  - The caller owns every device buffer (raw and packed weights, workspace,
- *    states, codes, PCM).  The library allocates no device memory; it owns only
- *    its host-side handle.
+ *    states, codes, PCM).  The library allocates no device memory; it owns its
+ *    host-side handle, two streams and three events created by vocoder_create,
+ *    and the graphs vocoder_decode_chunk_graph records, all released by
+ *    vocoder_destroy.
  *  - Return values: VOCODER_OK (0) or a negative VOCODER_E* code.  Argument
  *    errors are detected on the host before any HIP call.  Errors the device
  *    detects (a code out of range, a state that belongs to another decoder) are
