@@ -65,6 +65,10 @@ def test_invalid_configs_rejected():
         cfg = vb.make_config(bad, 1, 1)
         assert vb.vocoder_raw_weights_count(cfg) == 0, key
         assert vb.vocoder_state_bytes(cfg) == 0, key
+    # a LayerNorm row must fit one wave's registers: d <= 4096 (here head size 256)
+    wide = dict(good, model_dim=4352, n_heads=17)
+    assert vb.vocoder_raw_weights_count(vb.make_config(wide, 1, 1)) == 0
+    assert vb.vocoder_raw_weights_count(vb.make_config(dict(good, model_dim=4096, n_heads=16), 1, 1)) > 0
     assert vb.vocoder_workspace_bytes(vb.make_config(good, 0, 1)) == 0
     assert vb.vocoder_workspace_bytes(vb.make_config(good, 1, 0)) == 0
 

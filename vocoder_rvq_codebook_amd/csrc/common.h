@@ -6,6 +6,73 @@
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// LayerNorm over d channels of one row by one block of 64 * NV threads
+// (NV = layernorm_nv(d)): thread t holds channels 4t..4t+3 (t < d/4).  Biased
+// variance, two passes; each pass sums the per-thread partials of lane l in
+// thread order l, l + 64, ... in wave 0, then across the wave.  Optionally
+// the last H rows of each stream (T rows per stream) also go to a state slot.
+// Shared by the LayerNorm kernel and the split-K fold that feeds one, so both
+// give the same bits.
+struct LnArgs {
+  const float* g;
+  const float* b;
+  float eps;
+  int d;
+  float* out;
+  int T;
+  float* hist;
+  int H;
+  long long sstride;
+};
+
+// Widest row: 64 x LN_MAX_NV float4 (one thread each).
+#define LN_MAX_NV 16
+
+// red: LDS of at least 64 * NV + 1 floats.  Every thread of the block calls it.
+template <int NV>
+__device__ __forceinline__ void layernorm_block(const LnArgs& a, f32x4 x, int row, float* red) {
+  const int t = threadIdx.x, lane = t & 63;
+  const int d4 = a.d / 4;
+  const bool have = t < d4;
+  if (have) red[t] = (x.x + x.y) + (x.z + x.w);
+  __syncthreads();
+  if (t < 64) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (64 * i + lane < d4) s += red[64 * i + lane];
+    s = wave_sum(s);
+    if (t == 0) red[64 * NV] = s / (float)a.d;
+  }
+  __syncthreads();
+  const float mean = red[64 * NV];
+  const f32x4 v = x - mean;
+  if (have) red[t] = (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
+  __syncthreads();
+  if (t < 64) {
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (64 * i + lane < d4) q += red[64 * i + lane];
+    q = wave_sum(q);
+    if (t == 0) red[64 * NV] = 1.0f / sqrtf(q / (float)a.d + a.eps);
+  }
+  __syncthreads();
+  const float rstd = red[64 * NV];
+  if (!have) return;
+  const int b = row / a.T, tt = row - b * a.T;
+  const f32x4 y = v * rstd * *reinterpret_cast<const f32x4*>(a.g + 4 * t) + *reinterpret_cast<const f32x4*>(a.b + 4 * t);
+  *reinterpret_cast<f32x4*>(a.out + (size_t)row * a.d + 4 * t) = y;
+  if (a.hist && tt >= a.T - a.H)
+    *reinterpret_cast<f32x4*>(a.hist + (size_t)b * a.sstride + (size_t)(a.H - a.T + tt) * a.d + 4 * t) = y;
+}
+
 // ---------------------------------------------------------------------------
 // implicit-GEMM convolution (conv1d, transposed conv, linear)
 // ---------------------------------------------------------------------------
@@ -103,9 +170,13 @@ enum GemmTile { TILE_128x128 = 0, TILE_64x64 = 1, TILE_96x128 = 2, TILE_S64x16 =
 int gemm_tile_bm(int tile);
 int gemm_tile_bn(int tile);
 int gemm_tile_bk(int tile, int cin, bool half);
-hipError_t launch_conv_gemm(const ConvParams& p, int tile, hipStream_t s);
+// ln: for a split launch (p.splits > 1) whose first output (fp32, one phase,
+// M = ln.d) feeds a LayerNorm, fold the partials, run the epilogue and
+// normalise each row in one kernel (the same bits as the reduction followed
+// by the LayerNorm kernel); null otherwise.
+hipError_t launch_conv_gemm(const ConvParams& p, int tile, hipStream_t s, const LnArgs* ln = nullptr);
 // fp16-operand GEMM: p.w points at fp16 weights [Mpad][k][cin]; tiles 128x128, 96x128, 64x64
-hipError_t launch_conv_gemm_f16(const ConvParams& p, int tile, hipStream_t s);
+hipError_t launch_conv_gemm_f16(const ConvParams& p, int tile, hipStream_t s, const LnArgs* ln = nullptr);
 
 hipError_t launch_begin(const void* state_in, void* state_out, long long sstride, int batch, int T,
                         uint64_t cfg_hash, const double* inv_freq, int half, float* rope_tab, int* pos,
@@ -115,6 +186,9 @@ hipError_t launch_state_shift(const Slot* slots, int nslots, int max_h, const fl
 hipError_t launch_gather(const int32_t* codes, const float* codebooks, int Q, int V, int D, int rows,
                          int T, float* out, float* hist, int H, long long sstride, int* status,
                          hipStream_t s);
+// waves per LayerNorm row of d channels (a power of two, one float4 per
+// thread), 0 if d is not a multiple of 4 or wider than 64 x LN_MAX_NV float4
+int layernorm_nv(int d);
 hipError_t launch_layernorm(const float* x, const float* g, const float* b, float eps, int rows, int d,
                             float* out, int T, float* hist, int H, long long sstride, hipStream_t s);
 hipError_t launch_rope_kv(float* qkv, const float* rope_tab, int rows, int T, int n_heads, int hd,

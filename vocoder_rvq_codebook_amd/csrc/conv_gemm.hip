@@ -75,8 +75,9 @@ __device__ __forceinline__ void st4(float* p, f32x4 v) { *reinterpret_cast<f32x4
 // reduced sum `acc`: bias, activation, residual, multi-receptive-field mean,
 // then up to four stores, each optionally through Snake and each optionally
 // also written to the stream's state tail.  Shared by the GEMM and the
-// split-K reduction, so both give the same bits.
-__device__ __forceinline__ void epilogue4(const ConvParams& p, int m, int g, f32x4 acc) {
+// split-K reduction, so both give the same bits.  Returns the first output's
+// value (as stored when it is fp32).
+__device__ __forceinline__ f32x4 epilogue4(const ConvParams& p, int m, int g, f32x4 acc) {
   const int nout_rows = p.nin * p.phases;
   const int ph = m / p.cout;
   const int c = m - ph * p.cout;
@@ -102,6 +103,7 @@ __device__ __forceinline__ void epilogue4(const ConvParams& p, int m, int g, f32
   }
   const int b = g / p.nin;
   const int no = (g - b * p.nin) * p.phases + ph;
+  f32x4 first = v;
 #pragma unroll
   for (int o = 0; o < 4; ++o) {
     if (o >= p.nout) break;
@@ -122,7 +124,9 @@ __device__ __forceinline__ void epilogue4(const ConvParams& p, int m, int g, f32
     if (eo.hist && no >= nout_rows - eo.H) {
       st4(eo.hist + (size_t)b * p.sstride + (size_t)(eo.H - nout_rows + no) * p.cout + c, val);
     }
+    if (o == 0) first = val;
   }
+  return first;
 }
 
 // Reduction values per accumulation group (see the two-level accumulation
@@ -383,6 +387,21 @@ __global__ void splitk_reduce_kernel(const ConvParams p, int ngroups) {
   const int g = (int)(idx / M4);
   const int m = (int)(idx - (long long)g * M4) * 4;
   epilogue4(p, m, g, fold_groups(p, m, g, ngroups));
+}
+
+// The same fold and epilogue for a GEMM whose first output feeds a LayerNorm
+// (one phase, M = ln.d): one block per row, one float4 per thread as above;
+// the row's epilogue values stay in registers for the LayerNorm, so the row
+// is not read back.  The same values and order as splitk_reduce_kernel then
+// layernorm_kernel.
+template <int NV>
+__global__ __launch_bounds__(64 * NV) void splitk_reduce_ln_kernel(const ConvParams p, int ngroups, const LnArgs ln) {
+  __shared__ float red[64 * NV + 1];
+  const int g = blockIdx.x;
+  const int m = 4 * threadIdx.x;
+  f32x4 v = {0.f, 0.f, 0.f, 0.f};
+  if (m < p.M) v = epilogue4(p, m, g, fold_groups(p, m, g, ngroups));
+  layernorm_block<NV>(ln, v, g, red);
 }
 
 // ---------------------------------------------------------------------------
@@ -683,15 +702,33 @@ hipError_t launch_cfg_q(const ConvParams& p, hipStream_t s) {
       hipLaunchKernelGGL((conv_gemm_kernel<C, false, Q8>), dim3((unsigned)tiles), dim3(C::NT), 0, s, p);
     return hipGetLastError();
   }
+  // split: the blocks store group partials; the fold is launched by the caller
   const long long nb = tiles * p.splits;
   if (nb > 0x7fffffffLL || !p.partial) return hipErrorInvalidValue;
   if constexpr (HALF)
     hipLaunchKernelGGL((conv_gemm_f16_kernel<C, true, Q8>), dim3((unsigned)nb), dim3(C::NT), 0, s, p);
   else
     hipLaunchKernelGGL((conv_gemm_kernel<C, true, Q8>), dim3((unsigned)nb), dim3(C::NT), 0, s, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+// After a split launch: fold the group partials and run the epilogue, fused
+// with the LayerNorm when ln is given and fits.
+hipError_t launch_fold(const ConvParams& p, hipStream_t s, const LnArgs* ln) {
   const int ngroups = (p.k * p.cin + GROUP_K - 1) / GROUP_K;
+  const int nv = ln ? layernorm_nv(ln->d) : 0;
+  if (ln && (nv == 0 || p.M != ln->d || p.phases != 1 || p.nout < 1 || p.out[0].half)) return hipErrorInvalidValue;
+  if (ln) {
+    const dim3 grid((unsigned)p.rows), block(64 * nv);
+    switch (nv) {
+      case 1: hipLaunchKernelGGL(splitk_reduce_ln_kernel<1>, grid, block, 0, s, p, ngroups, *ln); break;
+      case 2: hipLaunchKernelGGL(splitk_reduce_ln_kernel<2>, grid, block, 0, s, p, ngroups, *ln); break;
+      case 4: hipLaunchKernelGGL(splitk_reduce_ln_kernel<4>, grid, block, 0, s, p, ngroups, *ln); break;
+      case 8: hipLaunchKernelGGL(splitk_reduce_ln_kernel<8>, grid, block, 0, s, p, ngroups, *ln); break;
+      default: hipLaunchKernelGGL(splitk_reduce_ln_kernel<16>, grid, block, 0, s, p, ngroups, *ln); break;
+    }
+    return hipGetLastError();
+  }
   const long long n = (long long)p.rows * (p.M / 4);
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, ngroups);
   return hipGetLastError();
@@ -739,7 +776,9 @@ int gemm_tile_bk(int tile, int cin, bool half) {
   return tile == TILE_128x128 || cin % 32 != 0 ? 16 : 32;
 }
 
-hipError_t launch_conv_gemm(const ConvParams& p, int tile, hipStream_t s) {
+namespace {
+
+hipError_t launch_blocks_f32(const ConvParams& p, int tile, hipStream_t s) {
   const bool bk32 = (p.cin % 32) == 0;
   if (p.cin % 16 != 0) return hipErrorInvalidValue;
   switch (tile) {
@@ -771,7 +810,7 @@ hipError_t launch_conv_gemm(const ConvParams& p, int tile, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_conv_gemm_f16(const ConvParams& p, int tile, hipStream_t s) {
+hipError_t launch_blocks_f16(const ConvParams& p, int tile, hipStream_t s) {
   if (p.cin % 16 != 0) return hipErrorInvalidValue;
   const int bk = half_bk(p.cin);
   // (no interleaving hint with 16-wide slabs: iglp_opt(1) sends the compiler
@@ -807,4 +846,21 @@ hipError_t launch_conv_gemm_f16(const ConvParams& p, int tile, hipStream_t s) {
   }
 #undef VOC_F16_CASES
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm(const ConvParams& p, int tile, bool half, hipStream_t s, const LnArgs* ln) {
+  if (p.rows <= 0 || p.M <= 0) return hipSuccess;
+  const hipError_t e = half ? launch_blocks_f16(p, tile, s) : launch_blocks_f32(p, tile, s);
+  if (e != hipSuccess || p.splits <= 1) return e;
+  return launch_fold(p, s, ln);
+}
+
+}  // namespace
+
+hipError_t launch_conv_gemm(const ConvParams& p, int tile, hipStream_t s, const LnArgs* ln) {
+  return launch_gemm(p, tile, false, s, ln);
+}
+
+hipError_t launch_conv_gemm_f16(const ConvParams& p, int tile, hipStream_t s, const LnArgs* ln) {
+  return launch_gemm(p, tile, true, s, ln);
 }

@@ -10,11 +10,6 @@ namespace {
 __device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 __device__ __forceinline__ void st4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -127,35 +122,14 @@ __global__ void gather_kernel(const int32_t* __restrict__ codes, const float* __
 // LayerNorm over d channels, one wave per row, biased variance, two passes.
 // Optionally writes the last H rows of each stream into a state slot.
 // ---------------------------------------------------------------------------
-__global__ void layernorm_kernel(const float* __restrict__ x, const float* __restrict__ g,
-                                 const float* __restrict__ bta, float eps, int rows, int d,
-                                 float* __restrict__ out, int T, float* __restrict__ hist, int H,
-                                 long long sstride) {
-  const int row = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
-  const float* xr = x + (size_t)row * d;
-  const int d4 = d / 4;
-  float s = 0.f;
-  for (int c = lane; c < d4; c += 64) {
-    const f32x4 v = ld4(xr + 4 * c);
-    s += (v.x + v.y) + (v.z + v.w);
-  }
-  const float mean = wave_sum(s) / (float)d;
-  float q = 0.f;
-  for (int c = lane; c < d4; c += 64) {
-    const f32x4 v = ld4(xr + 4 * c) - mean;
-    q += (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
-  }
-  const float var = wave_sum(q) / (float)d;
-  const float rstd = 1.0f / sqrtf(var + eps);
-  const int b = row / T, t = row - b * T;
-  const bool tail = hist && t >= T - H;
-  for (int c = lane; c < d4; c += 64) {
-    const f32x4 v = (ld4(xr + 4 * c) - mean) * rstd * ld4(g + 4 * c) + ld4(bta + 4 * c);
-    st4(out + (size_t)row * d + 4 * c, v);
-    if (tail) st4(hist + (size_t)b * sstride + (size_t)(H - T + t) * d + 4 * c, v);
-  }
+// one block of 64 * NV threads per row
+template <int NV>
+__global__ __launch_bounds__(64 * NV) void layernorm_kernel(const float* __restrict__ x, const LnArgs a) {
+  __shared__ float red[64 * NV + 1];
+  const int row = blockIdx.x;
+  f32x4 v = {0.f, 0.f, 0.f, 0.f};
+  if ((int)threadIdx.x < a.d / 4) v = ld4(x + (size_t)row * a.d + 4 * threadIdx.x);
+  layernorm_block<NV>(a, v, row, red);
 }
 
 // ---------------------------------------------------------------------------
@@ -550,10 +524,27 @@ hipError_t launch_gather(const int32_t* codes, const float* codebooks, int Q, in
   return hipGetLastError();
 }
 
+int layernorm_nv(int d) {
+  const int need = cdiv(d / 4, 64);
+  int nv = 1;
+  while (nv < need) nv *= 2;
+  return d % 4 == 0 && nv <= LN_MAX_NV ? nv : 0;
+}
+
 hipError_t launch_layernorm(const float* x, const float* g, const float* b, float eps, int rows, int d, float* out,
                             int T, float* hist, int H, long long sstride, hipStream_t s) {
-  hipLaunchKernelGGL(layernorm_kernel, dim3(cdiv(rows, 4)), dim3(256), 0, s, x, g, b, eps, rows, d, out, T, hist,
-                     H, sstride);
+  const LnArgs a{g, b, eps, d, out, T, hist, H, sstride};
+  if (rows <= 0) return hipSuccess;
+  const int nv = layernorm_nv(d);
+  const dim3 grid(rows), block(64 * nv);
+  switch (nv) {
+    case 1: hipLaunchKernelGGL(layernorm_kernel<1>, grid, block, 0, s, x, a); break;
+    case 2: hipLaunchKernelGGL(layernorm_kernel<2>, grid, block, 0, s, x, a); break;
+    case 4: hipLaunchKernelGGL(layernorm_kernel<4>, grid, block, 0, s, x, a); break;
+    case 8: hipLaunchKernelGGL(layernorm_kernel<8>, grid, block, 0, s, x, a); break;
+    case 16: hipLaunchKernelGGL(layernorm_kernel<16>, grid, block, 0, s, x, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

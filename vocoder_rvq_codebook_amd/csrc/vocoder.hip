@@ -37,6 +37,7 @@ bool config_valid(const vocoder_config* c) {
   if (c->n_layers < 0 || c->n_layers > 64 || c->n_heads < 1 || c->model_dim % c->n_heads) return false;
   const int hd = c->model_dim / c->n_heads;
   if (hd % 4 || hd > 256) return false;  // rotate-half pairs; attention stages 16-byte rows
+  if (c->model_dim > 4096) return false;  // a LayerNorm row is held in one wave's registers
   if (c->window < 0 || c->window > 255) return false;
   // the attention kernel stages (16 + window) keys and values plus 16 queries in 64 KB of LDS
   if ((16LL + c->window) * (2LL * hd + 1) + 16LL * hd > 16384) return false;
@@ -588,7 +589,9 @@ int pick_splits(long long partial_floats, int tile, int M, long long rows, int k
   return (int)std::max<long long>(splits, 1);
 }
 
-int run_gemm(const Ctx& cx, const ConvParams& pin) {
+// ln: the GEMM's first output feeds this LayerNorm (its input is that output).
+// A split GEMM normalises in its fold kernel; otherwise the LayerNorm kernel follows.
+int run_gemm(const Ctx& cx, const ConvParams& pin, const LnArgs* ln = nullptr) {
   ConvParams p = pin;
   const int tile = pick_tile(p.M, p.rows);
   const int bm = gemm_tile_bm(tile);
@@ -608,15 +611,24 @@ int run_gemm(const Ctx& cx, const ConvParams& pin) {
   const bool f16 = cx.v->P.f16;
   if (p.wscale) bytes -= (4.0 - 1.0625) * p.M * K;  // int8 weights and their scales
   else if (f16) bytes -= 2.0 * p.M * K;             // fp16 weights
+  const bool fuse_ln = ln && p.splits > 1;
+  if (fuse_ln) bytes += 8.0 * p.rows * ln->d;
   char name[48];
   snprintf(name, sizeof(name), "conv_gemm_%s%s%dx%d_bk%d%s", f16 ? "f16_" : "", p.wscale ? "q8_" : "", bm,
            gemm_tile_bn(tile),
-           gemm_tile_bk(tile, p.cin, f16), p.splits > 1 ? "_splitk" : "");
-  Prof pr(cx.v, cx.s, name, flops, bytes);
-  if (f16)
-    HIP_OK(launch_conv_gemm_f16(p, tile, cx.s));
-  else
-    HIP_OK(launch_conv_gemm(p, tile, cx.s));
+           gemm_tile_bk(tile, p.cin, f16), p.splits > 1 ? (fuse_ln ? "_splitk_ln" : "_splitk") : "");
+  {
+    Prof pr(cx.v, cx.s, name, flops, bytes);
+    if (f16)
+      HIP_OK(launch_conv_gemm_f16(p, tile, cx.s, fuse_ln ? ln : nullptr));
+    else
+      HIP_OK(launch_conv_gemm(p, tile, cx.s, fuse_ln ? ln : nullptr));
+  }
+  if (ln && !fuse_ln) {
+    Prof pr(cx.v, cx.s, "layernorm", 0, 8.0 * p.rows * ln->d);
+    HIP_OK(launch_layernorm(p.out[0].dst, ln->g, ln->b, ln->eps, p.rows, ln->d, ln->out, ln->T, ln->hist, ln->H,
+                            ln->sstride, cx.s));
+  }
   return VOCODER_OK;
 }
 
@@ -866,26 +878,32 @@ int decode_launches(vocoder* v, const int32_t* codes, int batch, int n_frames, c
   }
   tap(cx, "embed", emb, (long long)R * c.embed_dim);
 
-  // causal conv before the transformer
+  // Each LayerNorm runs with the GEMM that produces its input (the pre-conv
+  // or a residual projection): the next layer's first norm, or the final
+  // norm, whose last row feeds the first transposed conv's history.
   float* h = ws + P.ws_h;
+  float* u = ws + P.ws_u;
+  auto ln_after = [&](int l) {
+    if (l < c.n_layers) return LnArgs{pk + P.layers[l].ln1_g, pk + P.layers[l].ln1_b, c.ln_eps, d, u, T, nullptr, 0, 0};
+    const Slot& so = P.slots[c.n_up > 0 ? P.slot_ups[0] : P.slot_conv_pre];
+    return LnArgs{pk + P.fln_g, pk + P.fln_b, c.ln_eps, d, u, T, cx.sout + so.off, so.H, cx.sstride};
+  };
+
+  // causal conv before the transformer
   {
     ConvParams p = base_params(cx, P.pre, emb, R, T, 1, P.slot_pre);
     add_out(cx, p, h, nullptr, -1);
-    CHECK(run_gemm(cx, p));
+    const LnArgs ln = ln_after(0);
+    CHECK(run_gemm(cx, p, &ln));
   }
   tap(cx, "pre_conv", h, (long long)R * d);
 
   // transformer
-  float* u = ws + P.ws_u;
   float* qkv = ws + P.ws_qkv;
   float* att = ws + P.ws_att;
   float* ffn = ws + P.ws_ffn;
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerP& L = P.layers[l];
-    {
-      Prof pr(v, cx.s, "layernorm", 0, 8.0 * R * d);
-      HIP_OK(launch_layernorm(h, pk + L.ln1_g, pk + L.ln1_b, c.ln_eps, R, d, u, T, nullptr, 0, 0, cx.s));
-    }
     {
       ConvParams p = base_params(cx, L.qkv, u, R, T, 1, -1);
       add_out(cx, p, qkv, nullptr, -1);
@@ -908,11 +926,8 @@ int decode_launches(vocoder* v, const int32_t* codes, int batch, int n_frames, c
       ConvParams p = base_params(cx, L.o, att, R, T, 1, -1);
       p.resid = h;
       add_out(cx, p, h, nullptr, -1);
-      CHECK(run_gemm(cx, p));
-    }
-    {
-      Prof pr(v, cx.s, "layernorm", 0, 8.0 * R * d);
-      HIP_OK(launch_layernorm(h, pk + L.ln2_g, pk + L.ln2_b, c.ln_eps, R, d, u, T, nullptr, 0, 0, cx.s));
+      const LnArgs ln{pk + L.ln2_g, pk + L.ln2_b, c.ln_eps, d, u, T, nullptr, 0, 0};
+      CHECK(run_gemm(cx, p, &ln));
     }
     {
       ConvParams p = base_params(cx, L.fc1, u, R, T, 1, -1);
@@ -924,19 +939,12 @@ int decode_launches(vocoder* v, const int32_t* codes, int batch, int n_frames, c
       ConvParams p = base_params(cx, L.fc2, ffn, R, T, 1, -1);
       p.resid = h;
       add_out(cx, p, h, nullptr, -1);
-      CHECK(run_gemm(cx, p));
+      const LnArgs ln = ln_after(l + 1);
+      CHECK(run_gemm(cx, p, &ln));
     }
     char nm[32];
     snprintf(nm, sizeof(nm), "layer%d", l);
     tap(cx, nm, h, (long long)R * d);
-  }
-  // final LayerNorm; its last row feeds the first transposed conv's history
-  {
-    const int s0 = c.n_up > 0 ? P.slot_ups[0] : P.slot_conv_pre;
-    const Slot& so = P.slots[s0];
-    Prof pr(v, cx.s, "layernorm", 0, 8.0 * R * d);
-    HIP_OK(launch_layernorm(h, pk + P.fln_g, pk + P.fln_b, c.ln_eps, R, d, u, T, cx.sout + so.off, so.H,
-                            cx.sstride, cx.s));
   }
   tap(cx, "final_ln", u, (long long)R * d);
 
