@@ -119,10 +119,10 @@ __global__ void gather_kernel(const int32_t* __restrict__ codes, const float* __
 }
 
 // ---------------------------------------------------------------------------
-// LayerNorm over d channels, one wave per row, biased variance, two passes.
-// Optionally writes the last H rows of each stream into a state slot.
+// LayerNorm over d channels (layernorm_block): one block of 64 * NV threads
+// per row, biased variance, two passes.  Optionally writes the last H rows of
+// each stream into a state slot.
 // ---------------------------------------------------------------------------
-// one block of 64 * NV threads per row
 template <int NV>
 __global__ __launch_bounds__(64 * NV) void layernorm_kernel(const float* __restrict__ x, const LnArgs a) {
   __shared__ float red[64 * NV + 1];
