@@ -170,6 +170,9 @@ enum GemmTile { TILE_128x128 = 0, TILE_64x64 = 1, TILE_96x128 = 2, TILE_S64x16 =
 int gemm_tile_bm(int tile);
 int gemm_tile_bn(int tile);
 int gemm_tile_bk(int tile, int cin, bool half);
+// the fp16-operand GEMM of this tile loads its operands straight into LDS
+// (float or fp16 weights, channel count a multiple of 32, 128x128 or 96x128)
+bool gemm_f16_direct(bool int8, int cin, int tile);
 // ln: for a split launch (p.splits > 1) whose first output (fp32, one phase,
 // M = ln.d) feeds a LayerNorm, fold the partials, run the epilogue and
 // normalise each row in one kernel (the same bits as the reduction followed

@@ -89,17 +89,23 @@ __device__ __forceinline__ f32x4 epilogue4(const ConvParams& p, int m, int g, f3
   const size_t oidx = orow * p.cout + c;
   if (p.resid) v = v + ld4(p.resid + oidx);
   f32x4 sm = v;
-  if (p.mrf_mode == MRF_FIRST) {
+  // (fields read into scalars first: reading them in place let the optimizer
+  // copy part of the argument block to private memory in some kernels)
+  const int mrf_mode = p.mrf_mode;
+  const float* mrf = p.mrf;
+  const float* mrf2 = p.mrf2;
+  const float mrf_div = p.mrf_div;
+  if (mrf_mode == MRF_FIRST) {
     sm = v;
-  } else if (p.mrf_mode == MRF_ACCUM) {
-    sm = ld4(p.mrf + oidx) + v;
-  } else if (p.mrf_mode == MRF_LAST) {
+  } else if (mrf_mode == MRF_ACCUM) {
+    sm = ld4(mrf + oidx) + v;
+  } else if (mrf_mode == MRF_LAST) {
     // ((block 0 + block 1) + this block): the order of the running sum
-    f32x4 acc = ld4(p.mrf + oidx);
-    if (p.mrf2) acc = acc + ld4(p.mrf2 + oidx);
-    sm = (acc + v) / p.mrf_div;
-  } else if (p.mrf_mode == MRF_ONLY) {
-    sm = v / p.mrf_div;
+    f32x4 acc = ld4(mrf + oidx);
+    if (mrf2) acc = acc + ld4(mrf2 + oidx);
+    sm = (acc + v) / mrf_div;
+  } else if (mrf_mode == MRF_ONLY) {
+    sm = v / mrf_div;
   }
   const int b = g / p.nin;
   const int no = (g - b * p.nin) * p.phases + ph;
@@ -688,6 +694,279 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
   }
 }
 
+// ---------------------------------------------------------------------------
+// fp16-operand variant fed by direct global->LDS loads (global_load_lds_dwordx4:
+// each lane's 16 bytes land at the wave's LDS base + 16 * lane), so no register
+// staging: an NS-deep ring of LDS stages keeps the loads of NS - 1 K-steps in
+// flight, which the register-staged kernel cannot afford in registers.  One
+// K-step is one 32-half MFMA slab of one tap; the K-steps, their order, the
+// accumulation groups and split-K are those of conv_gemm_f16_kernel, so both
+// give the same bits.
+//
+// LDS stage = A tile (BM rows x 32 halves, 4 chunks of 16 bytes per row), then
+// the B tile: 32 halves per row when the input rows are fp16 (XH), else 32
+// floats (8 chunks per row), rounded to fp16 as the MFMA operands are read.
+// Chunks are XOR-swizzled within a row so that the 8 lanes an LDS read
+// serves together (8 rows, one 16-byte chunk each, 128 bytes of banks) hit
+// distinct banks: chunk c of row r sits at position c ^ ((r >> 1) & 3)
+// (4-chunk rows) or c ^ (r & 7) (8-chunk rows).
+// Every wave issues the same number of loads per K-step (lanes past a tile's
+// slots are masked), so a wave's vmcnt tells when its own share of a stage has
+// landed; a barrier then makes every wave's share visible.  History rows of
+// an fp16 input come from the fp32 state and are converted through registers.
+// ---------------------------------------------------------------------------
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int NS_>
+struct TileCfgD {
+  static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, NS = NS_;
+  static constexpr int BK = 32, SLAB = 32;
+  static constexpr int WAVES = WAVES_M * WAVES_N;
+  static constexpr int NT = WAVES * 64;
+  static constexpr int WTM = BM / WAVES_M;
+  static constexpr int WTN = BN / WAVES_N;
+  static constexpr int FM = WTM / 16;
+  static constexpr int FN = WTN / 16;
+  static constexpr int A_SLOTS = BM * 4;            // 16-byte chunks per stage
+  static constexpr int A_PER_WAVE = A_SLOTS / WAVES;
+  static_assert(A_SLOTS % WAVES == 0 && A_PER_WAVE <= 64, "A chunks per wave");
+  static_assert(WTM % 16 == 0 && WTN % 16 == 0 && NS >= 2, "tile");
+  template <bool XH>
+  static constexpr int b_slots() { return BN * (XH ? 4 : 8); }
+  template <bool XH>
+  static constexpr int b_per_wave() { return b_slots<XH>() / WAVES; }  // multiple of 64 or <= 64
+  template <bool XH>
+  static constexpr int stage_bytes() { return (A_SLOTS + b_slots<XH>()) * 16; }
+};
+
+__device__ __forceinline__ void lds_dma16(const void* gaddr, uint32_t lds_wave_base) {
+  // m0 holds the wave's LDS destination; the address is wave-uniform
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_wave_base)), "v"(gaddr)
+               : "memory");
+}
+
+// wait until at most N vector-memory operations of this wave are outstanding,
+// and for all of its LDS operations
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
+}
+
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <class C, bool SPLIT, bool XH>
+__global__ __launch_bounds__(C::NT) void conv_gemm_f16_dma_kernel(const ConvParams p) {
+  constexpr int STAGE = C::template stage_bytes<XH>();
+  constexpr int A_BYTES = C::A_SLOTS * 16;
+  constexpr int B_SLOTS = C::template b_slots<XH>();
+  constexpr int B_PER_WAVE = C::template b_per_wave<XH>();
+  constexpr int B_DMAS = B_PER_WAVE >= 64 ? B_PER_WAVE / 64 : 1;  // loads per wave per K-step
+  constexpr int B_LANES = B_PER_WAVE >= 64 ? 64 : B_PER_WAVE;
+  static_assert(B_SLOTS % C::WAVES == 0 && (B_PER_WAVE <= 64 || B_PER_WAVE % 64 == 0), "B chunks per wave");
+  constexpr int OPS = 1 + B_DMAS;  // vector-memory operations per wave per K-step (at least)
+  __shared__ __attribute__((aligned(16))) char lds[C::NS * STAGE];
+  const _Float16* W = reinterpret_cast<const _Float16*>(p.w);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave % C::WAVES_M;
+  const int wn = wave / C::WAVES_M;
+
+  const int mtiles = (p.M + C::BM - 1) / C::BM;
+  int tile_id;
+  {
+    const int L = blockIdx.x, nb = gridDim.x;
+    const int xcd = L & 7, i = L >> 3;
+    const int per = nb >> 3, extra = nb & 7;
+    tile_id = xcd * per + (xcd < extra ? xcd : extra) + i;
+  }
+  int split = 0;
+  if (SPLIT) {
+    split = tile_id % p.splits;
+    tile_id /= p.splits;
+  }
+  const int mt = tile_id % mtiles;
+  const int nt = tile_id / mtiles;
+  const int m0 = mt * C::BM;
+  const int g0 = nt * C::BN;
+
+  const int cin = p.cin;
+  const int ktaps = p.k, dil = p.dil;
+  const int ksteps_per_tap = cin / C::BK;
+  const int nsteps_all = p.k * ksteps_per_tap;
+  constexpr int GROUP_STEPS = GROUP_K / C::BK;
+  int s_begin = 0, nsteps = nsteps_all;
+  if (SPLIT) {
+    const int ngroups = (nsteps_all + GROUP_STEPS - 1) / GROUP_STEPS;
+    const int gps = (ngroups + p.splits - 1) / p.splits;
+    s_begin = min(split * gps, ngroups) * GROUP_STEPS;
+    nsteps = min(min((split + 1) * gps, ngroups) * GROUP_STEPS, nsteps_all);
+    if (s_begin >= nsteps) return;
+  }
+
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
+  // A: this lane's chunk of the wave's A_PER_WAVE slots
+  const bool a_on = lane < C::A_PER_WAVE;
+  const _Float16* a_src;
+  {
+    const int j = wave * C::A_PER_WAVE + (a_on ? lane : 0);
+    const int r = j >> 2, c = (j & 3) ^ ((r >> 1) & 3);
+    a_src = W + (size_t)(m0 + r) * ((size_t)p.k * cin) + c * 8;
+  }
+  const uint32_t a_dst = lds0 + (uint32_t)(wave * C::A_PER_WAVE) * 16;
+  // B: B_DMAS loads of 64 (or B_LANES) chunks per wave
+  const char* bx[B_DMAS];
+  const float* bh[B_DMAS];
+  int bn[B_DMAS];
+  bool b_on[B_DMAS];
+  const size_t esz = XH ? 2 : 4;
+#pragma unroll
+  for (int h = 0; h < B_DMAS; ++h) {
+    b_on[h] = lane < B_LANES;
+    const int j = wave * B_PER_WAVE + h * 64 + (b_on[h] ? lane : 0);
+    const int r = XH ? (j >> 2) : (j >> 3);
+    const int c = XH ? ((j & 3) ^ ((r >> 1) & 3)) : ((j & 7) ^ (r & 7));
+    const int col = XH ? c * 8 : c * 4;
+    const int g = min(g0 + r, p.rows - 1);
+    const int b = g / p.nin;
+    const int n = g - b * p.nin;
+    bn[h] = n;
+    bx[h] = reinterpret_cast<const char*>(p.x) + ((size_t)g * cin + col) * esz;
+    bh[h] = p.hin ? p.hin + (size_t)b * p.sstride + (ptrdiff_t)(p.hin_rows + n) * cin + col
+                  : reinterpret_cast<const float*>(bx[h]);
+  }
+
+  // issue the loads of K-step s into ring stage st
+  auto issue = [&](int s, int st) __attribute__((always_inline)) {
+    const int tap = s / ksteps_per_tap;
+    const int c0 = (s - tap * ksteps_per_tap) * C::BK;
+    const int shift = (ktaps - 1 - tap) * dil;
+    const uint32_t sbase = (uint32_t)(st * STAGE);
+    if (a_on) lds_dma16(a_src + (ptrdiff_t)tap * cin + c0, a_dst + sbase);
+#pragma unroll
+    for (int h = 0; h < B_DMAS; ++h) {
+      const uint32_t dst = lds0 + sbase + A_BYTES + (uint32_t)(wave * B_PER_WAVE + h * 64) * 16;
+      const ptrdiff_t boff = c0 - (ptrdiff_t)shift * cin;
+      if (!b_on[h]) continue;
+      if (bn[h] >= shift) {
+        lds_dma16(bx[h] + boff * (ptrdiff_t)esz, dst);
+      } else if constexpr (XH) {
+        // an fp32 history row of an fp16 input: round through registers
+        const float* src = bh[h] + boff;
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 4);
+        *reinterpret_cast<f16x8*>(lds + (dst - lds0) + lane * 16) = to_half8(lo, hi);
+      } else {
+        lds_dma16(bh[h] + boff, dst);
+      }
+    }
+  };
+
+  // operand reads: lane l reads chunk l/16 of rows (fragment base + l%16)
+  const int lr = lane & 15, q = lane >> 4;
+  // (fragment rows start at multiples of 16, so the swizzle depends on l%16 only)
+  const int a_rd = ((wm * C::WTM + lr) * 4 + (q ^ ((lr >> 1) & 3))) * 16;
+  const int b_rd = XH ? A_BYTES + ((wn * C::WTN + lr) * 4 + (q ^ ((lr >> 1) & 3))) * 16 : 0;
+  const int b_rd0 = A_BYTES + ((wn * C::WTN + lr) * 8 + ((2 * q) ^ (lr & 7))) * 16;
+  const int b_rd1 = A_BYTES + ((wn * C::WTN + lr) * 8 + ((2 * q + 1) ^ (lr & 7))) * 16;
+
+  f32x4 acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  auto mma_step = [&](int st, f32x4 (&part)[C::FM][C::FN], auto first) __attribute__((always_inline)) {
+    const char* S = lds + st * STAGE;
+    f16x8 af[C::FM], bf[C::FN];
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) af[i] = *reinterpret_cast<const f16x8*>(S + a_rd + i * 16 * 64);
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+      if constexpr (XH) {
+        bf[j] = *reinterpret_cast<const f16x8*>(S + b_rd + j * 16 * 64);
+      } else {
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(S + b_rd0 + j * 16 * 128);
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(S + b_rd1 + j * 16 * 128);
+        bf[j] = to_half8(lo, hi);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) {
+        if (decltype(first)::value)
+          part[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        else
+          part[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], part[i][j], 0, 0, 0);
+      }
+  };
+
+  // prologue: K-steps s_begin .. s_begin + NS - 2 in flight
+#pragma unroll
+  for (int t = 0; t < C::NS - 1; ++t)
+    if (s_begin + t < nsteps) issue(s_begin + t, t);
+
+  int st = 0;  // ring stage of step s
+  for (int gs = s_begin; gs < nsteps; gs += GROUP_STEPS) {
+    const int ge = min(gs + GROUP_STEPS, nsteps);
+    f32x4 part[C::FM][C::FN];
+    for (int s = gs; s < ge; ++s) {
+      // this wave's loads of step s have landed once at most (steps issued
+      // after it) x OPS operations remain; then every wave's have
+      const int later = min(C::NS - 2, nsteps - 1 - s);
+      if constexpr (C::NS >= 4) {
+        if (later >= 2) wait_vm_lgkm<2 * OPS>();
+        else if (later == 1) wait_vm_lgkm<OPS>();
+        else wait_vm_lgkm<0>();
+      } else {
+        if (later >= 1) wait_vm_lgkm<OPS>();
+        else wait_vm_lgkm<0>();
+      }
+      block_barrier();
+      // refill the stage every wave finished reading at step s - 1
+      if (s + C::NS - 1 < nsteps) issue(s + C::NS - 1, st == 0 ? C::NS - 1 : st - 1);
+      if (s == gs)
+        mma_step(st, part, std::true_type{});
+      else
+        mma_step(st, part, std::false_type{});
+      st = st == C::NS - 1 ? 0 : st + 1;
+    }
+    if (SPLIT) {
+      const size_t gbase = (size_t)(gs / GROUP_STEPS) * p.rows;
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i) {
+        const int m = m0 + wm * C::WTM + i * 16 + (lane >> 4) * 4;
+        if (m >= p.M) continue;
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+          const int g = g0 + wn * C::WTN + j * 16 + lr;
+          if (g < p.rows) st4(p.partial + (gbase + g) * p.M + m, part[i][j]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) acc[i][j] += part[i][j];
+    }
+  }
+  if (SPLIT) return;
+
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) {
+    const int m = m0 + wm * C::WTM + i * 16 + (lane >> 4) * 4;
+    if (m >= p.M) continue;
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+      const int g = g0 + wn * C::WTN + j * 16 + lr;
+      if (g < p.rows) epilogue4(p, m, g, acc[i][j]);
+    }
+  }
+}
+
 template <class C, bool HALF, bool Q8>
 hipError_t launch_cfg_q(const ConvParams& p, hipStream_t s) {
   const int mtiles = (p.M + C::BM - 1) / C::BM;
@@ -734,6 +1013,29 @@ hipError_t launch_fold(const ConvParams& p, hipStream_t s, const LnArgs* ln) {
   return hipGetLastError();
 }
 
+template <class C, bool XH>
+hipError_t launch_dma_x(const ConvParams& p, hipStream_t s) {
+  const int mtiles = (p.M + C::BM - 1) / C::BM;
+  const int ntiles = (p.rows + C::BN - 1) / C::BN;
+  const long long tiles = (long long)mtiles * ntiles;
+  if (tiles <= 0) return hipSuccess;
+  if (p.splits <= 1) {
+    if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((conv_gemm_f16_dma_kernel<C, false, XH>), dim3((unsigned)tiles), dim3(C::NT), 0, s, p);
+    return hipGetLastError();
+  }
+  const long long nb = tiles * p.splits;
+  if (nb > 0x7fffffffLL || !p.partial) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((conv_gemm_f16_dma_kernel<C, true, XH>), dim3((unsigned)nb), dim3(C::NT), 0, s, p);
+  return hipGetLastError();
+}
+
+// fp16 rows (CH) or fp32 rows (CF) as the B operand
+template <class CH, class CF>
+hipError_t launch_dma(const ConvParams& p, hipStream_t s) {
+  return p.x_half ? launch_dma_x<CH, true>(p, s) : launch_dma_x<CF, false>(p, s);
+}
+
 // int8 weights (p.wscale set) or float weights
 template <class C, bool HALF = false>
 hipError_t launch_cfg(const ConvParams& p, hipStream_t s) {
@@ -769,6 +1071,10 @@ namespace {
 int skinny_bk(int cin) { return cin % 128 == 0 ? 128 : cin % 64 == 0 ? 64 : cin % 32 == 0 ? 32 : 16; }
 int half_bk(int cin) { return cin % 64 == 0 ? 64 : cin % 32 == 0 ? 32 : 16; }
 }  // namespace
+
+bool gemm_f16_direct(bool int8, int cin, int tile) {
+  return !int8 && cin % 32 == 0 && (tile == TILE_128x128 || tile == TILE_96x128);
+}
 
 int gemm_tile_bk(int tile, int cin, bool half) {
   if (tile == TILE_S64x16 || tile == TILE_S64x32) return skinny_bk(cin);
@@ -819,6 +1125,11 @@ hipError_t launch_blocks_f16(const ConvParams& p, int tile, hipStream_t s) {
   return bk == 64 ? launch_cfg<TileCfgH<BM, BN, WM, WN, 64, 32, IG>, true>(p, s)                    \
        : bk == 32 ? launch_cfg<TileCfgH<BM, BN, WM, WN, 32, 32, IG>, true>(p, s)                    \
                   : launch_cfg<TileCfgH<BM, BN, WM, WN, 16, 16, -1>, true>(p, s)
+  if (gemm_f16_direct(p.wscale != nullptr, p.cin, tile)) {
+    // direct-to-LDS loads, 4 (fp16 rows) or 3 (fp32 rows) K-steps in flight
+    if (tile == TILE_128x128) return launch_dma<TileCfgD<128, 128, 2, 4, 4>, TileCfgD<128, 128, 2, 4, 3>>(p, s);
+    return launch_dma<TileCfgD<96, 128, 2, 4, 4>, TileCfgD<96, 128, 2, 4, 3>>(p, s);
+  }
   switch (tile) {
     case TILE_128x128:
       // at most 32-deep K-steps: fewer staging registers, two blocks per CU

@@ -614,9 +614,10 @@ int run_gemm(const Ctx& cx, const ConvParams& pin, const LnArgs* ln = nullptr) {
   const bool fuse_ln = ln && p.splits > 1;
   if (fuse_ln) bytes += 8.0 * p.rows * ln->d;
   char name[48];
-  snprintf(name, sizeof(name), "conv_gemm_%s%s%dx%d_bk%d%s", f16 ? "f16_" : "", p.wscale ? "q8_" : "", bm,
+  const bool direct = f16 && gemm_f16_direct(p.wscale != nullptr, p.cin, tile);
+  snprintf(name, sizeof(name), "conv_gemm_%s%s%dx%d_bk%d%s", direct ? "f16_dma_" : f16 ? "f16_" : "", p.wscale ? "q8_" : "", bm,
            gemm_tile_bn(tile),
-           gemm_tile_bk(tile, p.cin, f16), p.splits > 1 ? (fuse_ln ? "_splitk_ln" : "_splitk") : "");
+           direct ? 32 : gemm_tile_bk(tile, p.cin, f16), p.splits > 1 ? (fuse_ln ? "_splitk_ln" : "_splitk") : "");
   {
     Prof pr(cx.v, cx.s, name, flops, bytes);
     if (f16)
