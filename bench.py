@@ -60,6 +60,11 @@ def parse():
 
 def _kernel_family(name):
     import re
+    # direct-to-LDS fp16 GEMM: TileCfgD<BM, BN, waves_m, waves_n, stages>, split, fp16 rows
+    m = re.search(r"TileCfgD<(\d+), (\d+), \d+, \d+, \d+>, (true|false)", name)
+    if m:
+        split = "_splitk" if m.group(3) == "true" else ""
+        return f"conv_gemm_f16_dma_{m.group(1)}x{m.group(2)}_bk32{split}"
     m = re.search(r"TileCfg(H?)<(\d+), (\d+), \d+, \d+, (\d+)(?:, -?\d+)*\s*>(?:, (true|false))?"
                   r"(?:, (true|false))?", name)
     if m:
