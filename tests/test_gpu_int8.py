@@ -112,14 +112,12 @@ def test_int8_streamed_equals_whole_bitwise():
     assert torch.equal(whole, parts) and torch.equal(st_w, st_p)
 
 
-def test_int8_full_size_250_frames():
-    """fp32 arithmetic on int8 weights: the north-star bar against the oracle
-    run on the same dequantized weights."""
-    print("\n[int8 full] 250-frame whole-sequence decode", flush=True)
-    path = os.path.join(GOLDEN, "qwen3_whole_int8.npz")
-    assert os.path.exists(path), f"missing {path}: run tests/golden/make_golden.py qwen3_whole_int8"
-    g = dict(np.load(path))
-    model = q8(S.QWEN3)
+@pytest.fixture(scope="module", params=["f32", "f16"])
+def int8_whole_250(request):
+    """The 250-frame stream decoded in one call with int8 weights: every big
+    launch expands its int8 layer once and runs the float-weight kernel."""
+    print(f"\n[int8 full] 250-frame whole-sequence decode, {request.param} operands", flush=True)
+    model = q8(S.QWEN3, request.param)
     dec, _ = decoder(model, 1, 1, 250)
     codes = S.workload_codes("qwen3_b1_t250_whole")
     pre = torch.empty(250 * model["hop"], device="cuda")
@@ -127,9 +125,31 @@ def test_int8_full_size_250_frames():
     pcm, _ = run_schedule(dec, codes, [250])
     dec.set_tap("pre_tanh", None)
     assert dec.status() == vb.VOCODER_OK
-    pcm = pcm[0].cpu().numpy().astype(np.float64)
-    pre = pre.cpu().numpy().astype(np.float64)
+    return (request.param, dec, codes, pcm[0].cpu().numpy().astype(np.float64),
+            pre.cpu().numpy().astype(np.float64))
+
+
+@pytest.mark.parametrize("int8_whole_250", ["f32"], indirect=True)
+def test_int8_full_size_250_frames(int8_whole_250):
+    """fp32 arithmetic on int8 weights: the north-star bar against the oracle
+    run on the same dequantized weights (stored values are for fp32
+    arithmetic; fp16 operands are checked at small shapes)."""
+    _, _, _, pcm, pre = int8_whole_250
+    path = os.path.join(GOLDEN, "qwen3_whole_int8.npz")
+    assert os.path.exists(path), f"missing {path}: run tests/golden/make_golden.py qwen3_whole_int8"
+    g = dict(np.load(path))
     idx = g["idx"]
     check_close(pcm[idx], g["pcm"], "int8 250 frames pcm", rel=REL_L2, max_abs=PCM_MAX_ABS)
     check_close(pre[idx], g["pre"], "int8 250 frames pre-tanh", rel=REL_L2)
     assert abs(np.linalg.norm(pre) / g["pre_norm"][0] - 1) < 1e-5
+
+
+def test_int8_full_size_streamed_equals_whole(int8_whole_250):
+    """A 1-frame chunk then 25s: their few-row launches dequantize int8 per
+    tile inside the GEMM, the whole decode's launches use the expanded layer;
+    the operands are the same, so the output is bitwise the same."""
+    precision, dec, codes, pcm_whole, _ = int8_whole_250
+    print(f"\n[int8 full] streamed 1 + 25x9 + 24, {precision} operands", flush=True)
+    pcm, _ = run_schedule(dec, codes, S.workload("qwen3_b1_t250_stream")["schedule"])
+    assert dec.status() == vb.VOCODER_OK
+    assert np.array_equal(pcm[0].cpu().numpy().astype(np.float64), pcm_whole)

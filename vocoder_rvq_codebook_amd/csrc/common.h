@@ -209,6 +209,10 @@ hipError_t launch_repack_convT(const float* src, void* dst, int cin, int cout, i
 hipError_t launch_expand_vec(const float* src, float* dst, int C, int phases, int Mpad, hipStream_t s);
 // int8 with one fp16 scale per 32 values of each row of a [rows][K] fp32 matrix
 hipError_t launch_quantize_rows(const float* src, long long rows, int K, void* q, void* scale, hipStream_t s);
+// int8 values q (groups of 32 with one fp16 scale each, values % 32 == 0) to
+// fp32, or fp16 when half: q * scale, as the int8 GEMM kernels dequantize
+hipError_t launch_dequant_rows(const void* q, const void* scale, long long values, void* dst, bool half,
+                               hipStream_t s);
 hipError_t launch_fill(void* dst, size_t bytes, hipStream_t s);
 hipError_t launch_reset_headers(void* state, long long sstride, int batch, uint64_t cfg_hash,
                                 hipStream_t s);

@@ -437,6 +437,34 @@ __global__ void repack_convT_kernel(const float* __restrict__ src, T* __restrict
 // phonon", section Weights): the values rounded to fp16, scale = fp16(max |v| /
 // 127), each value rint(v / scale) (ties to even); divisions correctly rounded
 // in fp32; a zero group keeps scale 0 and values 0.  One thread per group.
+// int8 weights back to the GEMM operand: value = q * scale of its group of 32
+// (exact in fp32), stored as fp32 or rounded once to fp16 -- what the int8
+// GEMM kernels compute per tile.  One thread per 8 values.
+__global__ void dequant_rows_kernel(const int8_t* __restrict__ q, const _Float16* __restrict__ scale,
+                                    long long units, void* __restrict__ dst, int half) {
+  const long long u = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (u >= units) return;
+  const uint2 w = *reinterpret_cast<const uint2*>(q + u * 8);
+  const float sc = (float)scale[u >> 2];
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = (float)(int8_t)(w.x >> (8 * i)) * sc;
+    v[4 + i] = (float)(int8_t)(w.y >> (8 * i)) * sc;
+  }
+  if (half) {
+    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+    h8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = (_Float16)v[i];
+    reinterpret_cast<h8*>(dst)[u] = r;
+  } else {
+    f32x4* o = reinterpret_cast<f32x4*>(dst) + 2 * u;
+    o[0] = (f32x4){v[0], v[1], v[2], v[3]};
+    o[1] = (f32x4){v[4], v[5], v[6], v[7]};
+  }
+}
+
 __global__ void quantize_rows_kernel(const float* __restrict__ src, long long groups, int8_t* __restrict__ q,
                                      _Float16* __restrict__ scale) {
   const long long gi = (long long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -614,6 +642,16 @@ hipError_t launch_quantize_rows(const float* src, long long rows, int K, void* q
   if (groups == 0) return hipSuccess;
   hipLaunchKernelGGL(quantize_rows_kernel, dim3((unsigned)cdiv(groups, 256)), dim3(256), 0, s, src, groups,
                      (int8_t*)q, (_Float16*)scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_rows(const void* q, const void* scale, long long values, void* dst, bool half,
+                               hipStream_t s) {
+  if (values <= 0) return hipSuccess;
+  if (values % 32) return hipErrorInvalidValue;
+  const long long units = values / 8;
+  hipLaunchKernelGGL(dequant_rows_kernel, dim3((unsigned)cdiv(units, 256)), dim3(256), 0, s, (const int8_t*)q,
+                     (const _Float16*)scale, units, dst, half ? 1 : 0);
   return hipGetLastError();
 }
 

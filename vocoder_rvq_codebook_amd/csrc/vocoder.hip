@@ -141,6 +141,8 @@ struct Plan {
   int d = 0, hd = 0, half = 0, hop = 0;
   bool f16 = false;  // fp16 GEMM operands (packed weights in fp16)
   long long max_gemm_values = 0;  // largest packed GEMM weight (values)
+  long long max_q8_values = 0;    // largest int8 GEMM weight (values)
+  long long ws_wdeq = 0;          // an int8 layer expanded to the GEMM operand type
   long long raw_count = 0;
   // packed
   long long raw_codebooks = 0, codebooks = 0;
@@ -225,6 +227,7 @@ bool make_plan(const vocoder_config* cp, Plan& P) {
     }
     g.bias = K(g.Mpad);
     P.max_gemm_values = std::max(P.max_gemm_values, welems);
+    if (g.q8) P.max_q8_values = std::max(P.max_q8_values, welems);
   };
 
   P.state_floats = VOC_STATE_HEADER_FLOATS;
@@ -374,6 +377,7 @@ bool make_plan(const vocoder_config* cp, Plan& P) {
     P.partial_aux_floats = 8LL << 20;
     for (int j = 0; j < 2; ++j) P.ws_partial_aux[j] = Wk(P.partial_aux_floats);
   }
+  if (P.max_q8_values > 0) P.ws_wdeq = Wk(P.f16 ? (P.max_q8_values + 1) / 2 : P.max_q8_values);
   P.ws_floats = ws;
   // int8 weights are quantized at create time from a float repack staged in
   // the workspace
@@ -525,6 +529,7 @@ struct Ctx {
   bool quiet = false;  // no taps
   float* partial = nullptr;       // split-K partials of launches on this stream
   long long partial_floats = 0;
+  float* wdeq = nullptr;          // room for one expanded int8 layer (caller's stream only)
 };
 
 ConvParams base_params(const Ctx& cx, const GemmW& g, const float* x, int rows, int nin, int dil,
@@ -596,6 +601,21 @@ int run_gemm(const Ctx& cx, const ConvParams& pin, const LnArgs* ln = nullptr) {
   const int tile = pick_tile(p.M, p.rows);
   const int bm = gemm_tile_bm(tile);
   const int mt = (p.M + bm - 1) / bm;
+  const bool f16 = cx.v->P.f16;
+  if (p.wscale && cx.wdeq && (tile == TILE_128x128 || tile == TILE_96x128)) {
+    // int8 weights of a many-row launch: expand the layer once into the
+    // workspace (q * scale, rounded to fp16 in fp16 mode, exactly what the
+    // int8 kernels stage per tile) and run the float-weight kernel on it, so
+    // the operands and the bits are the same
+    const long long values = (long long)round_up_i(p.M, 128) * p.k * p.cin;
+    if (values > cx.v->P.max_q8_values) return VOCODER_EINVAL;
+    {
+      Prof pr(cx.v, cx.s, "dequant_int8", 0, values * (1.0 + 2.0 / 32 + (f16 ? 2.0 : 4.0)));
+      HIP_OK(launch_dequant_rows(p.w, p.wscale, values, cx.wdeq, f16, cx.s));
+    }
+    p.w = cx.wdeq;
+    p.wscale = nullptr;
+  }
   p.splits = pick_splits(cx.partial_floats, tile, p.M, p.rows, p.k, p.cin);
   p.partial = p.splits > 1 ? cx.partial : nullptr;
   // A-tile rows read must lie inside the packed (zero-padded) weight rows
@@ -608,7 +628,6 @@ int run_gemm(const Ctx& cx, const ConvParams& pin, const LnArgs* ln = nullptr) {
     if (p.out[o].dst) bytes += (p.out[o].half ? 2.0 : 4.0) * (double)p.rows * p.M;
   if (p.resid) bytes += 4.0 * p.rows * p.M;
   if (p.mrf_mode == MRF_ACCUM || p.mrf_mode == MRF_LAST) bytes += 4.0 * p.rows * p.M;
-  const bool f16 = cx.v->P.f16;
   if (p.wscale) bytes -= (4.0 - 1.0625) * p.M * K;  // int8 weights and their scales
   else if (f16) bytes -= 2.0 * p.M * K;             // fp16 weights
   const bool fuse_ln = ln && p.splits > 1;
@@ -843,6 +862,7 @@ int decode_launches(vocoder* v, const int32_t* codes, int batch, int n_frames, c
   cx.quiet = prefill;
   cx.partial = v->ws + P.ws_partial;
   cx.partial_floats = P.partial_floats;
+  cx.wdeq = P.ws_wdeq ? v->ws + P.ws_wdeq : nullptr;
   cx.v = v;
   cx.s = (hipStream_t)stream;
   cx.sin_ = (const float*)state_in;
@@ -1036,6 +1056,7 @@ int decode_launches(vocoder* v, const int32_t* codes, int batch, int n_frames, c
         bc.s = v->aux[j];
         bc.partial = ws + P.ws_partial_aux[j];
         bc.partial_floats = P.partial_aux_floats;
+        bc.wdeq = nullptr;  // the int8 kernels dequantize per tile
         tb = ws + P.ws_conc_T[j];
         xr = ws + P.ws_conc_Xr[j];
         an = ws + P.ws_conc_An[j];
