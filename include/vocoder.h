@@ -115,8 +115,11 @@ typedef struct vocoder_config {
  * conv, transposed-conv and linear weights of at least 16,384 values whose
  * input channel count is a multiple of 32 (all of them at the Qwen3-TTS-12Hz
  * shape); the others, the codebooks, the vectors and the final C -> 1 conv
- * keep their float storage.  Every such weight is read as 1.0625 bytes per
- * value.  Weights must lie within the fp16 range. */
+ * keep their float storage.  Packed, every such weight takes 1.0625 bytes
+ * per value; launches with few rows read it so, while a launch with many rows
+ * first expands its layer into the workspace (4 or 2 bytes per value; the
+ * workspace holds the largest int8 layer) and reads that.  Weights must lie
+ * within the fp16 range. */
 #define VOCODER_WEIGHTS_FLOAT 0
 #define VOCODER_WEIGHTS_INT8 1
 
