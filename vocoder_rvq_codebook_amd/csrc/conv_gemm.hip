@@ -738,7 +738,10 @@ struct TileCfgD {
 };
 
 __device__ __forceinline__ void lds_dma16(const void* gaddr, uint32_t lds_wave_base) {
-  // m0 holds the wave's LDS destination; the address is wave-uniform
+  // m0 holds the wave's LDS destination; the address is wave-uniform.  m0 is
+  // a reserved register the compiler does not preserve across asm, so these
+  // kernels must not otherwise use it (checked on the generated code by the
+  // test suite: every m0 write in them is this one, right before its load).
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
                :
                : "s"(__builtin_amdgcn_readfirstlane(lds_wave_base)), "v"(gaddr)
