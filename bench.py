@@ -175,7 +175,13 @@ def cpu_baseline(model, W, codes_1, frames):
         O.decode_whole(model, Wf, codes_1[:frames], dtype=np.float32)
         el = time.perf_counter() - t0
     audio = frames * FRAME_SECONDS
-    return {"value": audio / el, "unit": "audio-s/s", "cores": int(used), "kind": "oracle",
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), cpu)
+    except OSError:
+        pass
+    return {"value": audio / el, "unit": "audio-s/s", "cores": int(used), "kind": "oracle", "cpu_model": cpu,
             "sample": f"1 stream x {frames} frames ({audio:g} s of audio) from a fresh state, float32 numpy "
                       f"oracle, {el:.1f} s wall"}
 
@@ -366,14 +372,18 @@ def main():
     vb.vocoder_profile_begin(dec.handle)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    # an event after every call as well: per-call durations for the median and quartiles
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     t0 = time.perf_counter()
     ev0.record(stream)
-    for _ in range(args.steps):
+    for i in range(args.steps):
         dec.decode(chunk, st_a, st_b, pcm)
         st_a, st_b = st_b, st_a
+        evs[i].record(stream)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    call_ms = np.array([ev0.elapsed_time(evs[0])] + [evs[i - 1].elapsed_time(evs[i]) for i in range(1, args.steps)])
     prof = vb.vocoder_profile_end(dec.handle)
     if dec.status() != vb.VOCODER_OK:
         raise SystemExit("device reported an error during the timed steps")
@@ -401,6 +411,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(elapsed / args.steps * 1e3, 3),
+        "call_ms": {"median": round(float(np.median(call_ms)), 3), "p25": round(float(np.percentile(call_ms, 25)), 3),
+                    "p75": round(float(np.percentile(call_ms, 75)), 3)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
