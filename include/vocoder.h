@@ -60,7 +60,7 @@ extern "C" {
 
 /* Decoder shape.  All channel counts that feed a convolution or linear layer
  * must be multiples of 16; model_dim is at most 4096; model_dim / n_heads (the
- * head size) must be at most 256 and a multiple of 4.  Qwen3-TTS-12Hz shape: 16, 2048, 512, 1024, 8, 16, 72, 4096,
+ * head size) must be at most 256 and a multiple of 8.  Qwen3-TTS-12Hz shape: 16, 2048, 512, 1024, 8, 16, 72, 4096,
  * 10000, 1e-5, 3, 2, {2,2}, 1536, 7, 4, {8,5,4,3}, 3, {3,7,11}, 3, {1,3,5}, 7. */
 typedef struct vocoder_config {
   int32_t n_codebooks;      /* codes per frame (16) */

@@ -58,7 +58,7 @@ def test_qwen3_sizes():
 def test_invalid_configs_rejected():
     good = dict(S.MINI)
     assert vb.vocoder_raw_weights_count(vb.make_config(good, 1, 1)) > 0
-    for key, val in [("embed_dim", 24), ("model_dim", 66), ("n_heads", 3), ("n_heads", 32), ("window", 300),
+    for key, val in [("embed_dim", 24), ("model_dim", 66), ("n_heads", 3), ("n_heads", 16), ("n_heads", 32), ("window", 300),
                      ("ffn_dim", 0), ("voc_ch0", 200)]:
         bad = dict(good)
         bad[key] = val

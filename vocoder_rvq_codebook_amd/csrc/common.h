@@ -194,11 +194,12 @@ hipError_t launch_gather(const int32_t* codes, const float* codebooks, int Q, in
 int layernorm_nv(int d);
 hipError_t launch_layernorm(const float* x, const float* g, const float* b, float eps, int rows, int d,
                             float* out, int T, float* hist, int H, long long sstride, hipStream_t s);
-hipError_t launch_rope_kv(float* qkv, const float* rope_tab, int rows, int T, int n_heads, int hd,
-                          float* k_hist, float* v_hist, int W, long long sstride, hipStream_t s);
-hipError_t launch_attention(const float* qkv, const float* k_state, const float* v_state,
-                            long long sstride, const int* pos, int batch, int T, int n_heads, int hd,
-                            int W, float* out, hipStream_t s);
+// Windowed attention of the new frames; RoPE is applied to their q and k as
+// they are staged, and their rotated keys and values (the last W frames of
+// each stream) go to k_state_out / v_state_out.
+hipError_t launch_attention(const float* qkv, const float* k_state, const float* v_state, long long sstride,
+                            const int* pos, int batch, int T, int n_heads, int hd, int W, const float* rope_tab,
+                            float* k_state_out, float* v_state_out, float* out, hipStream_t s);
 hipError_t launch_conv_post(const float* x, const float* hin, long long sstride, int H, const float* w,
                             const float* bias, int C, int k, int rows, int nin, float* pcm,
                             float* pre_tanh, hipStream_t s);

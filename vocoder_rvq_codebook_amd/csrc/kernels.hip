@@ -133,43 +133,6 @@ __global__ __launch_bounds__(64 * NV) void layernorm_kernel(const float* __restr
 }
 
 // ---------------------------------------------------------------------------
-// RoPE on q and k (rotate-half pairs (i, i + hd/2)) in place in the fused
-// qkv rows; the last W frames' rotated k and raw v go to the state slots.
-// ---------------------------------------------------------------------------
-__global__ void rope_kv_kernel(float* __restrict__ qkv, const float* __restrict__ tab, int rows, int T,
-                               int n_heads, int hd, float* __restrict__ kh, float* __restrict__ vh, int W,
-                               long long sstride) {
-  const int half = hd / 2;
-  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long long per_row = (long long)n_heads * half;
-  if (idx >= (long long)rows * per_row) return;
-  const int row = (int)(idx / per_row);
-  const int r = (int)(idx - (long long)row * per_row);
-  const int h = r / half, i = r - h * half;
-  const int d = n_heads * hd;
-  const int b = row / T, t = row - b * T;
-  const float c = tab[((size_t)row * half + i) * 2 + 0];
-  const float sn = tab[((size_t)row * half + i) * 2 + 1];
-  float* q = qkv + (size_t)row * 3 * d + h * hd;
-  float* k = q + d;
-  const float* v = q + 2 * d;
-  const float q1 = q[i], q2 = q[i + half];
-  q[i] = q1 * c - q2 * sn;
-  q[i + half] = q1 * sn + q2 * c;
-  const float k1 = k[i], k2 = k[i + half];
-  const float kr1 = k1 * c - k2 * sn, kr2 = k1 * sn + k2 * c;
-  k[i] = kr1;
-  k[i + half] = kr2;
-  if (W > 0 && t >= T - W) {
-    const size_t o = (size_t)b * sstride + (size_t)(W - T + t) * d + h * hd;
-    kh[o + i] = kr1;
-    kh[o + i + half] = kr2;
-    vh[o + i] = v[i];
-    vh[o + i + half] = v[i + half];
-  }
-}
-
-// ---------------------------------------------------------------------------
 // Sliding-window attention.  Block = (query tile of QT frames, head, stream);
 // the keys and values the tile needs (state window + new frames) are staged
 // in LDS.  Query at absolute position P attends positions [P - W, P]; lane
@@ -179,9 +142,24 @@ __global__ void rope_kv_kernel(float* __restrict__ qkv, const float* __restrict_
 constexpr int ATT_QT = 16;
 constexpr int ATT_THREADS = 256;
 
+// RoPE of one rotate-half pair of 4-wide pieces (channels c..c+3 and
+// c+hd/2..c+hd/2+3) of frame row `row` (table entries (cos, sin) per row and i)
+__device__ __forceinline__ void rope4(f32x4& x1, f32x4& x2, const float* __restrict__ tab, size_t row, int half,
+                                      int c) {
+  const float* cs = tab + (row * half + c) * 2;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float co = cs[2 * e], sn = cs[2 * e + 1];
+    const float a = x1[e], bb = x2[e];
+    x1[e] = a * co - bb * sn;
+    x2[e] = a * sn + bb * co;
+  }
+}
+
 __global__ __launch_bounds__(ATT_THREADS) void attention_kernel(
     const float* __restrict__ qkv, const float* __restrict__ ks, const float* __restrict__ vs, long long sstride,
-    const int* __restrict__ pos, int T, int n_heads, int hd, int W, float* __restrict__ out) {
+    const int* __restrict__ pos, int T, int n_heads, int hd, int W, const float* __restrict__ tab,
+    float* __restrict__ ks_out, float* __restrict__ vs_out, float* __restrict__ out) {
   extern __shared__ float smem[];
   const int d = n_heads * hd;
   const int t0 = blockIdx.x * ATT_QT, h = blockIdx.y, b = blockIdx.z;
@@ -193,33 +171,55 @@ __global__ __launch_bounds__(ATT_THREADS) void attention_kernel(
   float* Vs = Ks + (ATT_QT + W) * ldk;    // [(QT + W)][hd]
   float* Qs = Vs + (ATT_QT + W) * hd;     // [QT][hd]
   const int tid = threadIdx.x;
-  // staged with 16-byte loads (hd is a multiple of 4)
-  const int hd4 = hd / 4;
-  for (int idx = tid; idx < nk * hd4; idx += ATT_THREADS) {
-    const int r = idx / hd4, c = (idx - r * hd4) * 4;
+  // Staged with 16-byte loads, a rotate-half pair of pieces per thread (hd is
+  // a multiple of 8).  State rows hold rotated keys already; new frames' q
+  // and k are rotated here, and the block whose query tile holds a new frame
+  // writes that frame's rotated key and its value to the state tail.
+  const int half = hd / 2, half4 = half / 4;
+  for (int idx = tid; idx < nk * half4; idx += ATT_THREADS) {
+    const int r = idx / half4, c = (idx - r * half4) * 4;
     const int j = t0 + r;  // concat index: j < W state row, else new frame j - W
-    f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
+    f32x4 k1 = {0.f, 0.f, 0.f, 0.f}, k2 = k1, v1 = k1, v2 = k1;
     if (j < W) {
       if (p0 - W + j >= 0) {
         const size_t o = (size_t)b * sstride + (size_t)j * d + h * hd + c;
-        kv = *reinterpret_cast<const f32x4*>(ks + o);
-        vv = *reinterpret_cast<const f32x4*>(vs + o);
+        k1 = *reinterpret_cast<const f32x4*>(ks + o);
+        k2 = *reinterpret_cast<const f32x4*>(ks + o + half);
+        v1 = *reinterpret_cast<const f32x4*>(vs + o);
+        v2 = *reinterpret_cast<const f32x4*>(vs + o + half);
       }
     } else if (j - W < T) {
-      const float* row = qkv + ((size_t)b * T + (j - W)) * 3 * d;
-      kv = *reinterpret_cast<const f32x4*>(row + d + h * hd + c);
-      vv = *reinterpret_cast<const f32x4*>(row + 2 * d + h * hd + c);
+      const int t = j - W;
+      const size_t grow = (size_t)b * T + t;
+      const float* row = qkv + grow * 3 * d + h * hd + c;
+      k1 = *reinterpret_cast<const f32x4*>(row + d);
+      k2 = *reinterpret_cast<const f32x4*>(row + d + half);
+      v1 = *reinterpret_cast<const f32x4*>(row + 2 * d);
+      v2 = *reinterpret_cast<const f32x4*>(row + 2 * d + half);
+      rope4(k1, k2, tab, grow, half, c);
+      if (W > 0 && t >= t0 && t < t0 + nq && t >= T - W) {
+        const size_t o = (size_t)b * sstride + (size_t)(W - T + t) * d + h * hd + c;
+        *reinterpret_cast<f32x4*>(ks_out + o) = k1;
+        *reinterpret_cast<f32x4*>(ks_out + o + half) = k2;
+        *reinterpret_cast<f32x4*>(vs_out + o) = v1;
+        *reinterpret_cast<f32x4*>(vs_out + o + half) = v2;
+      }
     }
     float* kd = Ks + r * ldk + c;
-    kd[0] = kv.x; kd[1] = kv.y; kd[2] = kv.z; kd[3] = kv.w;
-    float* vd = Vs + r * hd + c;
-    vd[0] = vv.x; vd[1] = vv.y; vd[2] = vv.z; vd[3] = vv.w;
+    kd[0] = k1.x; kd[1] = k1.y; kd[2] = k1.z; kd[3] = k1.w;
+    kd[half] = k2.x; kd[half + 1] = k2.y; kd[half + 2] = k2.z; kd[half + 3] = k2.w;
+    *reinterpret_cast<f32x4*>(Vs + r * hd + c) = v1;
+    *reinterpret_cast<f32x4*>(Vs + r * hd + c + half) = v2;
   }
-  for (int idx = tid; idx < nq * hd4; idx += ATT_THREADS) {
-    const int r = idx / hd4, c = (idx - r * hd4) * 4;
-    const f32x4 qv = *reinterpret_cast<const f32x4*>(qkv + ((size_t)b * T + t0 + r) * 3 * d + h * hd + c);
-    float* qd = Qs + r * hd + c;
-    qd[0] = qv.x; qd[1] = qv.y; qd[2] = qv.z; qd[3] = qv.w;
+  for (int idx = tid; idx < nq * half4; idx += ATT_THREADS) {
+    const int r = idx / half4, c = (idx - r * half4) * 4;
+    const size_t grow = (size_t)b * T + t0 + r;
+    const float* row = qkv + grow * 3 * d + h * hd + c;
+    f32x4 q1 = *reinterpret_cast<const f32x4*>(row);
+    f32x4 q2 = *reinterpret_cast<const f32x4*>(row + half);
+    rope4(q1, q2, tab, grow, half, c);
+    *reinterpret_cast<f32x4*>(Qs + r * hd + c) = q1;
+    *reinterpret_cast<f32x4*>(Qs + r * hd + c + half) = q2;
   }
   __syncthreads();
   const int lane = tid & 63, wave = tid >> 6;
@@ -576,22 +576,14 @@ hipError_t launch_layernorm(const float* x, const float* g, const float* b, floa
   return hipGetLastError();
 }
 
-hipError_t launch_rope_kv(float* qkv, const float* rope_tab, int rows, int T, int n_heads, int hd, float* k_hist,
-                          float* v_hist, int W, long long sstride, hipStream_t s) {
-  const long long n = (long long)rows * n_heads * (hd / 2);
-  hipLaunchKernelGGL(rope_kv_kernel, dim3(cdiv(n, 256)), dim3(256), 0, s, qkv, rope_tab, rows, T, n_heads, hd,
-                     k_hist, v_hist, W, sstride);
-  return hipGetLastError();
-}
-
 hipError_t launch_attention(const float* qkv, const float* k_state, const float* v_state, long long sstride,
-                            const int* pos, int batch, int T, int n_heads, int hd, int W, float* out,
-                            hipStream_t s) {
+                            const int* pos, int batch, int T, int n_heads, int hd, int W, const float* rope_tab,
+                            float* k_state_out, float* v_state_out, float* out, hipStream_t s) {
   const size_t smem = ((size_t)(ATT_QT + W) * (hd + 1) + (size_t)(ATT_QT + W) * hd + (size_t)ATT_QT * hd) *
                       sizeof(float);
-  if (smem > 64 * 1024) return hipErrorInvalidValue;
+  if (smem > 64 * 1024 || hd % 8) return hipErrorInvalidValue;
   hipLaunchKernelGGL(attention_kernel, dim3(cdiv(T, ATT_QT), n_heads, batch), dim3(ATT_THREADS), smem, s, qkv,
-                     k_state, v_state, sstride, pos, T, n_heads, hd, W, out);
+                     k_state, v_state, sstride, pos, T, n_heads, hd, W, rope_tab, k_state_out, v_state_out, out);
   return hipGetLastError();
 }
 

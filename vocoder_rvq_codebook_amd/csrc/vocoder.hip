@@ -36,7 +36,7 @@ bool config_valid(const vocoder_config* c) {
   if (!m16(c->embed_dim) || !m16(c->model_dim) || !m16(c->ffn_dim)) return false;
   if (c->n_layers < 0 || c->n_layers > 64 || c->n_heads < 1 || c->model_dim % c->n_heads) return false;
   const int hd = c->model_dim / c->n_heads;
-  if (hd % 4 || hd > 256) return false;  // rotate-half pairs; attention stages 16-byte rows
+  if (hd % 8 || hd > 256) return false;  // rotate-half pairs of 16-byte pieces
   if (c->model_dim > 4096) return false;  // a LayerNorm row is held in one wave's registers
   if (c->window < 0 || c->window > 255) return false;
   // the attention kernel stages (16 + window) keys and values plus 16 queries in 64 KB of LDS
@@ -933,15 +933,13 @@ int decode_launches(vocoder* v, const int32_t* codes, int batch, int n_frames, c
     const Slot& sk = P.slots[L.slot_k];
     const Slot& sv = P.slots[L.slot_v];
     {
-      Prof pr(v, cx.s, "rope_kv", 0, 4.0 * R * d * 4);
-      HIP_OK(launch_rope_kv(qkv, rope, R, T, c.n_heads, P.hd, cx.sout + sk.off, cx.sout + sv.off, c.window,
-                            cx.sstride, cx.s));
-    }
-    {
+      // RoPE on the new frames' q and k, and their K/V into the state tail, happen in the staging
       const double keys = (double)c.window + 1;
-      Prof pr(v, cx.s, "attention", 4.0 * R * keys * d, 4.0 * ((double)B * c.window * 2 * d + 3.0 * R * d + R * d));
+      const double tail = (double)B * std::min(T, c.window) * 2 * d;
+      Prof pr(v, cx.s, "attention", 4.0 * R * keys * d,
+              4.0 * ((double)B * c.window * 2 * d + 3.0 * R * d + R * d + tail) + 8.0 * R * (P.hd / 2));
       HIP_OK(launch_attention(qkv, cx.sin_ + sk.off, cx.sin_ + sv.off, cx.sstride, pos, B, T, c.n_heads, P.hd,
-                              c.window, att, cx.s));
+                              c.window, rope, cx.sout + sk.off, cx.sout + sv.off, att, cx.s));
     }
     {
       ConvParams p = base_params(cx, L.o, att, R, T, 1, -1);
