@@ -47,7 +47,10 @@ SCHEDULES = {
 
 
 @pytest.mark.parametrize("name", list(SCHEDULES))
-@pytest.mark.parametrize("model", [S.MINI, dict(S.MINI, name="mini_f16", precision="f16")], ids=["f32", "f16"])
+@pytest.mark.parametrize("model", [S.MINI, dict(S.MINI, name="mini_f16", precision="f16"),
+                                   dict(S.MINI, name="mini_q8", weights="int8"),
+                                   dict(S.MINI, name="mini_q8_f16", weights="int8", precision="f16")],
+                         ids=["f32", "f16", "int8", "int8_f16"])
 def test_graph_replays_equal_eager(name, model):
     schedule = SCHEDULES[name]
     T = sum(schedule)

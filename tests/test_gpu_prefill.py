@@ -73,6 +73,27 @@ def test_prefill_state_equals_decode_state(model):
                         rel=rel)
 
 
+@pytest.mark.parametrize("precision", ["f32", "f16"])
+def test_prefill_state_equals_decode_state_int8(precision):
+    """int8 weights: the prefilled state is bitwise the decoded one (the
+    decodes against the oracle on dequantized weights are tested with the
+    int8 format itself)."""
+    model = dict(S.MINI, name=f"mini_q8_{precision}", weights="int8", precision=precision)
+    tail = tail_frames(model)
+    B, warm = 2, [0, 9]
+    dec, _ = decoder(model, 31, B, tail + 7)
+    codes = S.make_codes(model, B, max(warm) + tail + 7, 72)
+    for T in (tail + 7, 3):
+        st0 = _warm(dec, codes, warm)
+        chunk = torch.from_numpy(np.stack([codes[b, nw:nw + T] for b, nw in enumerate(warm)])).cuda()
+        st_dec, st_pre = torch.empty_like(st0), torch.empty_like(st0)
+        dec.decode(chunk, st0, st_dec)
+        dec.prefill(chunk, st0, st_pre)
+        torch.cuda.synchronize()
+        assert dec.status() == vb.VOCODER_OK
+        assert torch.equal(st_pre, st_dec), f"T={T}"
+
+
 def test_prefill_rejects_bad_arguments_and_reports_bad_codes():
     model = S.TINY
     dec, _ = decoder(model, 0, 2, 8)
