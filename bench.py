@@ -191,7 +191,7 @@ def stream_latency(args, wl, torch, S, Decoder, vb):
     (warm-up passes untimed), timing every chunk call with HIP events on the
     caller's stream.  Prints one JSON line (not the headline metric)."""
     model = dict(wl["model"], precision=args.precision, weights=args.weights)
-    sched = wl["schedule"]
+    sched = [wl["frames"]] if wl["schedule"] == "whole" else wl["schedule"]
     B = wl["batch"]
     W = S.make_weights(model, wl["weight_seed"])
     codes = S.workload_codes(args.workload)
@@ -343,7 +343,7 @@ def main():
     wl = S.workload(args.workload)
     model = dict(wl["model"], precision=args.precision, weights=args.weights)
     peak = FP16_MFMA_PEAK_TFLOPS if args.precision == "f16" else FP32_MFMA_PEAK_TFLOPS
-    if isinstance(wl["schedule"], list):
+    if isinstance(wl["schedule"], list) or wl["schedule"] == "whole":
         stream_latency(args, wl, torch, S, Decoder, vb)
         return
     if wl["schedule"] != "warm_then_25":
