@@ -203,10 +203,12 @@ hipError_t launch_attention(const float* qkv, const float* k_state, const float*
 hipError_t launch_conv_post(const float* x, const float* hin, long long sstride, int H, const float* w,
                             const float* bias, int C, int k, int rows, int nin, float* pcm,
                             float* pre_tanh, hipStream_t s);
+// Weight repacking into GEMM rows [Mpad][k * cin]: tap-major ([k][cin]) or,
+// with slab (cin a multiple of 32; the fp16 GEMMs), [cin / 32][k][32].
 hipError_t launch_repack_conv(const float* src, void* dst, int M, int Mpad, int cin, int k, bool half_out,
-                              hipStream_t s);
+                              bool slab, hipStream_t s);
 hipError_t launch_repack_convT(const float* src, void* dst, int cin, int cout, int stride, int Mpad,
-                               bool half_out, hipStream_t s);
+                               bool half_out, bool slab, hipStream_t s);
 hipError_t launch_expand_vec(const float* src, float* dst, int C, int phases, int Mpad, hipStream_t s);
 // int8 with one fp16 scale per 32 values of each row of a [rows][K] fp32 matrix
 hipError_t launch_quantize_rows(const float* src, long long rows, int K, void* q, void* scale, hipStream_t s);

@@ -494,6 +494,17 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
     if (s_begin >= nsteps) return;
   }
 
+  // K order.  SLAB 32 (channel counts that are multiples of 32): slab j of
+  // 32 reduction values is channels 32 (j / k) .. + 32 of tap j % k
+  // (channel-major), so that the taps of one channel slab are consecutive.
+  // The weights are packed in that order ([Mpad][cin / 32][k][32]), so a
+  // K-step's weights are contiguous; its input rows are NSUB = BK / 32 slabs,
+  // each load slot belonging to one of them (its own tap shift and
+  // channels).  SLAB 16: tap-major ([Mpad][k][cin]), one contiguous run of BK
+  // channels of one tap per K-step.  Every fp16 kernel orders the reduction
+  // this way.
+  constexpr bool CM = C::SLAB == 32;
+  constexpr int NSUB = CM ? C::BK / 32 : 1;
   // int8 weights use the same slots: 8 values (two words) and their scale
   const _Float16* a_base[C::A_LD];
   const int8_t* q_base[C::A_LD];
@@ -517,18 +528,20 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
   const float* bh[C::B_LD];
   const bool x_half = p.x_half != 0;
   const int x_esz = x_half ? 2 : 4;
-  int bn[C::B_LD], b_lds[C::B_LD];
+  int bn[C::B_LD], b_lds[C::B_LD], b_sub[C::B_LD];
 #pragma unroll
   for (int i = 0; i < C::B_LD; ++i) {
     int idx = tid + i * C::NT;
     if (C::B_CH % C::NT != 0 && idx >= C::B_CH) idx = C::B_CH - 1;
     const int row = idx / C::KC, col = (idx % C::KC) * 8;
+    b_sub[i] = CM ? col / 32 : 0;
+    const int gcol = CM ? col % 32 : col;
     const int g = min(g0 + row, p.rows - 1);
     const int b = g / p.nin;
     const int n = g - b * p.nin;
     bn[i] = n;
-    bxb[i] = reinterpret_cast<const char*>(p.x) + ((size_t)g * cin + col) * x_esz;
-    bh[i] = p.hin ? p.hin + (size_t)b * p.sstride + (ptrdiff_t)(p.hin_rows + n) * cin + col
+    bxb[i] = reinterpret_cast<const char*>(p.x) + ((size_t)g * cin + gcol) * x_esz;
+    bh[i] = p.hin ? p.hin + (size_t)b * p.sstride + (ptrdiff_t)(p.hin_rows + n) * cin + gcol
                   : reinterpret_cast<const float*>(bxb[i]);
     b_lds[i] = row * C::LDK + col;
   }
@@ -537,16 +550,51 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
   // B: 8 fp32 values (rb_lo, rb_hi) or, for an fp16 input row, the 8 halves'
   // bits in rb_lo (bhalf set); rounded / stored as fp16 at the LDS store
   f32x4 rb_lo[C::B_LD], rb_hi[C::B_LD];
-  int b_shift = 0;  // tap shift of the staged step
+  int b_shift[C::B_LD];  // tap shift of each slot's slab in the staged step
   int2 rq[C::A_LD];
   float rs[C::A_LD];
 
+  // (channel slab, tap) of the next slab to load: K-steps are loaded in
+  // order, so it advances without divisions
+  int run_cb = 0, run_tap = 0;
+  if constexpr (CM) {
+    const int j0 = s_begin * NSUB;
+    run_cb = j0 / ktaps;
+    run_tap = j0 - run_cb * ktaps;
+  }
   auto gload = [&](int s) {
-    const int tap = s / ksteps_per_tap;
-    const int c0 = (s - tap * ksteps_per_tap) * C::BK;
-    const int shift = (ktaps - 1 - tap) * dil;
-    const ptrdiff_t aoff = (ptrdiff_t)tap * cin + c0;
-    const ptrdiff_t boff = c0 - (ptrdiff_t)shift * cin;
+    // each B slot's tap shift and input offset for this step (its own slab)
+    int shift_of[C::B_LD];
+    ptrdiff_t boff_of[C::B_LD];
+    ptrdiff_t aoff;
+    if constexpr (CM) {
+      aoff = (ptrdiff_t)s * C::BK;
+#pragma unroll
+      for (int u = 0; u < NSUB; ++u) {
+        const int sh = (ktaps - 1 - run_tap) * dil;
+        const ptrdiff_t bo = run_cb * 32 - (ptrdiff_t)sh * cin;
+#pragma unroll
+        for (int i = 0; i < C::B_LD; ++i)
+          if (u == 0 || b_sub[i] == u) {
+            shift_of[i] = sh;
+            boff_of[i] = bo;
+          }
+        if (++run_tap == ktaps) {
+          run_tap = 0;
+          ++run_cb;
+        }
+      }
+    } else {
+      const int tap = s / ksteps_per_tap;
+      const int c0 = (s - tap * ksteps_per_tap) * C::BK;
+      const int sh = (ktaps - 1 - tap) * dil;
+      aoff = (ptrdiff_t)tap * cin + c0;
+#pragma unroll
+      for (int i = 0; i < C::B_LD; ++i) {
+        shift_of[i] = sh;
+        boff_of[i] = c0 - (ptrdiff_t)sh * cin;
+      }
+    }
     if constexpr (Q8) {
 #pragma unroll
       for (int i = 0; i < C::A_LD; ++i) {
@@ -557,9 +605,11 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
 #pragma unroll
       for (int i = 0; i < C::A_LD; ++i) ra[i] = *reinterpret_cast<const f32x4*>(a_base[i] + aoff);
     }
-    b_shift = shift;
 #pragma unroll
     for (int i = 0; i < C::B_LD; ++i) {
+      const int shift = shift_of[i];
+      const ptrdiff_t boff = boff_of[i];
+      b_shift[i] = shift;
       // branch-free: an fp16 row needs one 16-byte load (its second load
       // repeats the first address), an fp32 row two
       const bool fromx = bn[i] >= shift;
@@ -584,7 +634,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
     }
 #pragma unroll
     for (int i = 0; i < C::B_LD; ++i)
-      *reinterpret_cast<f16x8*>(&Bs[buf][b_lds[i]]) = (x_half && bn[i] >= b_shift)
+      *reinterpret_cast<f16x8*>(&Bs[buf][b_lds[i]]) = (x_half && bn[i] >= b_shift[i])
                                                           ? __builtin_bit_cast(f16x8, rb_lo[i])
                                                           : to_half8(rb_lo[i], rb_hi[i]);
   };
@@ -841,13 +891,21 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_f16_dma_kernel(const ConvPara
                   : reinterpret_cast<const float*>(bx[h]);
   }
 
-  // issue the loads of K-step s into ring stage st
+  // issue the loads of K-step s into ring stage st.  Channel-major K order
+  // (one 32-channel slab of one tap per step), as conv_gemm_f16_kernel; steps
+  // are issued in order, so the (slab, tap) pair advances without divisions.
+  int run_cb = s_begin / ktaps, run_tap = s_begin - (s_begin / ktaps) * ktaps;
   auto issue = [&](int s, int st) __attribute__((always_inline)) {
-    const int tap = s / ksteps_per_tap;
-    const int c0 = (s - tap * ksteps_per_tap) * C::BK;
+    const int tap = run_tap;
+    const int c0 = run_cb * C::BK;
+    if (++run_tap == ktaps) {
+      run_tap = 0;
+      ++run_cb;
+    }
     const int shift = (ktaps - 1 - tap) * dil;
     const uint32_t sbase = (uint32_t)(st * STAGE);
-    if (a_on) lds_dma16(a_src + (ptrdiff_t)tap * cin + c0, a_dst + sbase);
+    // weights packed in the same slab order: step s is slab s
+    if (a_on) lds_dma16(a_src + (ptrdiff_t)s * C::BK, a_dst + sbase);
 #pragma unroll
     for (int h = 0; h < B_DMAS; ++h) {
       const uint32_t dst = lds0 + sbase + A_BYTES + (uint32_t)(wave * B_PER_WAVE + h * 64) * 16;

@@ -397,18 +397,36 @@ __global__ __launch_bounds__(POST_T) void conv_post_rows_kernel(
 // ---------------------------------------------------------------------------
 // weight repacking (create time)
 // ---------------------------------------------------------------------------
-// Conv1d / Linear [M][cin][k] -> [Mpad][k][cin], zero rows past M; T is the
-// packed element type (float, or _Float16 rounded to nearest even).
+// Row m of the packed weights at position idx: tap j and input channel c.
+// Tap-major rows are [k][cin]; slab-ordered rows are [cin / 32][k][32] (the
+// 32-channel slabs of the fp16 GEMMs' channel-major reduction order).
+__device__ __forceinline__ void packed_pos(long long idx, int cin, int k, bool slab, int& m, int& j, int& c) {
+  if (slab) {
+    const int e = (int)(idx & 31);
+    const long long r1 = idx >> 5;
+    j = (int)(r1 % k);
+    const long long r2 = r1 / k;
+    const int nb = cin / 32;
+    c = (int)(r2 % nb) * 32 + e;
+    m = (int)(r2 / nb);
+  } else {
+    c = (int)(idx % cin);
+    const long long r = idx / cin;
+    j = (int)(r % k);
+    m = (int)(r / k);
+  }
+}
+
+// Conv1d / Linear [M][cin][k] -> [Mpad] packed rows, zero rows past M; T is
+// the packed element type (float, or _Float16 rounded to nearest even).
 template <typename T>
 __global__ void repack_conv_kernel(const float* __restrict__ src, T* __restrict__ dst, int M, int Mpad,
-                                   int cin, int k) {
+                                   int cin, int k, int slab) {
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long total = (long long)Mpad * k * cin;
   if (idx >= total) return;
-  const int c = (int)(idx % cin);
-  const long long r = idx / cin;
-  const int j = (int)(r % k);
-  const int m = (int)(r / k);
+  int m, j, c;
+  packed_pos(idx, cin, k, slab != 0, m, j, c);
   dst[idx] = (T)(m < M ? src[((size_t)m * cin + c) * k + j] : 0.f);
 }
 
@@ -416,14 +434,12 @@ __global__ void repack_conv_kernel(const float* __restrict__ src, T* __restrict_
 // tap 0 (input row t-1) takes kernel index p + s, tap 1 (row t) takes p.
 template <typename T>
 __global__ void repack_convT_kernel(const float* __restrict__ src, T* __restrict__ dst, int cin, int cout,
-                                    int s, int Mpad) {
+                                    int s, int Mpad, int slab) {
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long total = (long long)Mpad * 2 * cin;
   if (idx >= total) return;
-  const int c = (int)(idx % cin);
-  const long long r = idx / cin;
-  const int j = (int)(r % 2);
-  const int m = (int)(r / 2);
+  int m, j, c;
+  packed_pos(idx, cin, 2, slab != 0, m, j, c);
   float v = 0.f;
   if (m < s * cout) {
     const int p = m / cout, o = m - p * cout;
@@ -605,26 +621,28 @@ hipError_t launch_conv_post(const float* x, const float* hin, long long sstride,
 }
 
 hipError_t launch_repack_conv(const float* src, void* dst, int M, int Mpad, int cin, int k, bool half_out,
-                              hipStream_t s) {
+                              bool slab, hipStream_t s) {
   const long long n = (long long)Mpad * k * cin;
+  if (slab && cin % 32) return hipErrorInvalidValue;
   if (half_out)
     hipLaunchKernelGGL(repack_conv_kernel<_Float16>, dim3(cdiv(n, 256)), dim3(256), 0, s, src, (_Float16*)dst, M,
-                       Mpad, cin, k);
+                       Mpad, cin, k, slab ? 1 : 0);
   else
     hipLaunchKernelGGL(repack_conv_kernel<float>, dim3(cdiv(n, 256)), dim3(256), 0, s, src, (float*)dst, M, Mpad,
-                       cin, k);
+                       cin, k, slab ? 1 : 0);
   return hipGetLastError();
 }
 
 hipError_t launch_repack_convT(const float* src, void* dst, int cin, int cout, int stride, int Mpad, bool half_out,
-                               hipStream_t s) {
+                               bool slab, hipStream_t s) {
   const long long n = (long long)Mpad * 2 * cin;
+  if (slab && cin % 32) return hipErrorInvalidValue;
   if (half_out)
     hipLaunchKernelGGL(repack_convT_kernel<_Float16>, dim3(cdiv(n, 256)), dim3(256), 0, s, src, (_Float16*)dst, cin,
-                       cout, stride, Mpad);
+                       cout, stride, Mpad, slab ? 1 : 0);
   else
     hipLaunchKernelGGL(repack_convT_kernel<float>, dim3(cdiv(n, 256)), dim3(256), 0, s, src, (float*)dst, cin, cout,
-                       stride, Mpad);
+                       stride, Mpad, slab ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -671,11 +671,13 @@ int repack_gemm(vocoder* v, const float* raw, const GemmW& g, bool transposed, h
   float* pk = v->packed;
   void* dst = g.q8 ? (void*)v->ws : (void*)(pk + g.w);
   const bool half = v->P.f16 && !g.q8;
+  // the fp16 GEMMs reduce in channel-major 32-channel slabs: pack in that order
+  const bool slab = v->P.f16 && g.cin % 32 == 0;
   if (transposed) {
-    HIP_OK(launch_repack_convT(raw + g.raw_w, dst, g.cin, g.cout, g.phases, g.Mpad, half, s));
+    HIP_OK(launch_repack_convT(raw + g.raw_w, dst, g.cin, g.cout, g.phases, g.Mpad, half, slab, s));
     HIP_OK(launch_expand_vec(raw + g.raw_b, pk + g.bias, g.cout, g.phases, g.Mpad, s));
   } else {
-    HIP_OK(launch_repack_conv(raw + g.raw_w, dst, g.M, g.Mpad, g.cin, g.k, half, s));
+    HIP_OK(launch_repack_conv(raw + g.raw_w, dst, g.M, g.Mpad, g.cin, g.k, half, slab, s));
     HIP_OK(launch_expand_vec(raw + g.raw_b, pk + g.bias, g.M, 1, g.Mpad, s));
   }
   if (g.q8) return quantize_packed(v, g, s);
@@ -758,7 +760,8 @@ int vocoder_create(const vocoder_config* cfg, const float* raw_weights, void* pa
       void* dst = L.qkv.q8 ? (void*)(v->ws + off)
                   : P.f16  ? (void*)(reinterpret_cast<_Float16*>(pk + L.qkv.w) + off)
                            : (void*)(pk + L.qkv.w + off);
-      if (launch_repack_conv(raw + raw_w[t], dst, d, d, d, 1, P.f16 && !L.qkv.q8, s) != hipSuccess)
+      // (one tap: both orders coincide)
+      if (launch_repack_conv(raw + raw_w[t], dst, d, d, d, 1, P.f16 && !L.qkv.q8, false, s) != hipSuccess)
         return fail(VOCODER_EHIP);
       if ((rc = copy_d2d(pk + L.qkv.bias + (long long)t * d, raw + raw_b[t], d, s))) return fail(rc);
     }
@@ -795,7 +798,7 @@ int vocoder_create(const vocoder_config* cfg, const float* raw_weights, void* pa
   const int CL = P.stages.back().c;
   if ((rc = copy_d2d(pk + P.post_alpha, raw + P.raw_post_alpha, CL, s))) return fail(rc);
   // conv_post [1][C][k] -> [k][C]
-  if (launch_repack_conv(raw + P.raw_post_w, pk + P.post_w, 1, 1, CL, c.post_kernel, false, s) != hipSuccess)
+  if (launch_repack_conv(raw + P.raw_post_w, pk + P.post_w, 1, 1, CL, c.post_kernel, false, false, s) != hipSuccess)
     return fail(VOCODER_EHIP);
   if ((rc = copy_d2d(pk + P.post_b, raw + P.raw_post_b, 1, s))) return fail(rc);
 
