@@ -43,8 +43,9 @@ def parse():
                     help="matrix weights stored as float, or int8 with one fp16 scale per 32 values")
     ap.add_argument("--graph", action="store_true",
                     help="chunk-schedule workloads: replay each call from a HIP graph")
-    ap.add_argument("--precision", choices=["f32", "f16"], default="f32",
-                    help="matrix-product operands: f32, or fp16 with fp32 sums (the half-precision decoder)")
+    ap.add_argument("--precision", choices=["f32", "f16", "split"], default="f32",
+                    help="matrix-product operands: f32; fp16 with fp32 sums (the half-precision decoder); or "
+                         "split (fp32 values, each product as three fp16 MFMA products of hi/lo halves)")
     # measurement helpers (each replaces the timed run)
     ap.add_argument("--counters", action="store_true",
                     help="decode exactly one batched step from fresh states, for rocprofv3 --pmc runs")
@@ -58,13 +59,18 @@ def parse():
     return ap.parse_args()
 
 
+# the arithmetic the matrix products run in: split = three fp16 products per pair, fp32 sums
+DTYPES = {"f32": "f32", "f16": "f16", "split": "f16x3"}
+
+
 def _kernel_family(name):
     import re
-    # direct-to-LDS fp16 GEMM: TileCfgD<BM, BN, waves_m, waves_n, stages>, split, fp16 rows
-    m = re.search(r"TileCfgD<(\d+), (\d+), \d+, \d+, \d+>, (true|false)", name)
+    # direct-to-LDS fp16 GEMM: TileCfgD<BM, BN, waves_m, waves_n, stages>, split-K, fp16 rows[, split fp16]
+    m = re.search(r"TileCfgD<(\d+), (\d+), \d+, \d+, \d+>, (true|false), (?:true|false)(, true)?", name)
     if m:
         split = "_splitk" if m.group(3) == "true" else ""
-        return f"conv_gemm_f16_dma_{m.group(1)}x{m.group(2)}_bk32{split}"
+        kind = "x3" if m.group(4) else "f16_dma"
+        return f"conv_gemm_{kind}_{m.group(1)}x{m.group(2)}_bk32{split}"
     m = re.search(r"TileCfg(H?)<(\d+), (\d+), \d+, \d+, (\d+)(?:, -?\d+)*\s*>(?:, (true|false))?"
                   r"(?:, (true|false))?", name)
     if m:
@@ -286,7 +292,7 @@ def stream_latency(args, wl, torch, S, Decoder, vb):
                                          for n in sorted(set(sched))},
            "total_ms_median": round(float(np.median(total)), 3),
            "audio_s_per_s": round(audio / (float(np.median(total)) / 1e3), 2),
-           "dtype": args.precision, "data": "synthetic"}
+           "dtype": DTYPES[args.precision], "data": "synthetic"}
     if pre_chunks:
         out["prefix_frames"] = prefix
         out["prefill_ms_median"] = round(float(np.median(pre_times)), 3)
@@ -342,7 +348,7 @@ def main():
 
     wl = S.workload(args.workload)
     model = dict(wl["model"], precision=args.precision, weights=args.weights)
-    peak = FP16_MFMA_PEAK_TFLOPS if args.precision == "f16" else FP32_MFMA_PEAK_TFLOPS
+    peak = FP32_MFMA_PEAK_TFLOPS if args.precision == "f32" else FP16_MFMA_PEAK_TFLOPS
     if isinstance(wl["schedule"], list) or wl["schedule"] == "whole":
         stream_latency(args, wl, torch, S, Decoder, vb)
         return
@@ -402,9 +408,11 @@ def main():
                for k, v in sorted(prof.items(), key=lambda kv: -kv[1]["total_ms"])}
 
     out = {
-        "metric": "audio-seconds/sec (\u00d7real-time) for 64\u00d725-frame chunks; % fp32 MFMA peak"
-                  if args.precision == "f32" else
-                  "audio-seconds/sec (\u00d7real-time) for 64\u00d725-frame chunks, fp16 operands; % fp16 MFMA peak",
+        "metric": {"f32": "audio-seconds/sec (\u00d7real-time) for 64\u00d725-frame chunks; % fp32 MFMA peak",
+                   "f16": "audio-seconds/sec (\u00d7real-time) for 64\u00d725-frame chunks, fp16 operands; "
+                          "% fp16 MFMA peak",
+                   "split": "audio-seconds/sec (\u00d7real-time) for 64\u00d725-frame chunks, fp32 values on "
+                            "split-fp16 MFMA (3 products per pair); % fp16 MFMA peak"}[args.precision],
         "value": round(value, 3),
         "unit": "audio-s/s",
         "n_gpus": 1,
@@ -416,7 +424,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": args.precision,
+        "dtype": DTYPES[args.precision],
         "data": "synthetic (seeded random-init weights, uniform random codes)",
         "config": {"workload": args.workload, "streams": B, "frames_per_chunk": T, "weights": args.weights,
                    "samples_per_frame": dec.hop, "warm_positions": sorted(set(warm))},

@@ -87,7 +87,7 @@ typedef struct vocoder_config {
   int32_t post_kernel;      /* final conv kernel, C -> 1 (7) */
   int32_t max_batch;        /* largest batch a decode call may pass (sizes the workspace) */
   int32_t max_frames;       /* largest n_frames a decode call may pass (sizes the workspace) */
-  int32_t precision;        /* VOCODER_PRECISION_F32 (0) or VOCODER_PRECISION_F16 (1), see below */
+  int32_t precision;        /* VOCODER_PRECISION_F32 (0), _F16 (1) or _SPLIT16 (2), see below */
   int32_t weight_format;    /* VOCODER_WEIGHTS_FLOAT (0) or VOCODER_WEIGHTS_INT8 (1), see below */
 } vocoder_config;
 
@@ -99,10 +99,26 @@ typedef struct vocoder_config {
  * residuals, biases, the final conv, all stored activations and the state)
  * stays fp32.  The edge design page (section 1.5, quality row) allows the
  * decoder fp16 at most; activations must stay within fp16 range (|x| < 65504).
+ * SPLIT16: fp32 values throughout, as F32, with the products of the matrix
+ * products made on the fp16 MFMA: each fp32 operand v is written as hi + lo,
+ * hi = fp16(v) and lo = fp16(v - hi) (both ties to even; the subtraction is
+ * exact), and a product w*x as lo_w*hi_x + hi_w*lo_x + hi_w*hi_x, summed in
+ * fp32 (lo_w*lo_x, below 2^-22 of w*x, is dropped).  This is the split of
+ * Ootomo and Yokota (2022, single-precision accuracy from fp16 matrix units),
+ * with one power-of-two scale per operand in place of their scaled lo term:
+ * weights are split as w * 2^8 and sums scaled back by 2^-8 (exact), which
+ * keeps their lo halves in fp16's normal range; inputs are split unscaled (the
+ * fp16 MFMA keeps subnormal inputs exactly).  Weights are split when packed
+ * (4 bytes per value, as fp32) and activations as they are read; layers whose
+ * input channel count is not a multiple of 32 run the F32 kernels.  Weights
+ * must lie within +-2^8 and activations within the fp16 range (|v| < 65504).
+ * Every product of a layer takes the same three MFMAs in the same order, so
+ * decodes stay bitwise independent of batch and chunking.
  * The precision is part of the state's identity: states are not
- * interchangeable between the two. */
+ * interchangeable between precisions. */
 #define VOCODER_PRECISION_F32 0
 #define VOCODER_PRECISION_F16 1
+#define VOCODER_PRECISION_SPLIT16 2
 
 /* Storage of the matrix-product weights.  FLOAT: fp32 (precision F32) or
  * fp16 (F16).  INT8: the blixt/phonon page's weight format (section Weights):
@@ -119,7 +135,7 @@ typedef struct vocoder_config {
  * per value; launches with few rows read it so, while a launch with many rows
  * first expands its layer into the workspace (4 or 2 bytes per value; the
  * workspace holds the largest int8 layer) and reads that.  Weights must lie
- * within the fp16 range. */
+ * within the fp16 range.  INT8 is not offered with SPLIT16. */
 #define VOCODER_WEIGHTS_FLOAT 0
 #define VOCODER_WEIGHTS_INT8 1
 

@@ -119,10 +119,24 @@ def test_f16_precision_halves_gemm_weight_bytes():
     # everything but the codebooks (67 MB) and the vectors halves
     assert 0.5 * b32 < b16 < 0.6 * b32
     bad = vb.make_config(S.QWEN3, 1, 1)
-    bad.precision = 2
+    bad.precision = 3
     assert vb.vocoder_packed_weights_bytes(bad) == 0
     with pytest.raises(ValueError):
         vb.make_config(dict(S.QWEN3, precision="bf16"), 1, 1)
+
+
+def test_split_precision_keeps_fp32_weight_bytes_and_refuses_int8():
+    f32 = vb.make_config(S.QWEN3, 1, 1)
+    sp = vb.make_config(dict(S.QWEN3, precision="split"), 1, 1)
+    assert sp.precision == 2
+    # two fp16 planes per split weight: the fp32 footprint
+    assert vb.vocoder_packed_weights_bytes(sp) == vb.vocoder_packed_weights_bytes(f32)
+    assert vb.vocoder_workspace_bytes(sp) == vb.vocoder_workspace_bytes(f32)
+    assert vb.vocoder_state_bytes(sp) == vb.vocoder_state_bytes(f32)
+    # the tiny decoder's 16-channel layers keep fp32 weights: same total there too
+    t32, tsp = vb.make_config(S.TINY, 1, 1), vb.make_config(dict(S.TINY, precision="split"), 1, 1)
+    assert vb.vocoder_packed_weights_bytes(tsp) == vb.vocoder_packed_weights_bytes(t32)
+    assert vb.vocoder_packed_weights_bytes(vb.make_config(dict(S.QWEN3, precision="split", weights="int8"), 1, 1)) == 0
 
 
 def test_int8_weights_shrink_the_packed_weights():

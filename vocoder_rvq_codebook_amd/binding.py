@@ -55,7 +55,7 @@ class VocoderConfig(ctypes.Structure):
     ]
 
 
-PRECISIONS = {"f32": 0, "f16": 1}
+PRECISIONS = {"f32": 0, "f16": 1, "split": 2}
 WEIGHT_FORMATS = {"float": 0, "int8": 1}
 
 

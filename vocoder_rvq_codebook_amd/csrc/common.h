@@ -96,6 +96,8 @@ enum { ACT_NONE = 0, ACT_GELU = 1 };
 struct ConvParams {
   const float* w;       // packed [Mpad][k][cin] (fp32, fp16, or int8 when wscale is set)
   const void* wscale;   // int8 weights: fp16 scales [Mpad][k*cin/32], else nullptr
+  const void* w_lo;     // split fp16 weights: the lo plane (w holds the hi plane), else nullptr
+  float acc_scale;      // power of two applied to the reduced sum before the bias (1 unless split)
   int M;                // GEMM columns (= phases * cout)
   int k, cin, dil;
   const float* x;       // [rows][cin], fp32 or (x_half) fp16
@@ -180,6 +182,14 @@ bool gemm_f16_direct(bool int8, int cin, int tile);
 hipError_t launch_conv_gemm(const ConvParams& p, int tile, hipStream_t s, const LnArgs* ln = nullptr);
 // fp16-operand GEMM: p.w points at fp16 weights [Mpad][k][cin]; tiles 128x128, 96x128, 64x64
 hipError_t launch_conv_gemm_f16(const ConvParams& p, int tile, hipStream_t s, const LnArgs* ln = nullptr);
+// split-fp16 GEMM (fp32 accuracy from three fp16 products per pair): p.w and
+// p.w_lo are the hi and lo planes of fp16 weights in 32-channel slab order,
+// p.x fp32 rows; cin a multiple of 32, tiles 128x128 and 96x128
+hipError_t launch_conv_gemm_split(const ConvParams& p, int tile, hipStream_t s, const LnArgs* ln = nullptr);
+
+// The two-term fp16 split of an fp32 value: hi = fp16(v), lo = fp16(v - hi),
+// both rounded to nearest even (v - hi is exact in fp32).
+__device__ __forceinline__ _Float16 split_lo(float v, _Float16 hi) { return (_Float16)(v - (float)hi); }
 
 hipError_t launch_begin(const void* state_in, void* state_out, long long sstride, int batch, int T,
                         uint64_t cfg_hash, const double* inv_freq, int half, float* rope_tab, int* pos,
@@ -205,10 +215,14 @@ hipError_t launch_conv_post(const float* x, const float* hin, long long sstride,
                             float* pre_tanh, hipStream_t s);
 // Weight repacking into GEMM rows [Mpad][k * cin]: tap-major ([k][cin]) or,
 // with slab (cin a multiple of 32; the fp16 GEMMs), [cin / 32][k][32].
+// lo_off > 0 (fp16 output only): split each value times split_scale (a
+// power of two) into hi and lo halves, the lo half lo_off elements after its
+// hi half.
 hipError_t launch_repack_conv(const float* src, void* dst, int M, int Mpad, int cin, int k, bool half_out,
-                              bool slab, hipStream_t s);
+                              bool slab, hipStream_t s, long long lo_off = 0, float split_scale = 1.f);
 hipError_t launch_repack_convT(const float* src, void* dst, int cin, int cout, int stride, int Mpad,
-                               bool half_out, bool slab, hipStream_t s);
+                               bool half_out, bool slab, hipStream_t s, long long lo_off = 0,
+                               float split_scale = 1.f);
 hipError_t launch_expand_vec(const float* src, float* dst, int C, int phases, int Mpad, hipStream_t s);
 // int8 with one fp16 scale per 32 values of each row of a [rows][K] fp32 matrix
 hipError_t launch_quantize_rows(const float* src, long long rows, int K, void* q, void* scale, hipStream_t s);

@@ -81,7 +81,7 @@ __device__ __forceinline__ f32x4 epilogue4(const ConvParams& p, int m, int g, f3
   const int nout_rows = p.nin * p.phases;
   const int ph = m / p.cout;
   const int c = m - ph * p.cout;
-  f32x4 v = acc + ld4(p.bias + m);
+  f32x4 v = acc * p.acc_scale + ld4(p.bias + m);
   if (p.act == ACT_GELU) {
     v.x = gelu1(v.x); v.y = gelu1(v.y); v.z = gelu1(v.z); v.w = gelu1(v.w);
   }
@@ -808,16 +808,24 @@ __device__ __forceinline__ void wait_vm_lgkm() {
 
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-template <class C, bool SPLIT, bool XH>
+// X3: split-fp16 operands (fp32 rows only).  The weights come as hi and lo
+// fp16 planes w1 + w2 (of the weights times a power of two), both staged.
+// Each fp32 input value is split as it is read from LDS into x1 = fp16(x) and
+// x2 = fp16(x - x1).  Every fragment pair takes three MFMAs into the same
+// accumulator, always in this order: w2 x1, w1 x2, w1 x1 (w2 x2, below 2^-22
+// of the product, is dropped); the epilogue scales the sum back.
+template <class C, bool SPLIT, bool XH, bool X3 = false>
 __global__ __launch_bounds__(C::NT) void conv_gemm_f16_dma_kernel(const ConvParams p) {
-  constexpr int STAGE = C::template stage_bytes<XH>();
+  static_assert(!(X3 && XH), "the split takes fp32 rows");
   constexpr int A_BYTES = C::A_SLOTS * 16;
+  constexpr int A_PLANES = X3 ? 2 : 1;
+  constexpr int STAGE = C::template stage_bytes<XH>() + (A_PLANES - 1) * A_BYTES;
   constexpr int B_SLOTS = C::template b_slots<XH>();
   constexpr int B_PER_WAVE = C::template b_per_wave<XH>();
   constexpr int B_DMAS = B_PER_WAVE >= 64 ? B_PER_WAVE / 64 : 1;  // loads per wave per K-step
   constexpr int B_LANES = B_PER_WAVE >= 64 ? 64 : B_PER_WAVE;
   static_assert(B_SLOTS % C::WAVES == 0 && (B_PER_WAVE <= 64 || B_PER_WAVE % 64 == 0), "B chunks per wave");
-  constexpr int OPS = 1 + B_DMAS;  // vector-memory operations per wave per K-step (at least)
+  constexpr int OPS = A_PLANES + B_DMAS;  // vector-memory operations per wave per K-step (at least)
   __shared__ __attribute__((aligned(16))) char lds[C::NS * STAGE];
   const _Float16* W = reinterpret_cast<const _Float16*>(p.w);
 
@@ -869,6 +877,8 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_f16_dma_kernel(const ConvPara
     a_src = W + (size_t)(m0 + r) * ((size_t)p.k * cin) + c * 8;
   }
   const uint32_t a_dst = lds0 + (uint32_t)(wave * C::A_PER_WAVE) * 16;
+  // the lo plane holds the same layout
+  const _Float16* a_lo_src = X3 ? reinterpret_cast<const _Float16*>(p.w_lo) + (a_src - W) : nullptr;
   // B: B_DMAS loads of 64 (or B_LANES) chunks per wave
   const char* bx[B_DMAS];
   const float* bh[B_DMAS];
@@ -906,9 +916,10 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_f16_dma_kernel(const ConvPara
     const uint32_t sbase = (uint32_t)(st * STAGE);
     // weights packed in the same slab order: step s is slab s
     if (a_on) lds_dma16(a_src + (ptrdiff_t)s * C::BK, a_dst + sbase);
+    if (X3 && a_on) lds_dma16(a_lo_src + (ptrdiff_t)s * C::BK, a_dst + sbase + A_BYTES);
 #pragma unroll
     for (int h = 0; h < B_DMAS; ++h) {
-      const uint32_t dst = lds0 + sbase + A_BYTES + (uint32_t)(wave * B_PER_WAVE + h * 64) * 16;
+      const uint32_t dst = lds0 + sbase + A_PLANES * A_BYTES + (uint32_t)(wave * B_PER_WAVE + h * 64) * 16;
       const ptrdiff_t boff = c0 - (ptrdiff_t)shift * cin;
       if (!b_on[h]) continue;
       if (bn[h] >= shift) {
@@ -930,8 +941,8 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_f16_dma_kernel(const ConvPara
   // (fragment rows start at multiples of 16, so the swizzle depends on l%16 only)
   const int a_rd = ((wm * C::WTM + lr) * 4 + (q ^ ((lr >> 1) & 3))) * 16;
   const int b_rd = XH ? A_BYTES + ((wn * C::WTN + lr) * 4 + (q ^ ((lr >> 1) & 3))) * 16 : 0;
-  const int b_rd0 = A_BYTES + ((wn * C::WTN + lr) * 8 + ((2 * q) ^ (lr & 7))) * 16;
-  const int b_rd1 = A_BYTES + ((wn * C::WTN + lr) * 8 + ((2 * q + 1) ^ (lr & 7))) * 16;
+  const int b_rd0 = A_PLANES * A_BYTES + ((wn * C::WTN + lr) * 8 + ((2 * q) ^ (lr & 7))) * 16;
+  const int b_rd1 = A_PLANES * A_BYTES + ((wn * C::WTN + lr) * 8 + ((2 * q + 1) ^ (lr & 7))) * 16;
 
   f32x4 acc[C::FM][C::FN];
 #pragma unroll
@@ -942,27 +953,57 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_f16_dma_kernel(const ConvPara
   auto mma_step = [&](int st, f32x4 (&part)[C::FM][C::FN], auto first) __attribute__((always_inline)) {
     const char* S = lds + st * STAGE;
     f16x8 af[C::FM], bf[C::FN];
+    f16x8 al[X3 ? C::FM : 1];  // weight lo halves (split)
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i) af[i] = *reinterpret_cast<const f16x8*>(S + a_rd + i * 16 * 64);
+    for (int i = 0; i < C::FM; ++i) {
+      af[i] = *reinterpret_cast<const f16x8*>(S + a_rd + i * 16 * 64);
+      if constexpr (X3) al[i] = *reinterpret_cast<const f16x8*>(S + A_BYTES + a_rd + i * 16 * 64);
+    }
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) {
       if constexpr (XH) {
         bf[j] = *reinterpret_cast<const f16x8*>(S + b_rd + j * 16 * 64);
-      } else {
+      } else if constexpr (!X3) {  // (the split reads its B fragments below)
         const f32x4 lo = *reinterpret_cast<const f32x4*>(S + b_rd0 + j * 16 * 128);
         const f32x4 hi = *reinterpret_cast<const f32x4*>(S + b_rd1 + j * 16 * 128);
         bf[j] = to_half8(lo, hi);
       }
     }
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i)
+    if constexpr (X3) {
+      // one B fragment's terms at a time (fewer live registers); the three
+      // (FM) accumulators of a fragment interleave the dependent MFMAs
 #pragma unroll
       for (int j = 0; j < C::FN; ++j) {
-        if (decltype(first)::value)
-          part[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        else
-          part[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], part[i][j], 0, 0, 0);
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(S + b_rd0 + j * 16 * 128);
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(S + b_rd1 + j * 16 * 128);
+        const f16x8 x1 = to_half8(lo, hi);
+        const float r[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        f16x8 x2;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x2[e] = split_lo(r[e], x1[e]);
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        bool fresh = decltype(first)::value;
+        auto mm = [&](const f16x8(&a)[C::FM], f16x8 b) __attribute__((always_inline)) {
+#pragma unroll
+          for (int i = 0; i < C::FM; ++i)
+            part[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b, fresh ? z : part[i][j], 0, 0, 0);
+          fresh = false;
+        };
+        mm(al, x1);
+        mm(af, x2);
+        mm(af, x1);
       }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+          if (decltype(first)::value)
+            part[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          else
+            part[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], part[i][j], 0, 0, 0);
+        }
+    }
   };
 
   // prologue: K-steps s_begin .. s_begin + NS - 2 in flight
@@ -1074,7 +1115,7 @@ hipError_t launch_fold(const ConvParams& p, hipStream_t s, const LnArgs* ln) {
   return hipGetLastError();
 }
 
-template <class C, bool XH>
+template <class C, bool XH, bool X3 = false>
 hipError_t launch_dma_x(const ConvParams& p, hipStream_t s) {
   const int mtiles = (p.M + C::BM - 1) / C::BM;
   const int ntiles = (p.rows + C::BN - 1) / C::BN;
@@ -1082,12 +1123,12 @@ hipError_t launch_dma_x(const ConvParams& p, hipStream_t s) {
   if (tiles <= 0) return hipSuccess;
   if (p.splits <= 1) {
     if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((conv_gemm_f16_dma_kernel<C, false, XH>), dim3((unsigned)tiles), dim3(C::NT), 0, s, p);
+    hipLaunchKernelGGL((conv_gemm_f16_dma_kernel<C, false, XH, X3>), dim3((unsigned)tiles), dim3(C::NT), 0, s, p);
     return hipGetLastError();
   }
   const long long nb = tiles * p.splits;
   if (nb > 0x7fffffffLL || !p.partial) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((conv_gemm_f16_dma_kernel<C, true, XH>), dim3((unsigned)nb), dim3(C::NT), 0, s, p);
+  hipLaunchKernelGGL((conv_gemm_f16_dma_kernel<C, true, XH, X3>), dim3((unsigned)nb), dim3(C::NT), 0, s, p);
   return hipGetLastError();
 }
 
@@ -1235,4 +1276,22 @@ hipError_t launch_conv_gemm(const ConvParams& p, int tile, hipStream_t s, const 
 
 hipError_t launch_conv_gemm_f16(const ConvParams& p, int tile, hipStream_t s, const LnArgs* ln) {
   return launch_gemm(p, tile, true, s, ln);
+}
+
+hipError_t launch_conv_gemm_split(const ConvParams& p, int tile, hipStream_t s, const LnArgs* ln) {
+  if (p.rows <= 0 || p.M <= 0) return hipSuccess;
+  if (!p.w_lo || p.x_half || p.wscale || p.cin % 32 != 0) return hipErrorInvalidValue;
+  // two K-steps in flight: the stage holds both weight planes and fp32 rows
+  // (28-32 KB), so two rings fit each CU's LDS.  96x128 keeps four waves per
+  // SIMD (127 VGPRs); 128x128 needs 149 and runs one block per CU (capped at
+  // 128 it spills), so the caller prefers 96-row tiles where M allows.
+  hipError_t e;
+  if (tile == TILE_128x128)
+    e = launch_dma_x<TileCfgD<128, 128, 2, 4, 2>, false, true>(p, s);
+  else if (tile == TILE_96x128)
+    e = launch_dma_x<TileCfgD<96, 128, 2, 4, 2>, false, true>(p, s);
+  else
+    return hipErrorInvalidValue;
+  if (e != hipSuccess || p.splits <= 1) return e;
+  return launch_fold(p, s, ln);
 }

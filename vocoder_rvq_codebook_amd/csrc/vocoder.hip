@@ -63,8 +63,11 @@ bool config_valid(const vocoder_config* c) {
     if ((long long)c->post_kernel * cl + (128LL + c->post_kernel - 1) * (cl + 1) > 16384) return false;
   }
   if (c->max_batch < 1 || c->max_frames < 1) return false;
-  if (c->precision != VOCODER_PRECISION_F32 && c->precision != VOCODER_PRECISION_F16) return false;
+  if (c->precision != VOCODER_PRECISION_F32 && c->precision != VOCODER_PRECISION_F16 &&
+      c->precision != VOCODER_PRECISION_SPLIT16)
+    return false;
   if (c->weight_format != VOCODER_WEIGHTS_FLOAT && c->weight_format != VOCODER_WEIGHTS_INT8) return false;
+  if (c->precision == VOCODER_PRECISION_SPLIT16 && c->weight_format != VOCODER_WEIGHTS_FLOAT) return false;
   // every GEMM row count must fit in int
   long long hop = 1;
   for (int i = 0; i < c->n_up; ++i) hop *= c->up_strides[i];
@@ -106,7 +109,17 @@ struct GemmW {
   long long raw_w = -1, raw_b = -1;
   int M = 0, Mpad = 0, k = 1, cin = 0, phases = 1, cout = 0;
   bool q8 = false;              // weights stored as int8 with one fp16 scale per 32
+  bool split = false;           // split fp16: hi plane, then lo plane, in 32-channel slab order
+  long long lo_halves() const { return (long long)Mpad * k * cin; }  // hi plane -> lo plane
 };
+
+// Split fp16: the weights are scaled by 2^SPLIT_W_EXP before their split (a
+// power of two: exact) and the sum scaled back before the bias.  Unscaled, the
+// lo half of a weight below 2^-3 is an fp16 subnormal (spacing 2^-24), which
+// for weights of typical size (~0.02) costs about 2^-19 of their value and
+// made the decoder's error 4x the fp32 path's; scaled, lo halves stay normal
+// down to 2^-11, and weights up to 2^8 keep their hi half finite.
+constexpr int SPLIT_W_EXP = 8;
 
 // Tensors of at least this many values whose input channel count is a
 // multiple of 32 are stored as int8 ("blixt/phonon", section Weights).
@@ -139,7 +152,8 @@ struct StageP {
 struct Plan {
   vocoder_config cfg{};
   int d = 0, hd = 0, half = 0, hop = 0;
-  bool f16 = false;  // fp16 GEMM operands (packed weights in fp16)
+  bool f16 = false;    // fp16 GEMM operands (packed weights in fp16)
+  bool split = false;  // split-fp16 GEMMs (fp32 values; weights as fp16 hi + lo planes)
   long long max_gemm_values = 0;  // largest packed GEMM weight (values)
   long long max_q8_values = 0;    // largest int8 GEMM weight (values)
   long long ws_wdeq = 0;          // an int8 layer expanded to the GEMM operand type
@@ -203,6 +217,7 @@ bool make_plan(const vocoder_config* cp, Plan& P) {
   P.half = P.hd / 2;
   P.hop = hop_of(c);
   P.f16 = c.precision == VOCODER_PRECISION_F16;
+  P.split = c.precision == VOCODER_PRECISION_SPLIT16;
   const int d = P.d, De = c.embed_dim, F = c.ffn_dim;
 
   long long raw = 0, pk = 0;
@@ -223,7 +238,9 @@ bool make_plan(const vocoder_config* cp, Plan& P) {
       g.w = K((welems + 3) / 4);          // int8 values
       g.scale = K((welems / 32 + 1) / 2);  // fp16 scales, one per 32 values
     } else {
-      g.w = K(P.f16 ? (welems + 1) / 2 : welems);  // fp16 weights take half the floats
+      // fp16 weights take half the floats; split weights two fp16 planes
+      g.split = P.split && cin % 32 == 0;
+      g.w = K(P.f16 ? (welems + 1) / 2 : welems);
     }
     g.bias = K(g.Mpad);
     P.max_gemm_values = std::max(P.max_gemm_values, welems);
@@ -538,6 +555,8 @@ ConvParams base_params(const Ctx& cx, const GemmW& g, const float* x, int rows, 
   ConvParams p{};
   p.w = cx.v->packed + g.w;
   p.wscale = g.q8 ? (const void*)(cx.v->packed + g.scale) : nullptr;
+  p.w_lo = g.split ? (const void*)(reinterpret_cast<const _Float16*>(p.w) + g.lo_halves()) : nullptr;
+  p.acc_scale = g.split ? std::ldexp(1.f, -SPLIT_W_EXP) : 1.f;
   p.M = g.M;
   p.k = g.k;
   p.cin = g.cin;
@@ -598,7 +617,11 @@ int pick_splits(long long partial_floats, int tile, int M, long long rows, int k
 // A split GEMM normalises in its fold kernel; otherwise the LayerNorm kernel follows.
 int run_gemm(const Ctx& cx, const ConvParams& pin, const LnArgs* ln = nullptr) {
   ConvParams p = pin;
-  const int tile = pick_tile(p.M, p.rows);
+  // split fp16: one kernel at every size (the bits must not depend on the
+  // tile), 96-row tiles where the padded weight rows cover them
+  const bool x3 = p.w_lo != nullptr;
+  const int tile = !x3 ? pick_tile(p.M, p.rows)
+                   : (long long)((p.M + 95) / 96) * 96 <= round_up_i(p.M, 128) ? TILE_96x128 : TILE_128x128;
   const int bm = gemm_tile_bm(tile);
   const int mt = (p.M + bm - 1) / bm;
   const bool f16 = cx.v->P.f16;
@@ -634,12 +657,14 @@ int run_gemm(const Ctx& cx, const ConvParams& pin, const LnArgs* ln = nullptr) {
   if (fuse_ln) bytes += 8.0 * p.rows * ln->d;
   char name[48];
   const bool direct = f16 && gemm_f16_direct(p.wscale != nullptr, p.cin, tile);
-  snprintf(name, sizeof(name), "conv_gemm_%s%s%dx%d_bk%d%s", direct ? "f16_dma_" : f16 ? "f16_" : "", p.wscale ? "q8_" : "", bm,
-           gemm_tile_bn(tile),
-           direct ? 32 : gemm_tile_bk(tile, p.cin, f16), p.splits > 1 ? (fuse_ln ? "_splitk_ln" : "_splitk") : "");
+  snprintf(name, sizeof(name), "conv_gemm_%s%s%dx%d_bk%d%s", x3 ? "x3_" : direct ? "f16_dma_" : f16 ? "f16_" : "",
+           p.wscale ? "q8_" : "", bm, gemm_tile_bn(tile),
+           direct || x3 ? 32 : gemm_tile_bk(tile, p.cin, f16), p.splits > 1 ? (fuse_ln ? "_splitk_ln" : "_splitk") : "");
   {
     Prof pr(cx.v, cx.s, name, flops, bytes);
-    if (f16)
+    if (x3)
+      HIP_OK(launch_conv_gemm_split(p, tile, cx.s, fuse_ln ? ln : nullptr));
+    else if (f16)
       HIP_OK(launch_conv_gemm_f16(p, tile, cx.s, fuse_ln ? ln : nullptr));
     else
       HIP_OK(launch_conv_gemm(p, tile, cx.s, fuse_ln ? ln : nullptr));
@@ -670,14 +695,16 @@ int quantize_packed(vocoder* v, const GemmW& g, hipStream_t s) {
 int repack_gemm(vocoder* v, const float* raw, const GemmW& g, bool transposed, hipStream_t s) {
   float* pk = v->packed;
   void* dst = g.q8 ? (void*)v->ws : (void*)(pk + g.w);
-  const bool half = v->P.f16 && !g.q8;
-  // the fp16 GEMMs reduce in channel-major 32-channel slabs: pack in that order
-  const bool slab = v->P.f16 && g.cin % 32 == 0;
+  const bool half = (v->P.f16 && !g.q8) || g.split;
+  // the fp16 and split GEMMs reduce in channel-major 32-channel slabs: pack in that order
+  const bool slab = (v->P.f16 || g.split) && g.cin % 32 == 0;
+  const long long lo = g.split ? g.lo_halves() : 0;
+  const float sc = std::ldexp(1.f, SPLIT_W_EXP);
   if (transposed) {
-    HIP_OK(launch_repack_convT(raw + g.raw_w, dst, g.cin, g.cout, g.phases, g.Mpad, half, slab, s));
+    HIP_OK(launch_repack_convT(raw + g.raw_w, dst, g.cin, g.cout, g.phases, g.Mpad, half, slab, s, lo, sc));
     HIP_OK(launch_expand_vec(raw + g.raw_b, pk + g.bias, g.cout, g.phases, g.Mpad, s));
   } else {
-    HIP_OK(launch_repack_conv(raw + g.raw_w, dst, g.M, g.Mpad, g.cin, g.k, half, slab, s));
+    HIP_OK(launch_repack_conv(raw + g.raw_w, dst, g.M, g.Mpad, g.cin, g.k, half, slab, s, lo, sc));
     HIP_OK(launch_expand_vec(raw + g.raw_b, pk + g.bias, g.M, 1, g.Mpad, s));
   }
   if (g.q8) return quantize_packed(v, g, s);
@@ -757,11 +784,14 @@ int vocoder_create(const vocoder_config* cfg, const float* raw_weights, void* pa
     const long long raw_b[3] = {L.raw_q_b, L.raw_k_b, L.raw_v_b};
     for (int t = 0; t < 3; ++t) {
       const long long off = (long long)t * d * d;  // elements
+      const bool half = (P.f16 && !L.qkv.q8) || L.qkv.split;
       void* dst = L.qkv.q8 ? (void*)(v->ws + off)
-                  : P.f16  ? (void*)(reinterpret_cast<_Float16*>(pk + L.qkv.w) + off)
+                  : half   ? (void*)(reinterpret_cast<_Float16*>(pk + L.qkv.w) + off)
                            : (void*)(pk + L.qkv.w + off);
-      // (one tap: both orders coincide)
-      if (launch_repack_conv(raw + raw_w[t], dst, d, d, d, 1, P.f16 && !L.qkv.q8, false, s) != hipSuccess)
+      // (one tap: the tap-major and slab orders coincide; a split's lo plane
+      // follows the whole stacked hi plane)
+      if (launch_repack_conv(raw + raw_w[t], dst, d, d, d, 1, half, false, s,
+                             L.qkv.split ? L.qkv.lo_halves() : 0, std::ldexp(1.f, SPLIT_W_EXP)) != hipSuccess)
         return fail(VOCODER_EHIP);
       if ((rc = copy_d2d(pk + L.qkv.bias + (long long)t * d, raw + raw_b[t], d, s))) return fail(rc);
     }
