@@ -111,7 +111,9 @@ typedef struct vocoder_config {
  * fp16 MFMA keeps subnormal inputs exactly).  Weights are split when packed
  * (4 bytes per value, as fp32) and activations as they are read; layers whose
  * input channel count is not a multiple of 32 run the F32 kernels.  Weights
- * must lie within +-2^8 and activations within the fp16 range (|v| < 65504).
+ * must lie within +-2^8 (vocoder_create returns VOCODER_EINVAL for a weight
+ * whose scaled hi half would not be finite) and activations within the fp16
+ * range (|v| < 65504).
  * Every product of a layer takes the same three MFMAs in the same order, so
  * decodes stay bitwise independent of batch and chunking.
  * The precision is part of the state's identity: states are not
@@ -180,8 +182,10 @@ size_t vocoder_state_bytes(const vocoder_config* cfg);
  * 256-byte aligned) by kernels on `stream`; raw_weights may be freed once
  * `stream` has completed that work.  `workspace` (device,
  * vocoder_workspace_bytes, 256-byte aligned) must stay valid and unshared for
- * the handle's life.  On success *out receives the handle.
- * Errors: VOCODER_EINVAL (bad config or pointer), VOCODER_EHIP. */
+ * the handle's life.  On success *out receives the handle.  It returns once
+ * the repacking is done (it synchronizes `stream`).
+ * Errors: VOCODER_EINVAL (bad config or pointer; SPLIT16 with a weight out of
+ * its range), VOCODER_EHIP. */
 int vocoder_create(const vocoder_config* cfg, const float* raw_weights, void* packed_weights,
                    void* workspace, void* stream, vocoder** out);
 

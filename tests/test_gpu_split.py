@@ -123,6 +123,38 @@ def test_split_batch_independence_bitwise():
         assert torch.equal(alone[0], both[b])
 
 
+def test_split_refuses_weights_beyond_its_range():
+    """A weight whose scaled hi half would be infinite (|w| * 2^8 >= 65520)
+    makes vocoder_create fail with VOCODER_EINVAL instead of decoding NaNs."""
+    model = split(S.TINY)
+    W = S.make_weights(model, 3)
+    name = "stages.0.blocks.0.0.conv1.weight"  # 32 input channels: a split layer
+    W[name].flat[5] = 300.0
+    flat = torch.from_numpy(S.flatten_weights(model, W))
+    with pytest.raises(vb.VocoderError) as e:
+        vb.Decoder(model, flat, 1, 4)
+    assert e.value.code == vb.VOCODER_EINVAL
+    W[name].flat[5] = 250.0  # within range: accepted
+    dec = vb.Decoder(model, torch.from_numpy(S.flatten_weights(model, W)), 1, 4)
+    pcm, _ = run_schedule(dec, S.make_codes(model, 1, 4, 5), [4])
+    assert torch.isfinite(pcm).all()
+
+
+def test_fp16_matrix_unit_keeps_subnormal_inputs():
+    """The inputs are split unscaled, so their lo halves are often fp16
+    subnormals: the fp16 matrix product must keep them (and their products)
+    exactly, not flush them."""
+    a = torch.zeros(64, 64, dtype=torch.float16, device="cuda")
+    b = torch.zeros(64, 64, dtype=torch.float16, device="cuda")
+    a[0, 0] = 2.0 ** -20       # subnormal inputs (fp16 normals start at 2^-14)
+    a[1, 1] = 3 * 2.0 ** -24   # the smallest subnormal times 3
+    b[0, 0] = 1.0
+    b[1, 1] = 2.0 ** 8
+    c = torch.matmul(a, b).float()
+    assert c[0, 0].item() == 2.0 ** -20
+    assert c[1, 1].item() == 3 * 2.0 ** -16
+
+
 # ---- the full decoder shape -------------------------------------------------
 
 MODEL = split(S.QWEN3)

@@ -217,12 +217,13 @@ hipError_t launch_conv_post(const float* x, const float* hin, long long sstride,
 // with slab (cin a multiple of 32; the fp16 GEMMs), [cin / 32][k][32].
 // lo_off > 0 (fp16 output only): split each value times split_scale (a
 // power of two) into hi and lo halves, the lo half lo_off elements after its
-// hi half.
+// hi half, and set *range_flag to 1 if a scaled value's hi half is not finite.
 hipError_t launch_repack_conv(const float* src, void* dst, int M, int Mpad, int cin, int k, bool half_out,
-                              bool slab, hipStream_t s, long long lo_off = 0, float split_scale = 1.f);
+                              bool slab, hipStream_t s, long long lo_off = 0, float split_scale = 1.f,
+                              int* range_flag = nullptr);
 hipError_t launch_repack_convT(const float* src, void* dst, int cin, int cout, int stride, int Mpad,
                                bool half_out, bool slab, hipStream_t s, long long lo_off = 0,
-                               float split_scale = 1.f);
+                               float split_scale = 1.f, int* range_flag = nullptr);
 hipError_t launch_expand_vec(const float* src, float* dst, int C, int phases, int Mpad, hipStream_t s);
 // int8 with one fp16 scale per 32 values of each row of a [rows][K] fp32 matrix
 hipError_t launch_quantize_rows(const float* src, long long rows, int K, void* q, void* scale, hipStream_t s);

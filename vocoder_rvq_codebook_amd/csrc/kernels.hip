@@ -421,15 +421,18 @@ __device__ __forceinline__ void packed_pos(long long idx, int cin, int k, bool s
 
 // Store one packed value: T is the packed element type (float, or _Float16
 // rounded to nearest even); fp16 with lo_off > 0 stores the split of v times
-// sc (a power of two: exact), its lo half lo_off elements further on.
+// sc (a power of two: exact), its lo half lo_off elements further on, and
+// flags a value whose hi half is not finite (|v sc| >= 65520, or NaN).
 template <typename T>
-__device__ __forceinline__ void put_packed(T* dst, long long idx, float v, long long lo_off, float sc) {
+__device__ __forceinline__ void put_packed(T* dst, long long idx, float v, long long lo_off, float sc,
+                                           int* range_flag) {
   if constexpr (std::is_same<T, _Float16>::value) {
     if (lo_off > 0) {
       v *= sc;
       const _Float16 h = (_Float16)v;
       dst[idx] = h;
       dst[idx + lo_off] = split_lo(v, h);
+      if (!(fabsf(v) < 65520.f)) *range_flag = 1;  // every writer stores the same value
       return;
     }
   }
@@ -439,20 +442,20 @@ __device__ __forceinline__ void put_packed(T* dst, long long idx, float v, long 
 // Conv1d / Linear [M][cin][k] -> [Mpad] packed rows, zero rows past M.
 template <typename T>
 __global__ void repack_conv_kernel(const float* __restrict__ src, T* __restrict__ dst, int M, int Mpad,
-                                   int cin, int k, int slab, long long lo_off, float sc) {
+                                   int cin, int k, int slab, long long lo_off, float sc, int* range_flag) {
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long total = (long long)Mpad * k * cin;
   if (idx >= total) return;
   int m, j, c;
   packed_pos(idx, cin, k, slab != 0, m, j, c);
-  put_packed(dst, idx, m < M ? src[((size_t)m * cin + c) * k + j] : 0.f, lo_off, sc);
+  put_packed(dst, idx, m < M ? src[((size_t)m * cin + c) * k + j] : 0.f, lo_off, sc, range_flag);
 }
 
 // ConvTranspose1d [cin][cout][2s] -> [Mpad][2][cin] with row m = p*cout + o:
 // tap 0 (input row t-1) takes kernel index p + s, tap 1 (row t) takes p.
 template <typename T>
 __global__ void repack_convT_kernel(const float* __restrict__ src, T* __restrict__ dst, int cin, int cout,
-                                    int s, int Mpad, int slab, long long lo_off, float sc) {
+                                    int s, int Mpad, int slab, long long lo_off, float sc, int* range_flag) {
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long total = (long long)Mpad * 2 * cin;
   if (idx >= total) return;
@@ -464,7 +467,7 @@ __global__ void repack_convT_kernel(const float* __restrict__ src, T* __restrict
     const int kk = j == 0 ? p + s : p;
     v = src[((size_t)c * cout + o) * (2 * s) + kk];
   }
-  put_packed(dst, idx, v, lo_off, sc);
+  put_packed(dst, idx, v, lo_off, sc, range_flag);
 }
 
 // int8 quantization of one group of 32 consecutive values of a row ("blixt/
@@ -639,30 +642,30 @@ hipError_t launch_conv_post(const float* x, const float* hin, long long sstride,
 }
 
 hipError_t launch_repack_conv(const float* src, void* dst, int M, int Mpad, int cin, int k, bool half_out,
-                              bool slab, hipStream_t s, long long lo_off, float split_scale) {
+                              bool slab, hipStream_t s, long long lo_off, float split_scale, int* range_flag) {
   const long long n = (long long)Mpad * k * cin;
   if (slab && cin % 32) return hipErrorInvalidValue;
-  if (lo_off < 0 || (lo_off > 0 && !half_out)) return hipErrorInvalidValue;
+  if (lo_off < 0 || (lo_off > 0 && (!half_out || !range_flag))) return hipErrorInvalidValue;
   if (half_out)
     hipLaunchKernelGGL(repack_conv_kernel<_Float16>, dim3(cdiv(n, 256)), dim3(256), 0, s, src, (_Float16*)dst, M,
-                       Mpad, cin, k, slab ? 1 : 0, lo_off, split_scale);
+                       Mpad, cin, k, slab ? 1 : 0, lo_off, split_scale, range_flag);
   else
     hipLaunchKernelGGL(repack_conv_kernel<float>, dim3(cdiv(n, 256)), dim3(256), 0, s, src, (float*)dst, M, Mpad,
-                       cin, k, slab ? 1 : 0, 0LL, 1.f);
+                       cin, k, slab ? 1 : 0, 0LL, 1.f, nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_repack_convT(const float* src, void* dst, int cin, int cout, int stride, int Mpad, bool half_out,
-                               bool slab, hipStream_t s, long long lo_off, float split_scale) {
+                               bool slab, hipStream_t s, long long lo_off, float split_scale, int* range_flag) {
   const long long n = (long long)Mpad * 2 * cin;
   if (slab && cin % 32) return hipErrorInvalidValue;
-  if (lo_off < 0 || (lo_off > 0 && !half_out)) return hipErrorInvalidValue;
+  if (lo_off < 0 || (lo_off > 0 && (!half_out || !range_flag))) return hipErrorInvalidValue;
   if (half_out)
     hipLaunchKernelGGL(repack_convT_kernel<_Float16>, dim3(cdiv(n, 256)), dim3(256), 0, s, src, (_Float16*)dst, cin,
-                       cout, stride, Mpad, slab ? 1 : 0, lo_off, split_scale);
+                       cout, stride, Mpad, slab ? 1 : 0, lo_off, split_scale, range_flag);
   else
     hipLaunchKernelGGL(repack_convT_kernel<float>, dim3(cdiv(n, 256)), dim3(256), 0, s, src, (float*)dst, cin, cout,
-                       stride, Mpad, slab ? 1 : 0, 0LL, 1.f);
+                       stride, Mpad, slab ? 1 : 0, 0LL, 1.f, nullptr);
   return hipGetLastError();
 }
 

@@ -700,11 +700,12 @@ int repack_gemm(vocoder* v, const float* raw, const GemmW& g, bool transposed, h
   const bool slab = (v->P.f16 || g.split) && g.cin % 32 == 0;
   const long long lo = g.split ? g.lo_halves() : 0;
   const float sc = std::ldexp(1.f, SPLIT_W_EXP);
+  int* flag = reinterpret_cast<int*>(v->ws + v->P.ws_status);  // cleared before the repacks
   if (transposed) {
-    HIP_OK(launch_repack_convT(raw + g.raw_w, dst, g.cin, g.cout, g.phases, g.Mpad, half, slab, s, lo, sc));
+    HIP_OK(launch_repack_convT(raw + g.raw_w, dst, g.cin, g.cout, g.phases, g.Mpad, half, slab, s, lo, sc, flag));
     HIP_OK(launch_expand_vec(raw + g.raw_b, pk + g.bias, g.cout, g.phases, g.Mpad, s));
   } else {
-    HIP_OK(launch_repack_conv(raw + g.raw_w, dst, g.M, g.Mpad, g.cin, g.k, half, slab, s, lo, sc));
+    HIP_OK(launch_repack_conv(raw + g.raw_w, dst, g.M, g.Mpad, g.cin, g.k, half, slab, s, lo, sc, flag));
     HIP_OK(launch_expand_vec(raw + g.raw_b, pk + g.bias, g.M, 1, g.Mpad, s));
   }
   if (g.q8) return quantize_packed(v, g, s);
@@ -770,6 +771,8 @@ int vocoder_create(const vocoder_config* cfg, const float* raw_weights, void* pa
   auto fail = [&](int r) { delete v; return r; };
 
   if (launch_fill(pk, (size_t)P.packed_floats * 4, s) != hipSuccess) return fail(VOCODER_EHIP);
+  // the split repacks flag weights out of range in the status word
+  if (launch_fill(v->ws + P.ws_status, 256, s) != hipSuccess) return fail(VOCODER_EHIP);
   if ((rc = copy_d2d(pk + P.codebooks, raw + P.raw_codebooks,
                      (long long)c.n_codebooks * c.codebook_size * c.embed_dim, s))) return fail(rc);
   if ((rc = repack_gemm(v, raw, P.pre, false, s))) return fail(rc);
@@ -791,7 +794,8 @@ int vocoder_create(const vocoder_config* cfg, const float* raw_weights, void* pa
       // (one tap: the tap-major and slab orders coincide; a split's lo plane
       // follows the whole stacked hi plane)
       if (launch_repack_conv(raw + raw_w[t], dst, d, d, d, 1, half, false, s,
-                             L.qkv.split ? L.qkv.lo_halves() : 0, std::ldexp(1.f, SPLIT_W_EXP)) != hipSuccess)
+                             L.qkv.split ? L.qkv.lo_halves() : 0, std::ldexp(1.f, SPLIT_W_EXP),
+                             reinterpret_cast<int*>(v->ws + P.ws_status)) != hipSuccess)
         return fail(VOCODER_EHIP);
       if ((rc = copy_d2d(pk + L.qkv.bias + (long long)t * d, raw + raw_b[t], d, s))) return fail(rc);
     }
@@ -843,6 +847,12 @@ int vocoder_create(const vocoder_config* cfg, const float* raw_weights, void* pa
     return fail(VOCODER_EHIP);
   // the host vectors above are released on return: wait for the copies
   if (hipStreamSynchronize(s) != hipSuccess) return fail(VOCODER_EHIP);
+  if (P.split) {
+    int range = 0;
+    if (hipMemcpy(&range, v->ws + P.ws_status, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess)
+      return fail(VOCODER_EHIP);
+    if (range) return fail(VOCODER_EINVAL);  // a weight beyond the split's range
+  }
   if (launch_fill(v->ws + P.ws_status, 256, s) != hipSuccess) return fail(VOCODER_EHIP);
   if (P.conc_frames > 0) {
     bool ok = hipEventCreateWithFlags(&v->ev_fork, hipEventDisableTiming) == hipSuccess;
