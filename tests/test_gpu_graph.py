@@ -49,8 +49,9 @@ SCHEDULES = {
 @pytest.mark.parametrize("name", list(SCHEDULES))
 @pytest.mark.parametrize("model", [S.MINI, dict(S.MINI, name="mini_f16", precision="f16"),
                                    dict(S.MINI, name="mini_q8", weights="int8"),
-                                   dict(S.MINI, name="mini_q8_f16", weights="int8", precision="f16")],
-                         ids=["f32", "f16", "int8", "int8_f16"])
+                                   dict(S.MINI, name="mini_q8_f16", weights="int8", precision="f16"),
+                                   dict(S.MINI, name="mini_split", precision="split")],
+                         ids=["f32", "f16", "int8", "int8_f16", "split"])
 def test_graph_replays_equal_eager(name, model):
     schedule = SCHEDULES[name]
     T = sum(schedule)

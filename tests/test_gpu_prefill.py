@@ -43,8 +43,9 @@ def _warm(dec, codes, warm):
     return st
 
 
-@pytest.mark.parametrize("model", [S.TINY, S.MINI, dict(S.MINI, name="mini_f16", precision="f16")],
-                         ids=["tiny", "mini", "mini_f16"])
+@pytest.mark.parametrize("model", [S.TINY, S.MINI, dict(S.MINI, name="mini_f16", precision="f16"),
+                                   dict(S.MINI, name="mini_split", precision="split")],
+                         ids=["tiny", "mini", "mini_f16", "mini_split"])
 def test_prefill_state_equals_decode_state(model):
     tail = tail_frames(model)
     B, warm, utt = 2, [0, 9], 6
@@ -66,8 +67,9 @@ def test_prefill_state_equals_decode_state(model):
         pcm, _ = run_schedule(dec, nxt, [utt], state=st_pre)
         for b, nw in enumerate(warm):
             sched = [n for n in (nw, T, utt) if n]
+            # fp16 operands: the oracle rounds the same operands; fp32 and split: the plain decoder
             ref = oracle_stream(model, W, codes[b, :nw + T + utt], sched,
-                                operands=model.get("precision") and "f16")
+                                operands="f16" if model.get("precision") == "f16" else None)
             rel = 2e-3 if model.get("precision") == "f16" else 1e-4
             check_close(pcm[b].cpu().numpy(), ref[(nw + T) * model["hop"]:], f"{model['name']} T={T} stream {b}",
                         rel=rel)
