@@ -157,6 +157,37 @@ __device__ __forceinline__ f32x4 fold_groups(const ConvParams& p, int m, int g, 
   return acc;
 }
 
+// Epilogue of a whole tile through LDS.  The accumulators go to an fp32
+// [BN][BM] tile in LDS (16-byte chunks of 4 GEMM columns, chunk c of row r
+// stored at c ^ (r & 7): conflict-free both for the fragment writes, 8 rows
+// of one chunk, and for the row reads, 8 chunks of one row); then thread t
+// runs the epilogue of chunks t, t + NT, ... in row-major order, so a wave's
+// loads and stores cover whole rows instead of 16-row columns.  Each element
+// gets the same epilogue on the same value: the same bits as epilogue4 called
+// from the fragments.  The caller has synchronised the block: T may overwrite
+// LDS that every wave has finished reading.
+template <class C>
+__device__ __forceinline__ void epilogue_tile(const ConvParams& p, float* T, const f32x4 (&acc)[C::FM][C::FN],
+                                              int m0, int g0, int wm, int wn, int lane, int tid) {
+  constexpr int CH = C::BM / 4;
+  static_assert(CH % 8 == 0, "row chunks: a multiple of 8");
+  const int lr = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+      const int r = wn * C::WTN + j * 16 + lr;
+      const int c = (wm * C::WTM + i * 16) / 4 + q;
+      st4(T + (r * CH + (c ^ (r & 7))) * 4, acc[i][j]);
+    }
+  __syncthreads();
+  for (int idx = tid; idx < C::BN * CH; idx += C::NT) {
+    const int r = idx / CH, c = idx - r * CH;
+    const int g = g0 + r, m = m0 + 4 * c;
+    if (g < p.rows && m < p.M) epilogue4(p, m, g, ld4(T + (r * CH + (c ^ (r & 7))) * 4));
+  }
+}
+
 // SPLIT = false: one block computes a whole output tile and runs the epilogue.
 // SPLIT = true: blocks are (tile, split) pairs; a split owns a contiguous,
 // non-empty range of accumulation groups and stores each group's partial sum,
@@ -164,9 +195,13 @@ __device__ __forceinline__ f32x4 fold_groups(const ConvParams& p, int m, int g, 
 // groups in order and runs the same epilogue.  Every group's partial is the
 // same MFMA chain in both modes, so both modes give the same bits.
 template <class C, bool SPLIT, bool Q8>
-__global__ __launch_bounds__(C::NT) void conv_gemm_kernel(const ConvParams p) {
-  __shared__ __attribute__((aligned(16))) float As[2][C::BM * C::LDK];
-  __shared__ __attribute__((aligned(16))) float Bs[2][C::BN * C::LDK];
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(4))) void conv_gemm_kernel(const ConvParams p) {
+  // double-buffered A and B tiles; after the K loop the same LDS holds the
+  // epilogue's [BN][BM] tile
+  constexpr int AB_FLOATS = 2 * (C::BM + C::BN) * C::LDK;
+  constexpr int T_FLOATS = SPLIT ? 0 : C::BM * C::BN;
+  __shared__ __attribute__((aligned(16))) float smem[AB_FLOATS > T_FLOATS ? AB_FLOATS : T_FLOATS];
+  constexpr int A_OFF = 0, B_OFF = 2 * C::BM * C::LDK;  // buffer b of A at A_OFF + b * BM * LDK
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -278,13 +313,13 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_kernel(const ConvParams p) {
   auto lstore = [&](int buf) {
     if constexpr (Q8) {
 #pragma unroll
-      for (int i = 0; i < C::A_LD; ++i) st4(&As[buf][a_lds[i]], dequant4(rq[i], rs[i]));
+      for (int i = 0; i < C::A_LD; ++i) st4(&smem[A_OFF + buf * (C::BM * C::LDK) + a_lds[i]], dequant4(rq[i], rs[i]));
     } else {
 #pragma unroll
-      for (int i = 0; i < C::A_LD; ++i) st4(&As[buf][a_lds[i]], ra[i]);
+      for (int i = 0; i < C::A_LD; ++i) st4(&smem[A_OFF + buf * (C::BM * C::LDK) + a_lds[i]], ra[i]);
     }
 #pragma unroll
-    for (int i = 0; i < C::B_LD; ++i) st4(&Bs[buf][b_lds[i]], rb[i]);
+    for (int i = 0; i < C::B_LD; ++i) st4(&smem[B_OFF + buf * (C::BN * C::LDK) + b_lds[i]], rb[i]);
   };
 
   // MFMA 16x16x4 f32: lane l supplies A[l%16][k] and B[k][l%16] with
@@ -306,8 +341,8 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_kernel(const ConvParams p) {
 
   auto mma_step = [&](int cur, f32x4 (&part)[C::FM][C::FN], auto first) {
     if constexpr (C::IGLP >= 0) __builtin_amdgcn_iglp_opt(C::IGLP);
-    const float* Ab = As[cur];
-    const float* Bb = Bs[cur];
+    const float* Ab = &smem[A_OFF + cur * (C::BM * C::LDK)];
+    const float* Bb = &smem[B_OFF + cur * (C::BN * C::LDK)];
 #pragma unroll
     for (int kk = 0; kk < C::BK; kk += 16) {
       f32x4 af[C::FM], bf[C::FN];
@@ -368,17 +403,8 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_kernel(const ConvParams p) {
   }
   if (SPLIT) return;
 
-  // epilogue: lane holds rows m..m+3 (4*(l/16) + r) of column g (l%16)
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i) {
-    const int m = m0 + wm * C::WTM + i * 16 + (lane >> 4) * 4;
-    if (m >= p.M) continue;
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j) {
-      const int g = g0 + wn * C::WTN + j * 16 + lr;
-      if (g < p.rows) epilogue4(p, m, g, acc[i][j]);
-    }
-  }
+  // (the K loop ended on a block barrier: every wave is done with As and Bs)
+  epilogue_tile<C>(p, smem, acc, m0, g0, wm, wn, lane, tid);
 }
 
 // Fold the split-K group partials of one output element (4 consecutive M)
@@ -1057,16 +1083,11 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_f16_dma_kernel(const ConvPara
   }
   if (SPLIT) return;
 
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i) {
-    const int m = m0 + wm * C::WTM + i * 16 + (lane >> 4) * 4;
-    if (m >= p.M) continue;
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j) {
-      const int g = g0 + wn * C::WTN + j * 16 + lr;
-      if (g < p.rows) epilogue4(p, m, g, acc[i][j]);
-    }
-  }
+  // every wave has left the K loop (no LDS reads or loads outstanding): the
+  // ring becomes the epilogue's tile
+  static_assert(C::BN * C::BM * 4 <= C::NS * STAGE, "epilogue tile fits the ring");
+  __syncthreads();
+  epilogue_tile<C>(p, reinterpret_cast<float*>(lds), acc, m0, g0, wm, wn, lane, tid);
 }
 
 template <class C, bool HALF, bool Q8>
