@@ -1,6 +1,7 @@
-// Implicit-GEMM causal convolution on fp32 MFMA (gfx950).
+// Implicit-GEMM causal convolution on the MFMA units (gfx950): fp32 MFMA, or
+// fp16 MFMA with fp16 operands or with fp32 operands split into fp16 pairs.
 //
-// One kernel serves every dense contraction of the decoder:
+// One kernel family serves every dense contraction of the decoder:
 //  - causal dilated Conv1d (pre-conv, conv_pre, the AMP convs of every BigVGAN
 //    stage): A = weights [Cout][tap][Cin], B = input rows shifted by
 //    (k-1-tap)*dil, rows before the chunk read from the stream's history slot;
@@ -15,8 +16,9 @@
 // output's last rows into the stream's next state.
 //
 // Each output element's reduction order depends only on (tap, channel): the K
-// loop is fixed and never split, so results are bitwise independent of batch,
-// chunking and tile shape.
+// loop order is fixed, and split-K splits only between accumulation groups and
+// folds them in order, so results are bitwise independent of batch, chunking,
+// tile shape and split.
 
 #include <type_traits>
 
@@ -779,9 +781,10 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
 // accumulation groups and split-K are those of conv_gemm_f16_kernel, so both
 // give the same bits.
 //
-// LDS stage = A tile (BM rows x 32 halves, 4 chunks of 16 bytes per row), then
-// the B tile: 32 halves per row when the input rows are fp16 (XH), else 32
-// floats (8 chunks per row), rounded to fp16 as the MFMA operands are read.
+// LDS stage = A tile (BM rows x 32 halves, 4 chunks of 16 bytes per row; with
+// the split, the hi plane's tile then the lo plane's), then the B tile: 32
+// halves per row when the input rows are fp16 (XH), else 32 floats (8 chunks
+// per row), rounded to fp16 (or split) as the MFMA operands are read.
 // Chunks are XOR-swizzled within a row so that the 8 lanes an LDS read
 // serves together (8 rows, one 16-byte chunk each, 128 bytes of banks) hit
 // distinct banks: chunk c of row r sits at position c ^ ((r >> 1) & 3)
