@@ -184,7 +184,7 @@ hipError_t launch_conv_gemm(const ConvParams& p, int tile, hipStream_t s, const 
 hipError_t launch_conv_gemm_f16(const ConvParams& p, int tile, hipStream_t s, const LnArgs* ln = nullptr);
 // split-fp16 GEMM (fp32 accuracy from three fp16 products per pair): p.w and
 // p.w_lo are the hi and lo planes of fp16 weights in 32-channel slab order,
-// p.x fp32 rows; cin a multiple of 32, tiles 128x128 and 96x128
+// p.x fp32 rows; cin a multiple of 32, tiles 128x128, 96x128, 64x64, 64x32, 64x16
 hipError_t launch_conv_gemm_split(const ConvParams& p, int tile, hipStream_t s, const LnArgs* ln = nullptr);
 
 // The two-term fp16 split of an fp32 value: hi = fp16(v), lo = fp16(v - hi),

@@ -1309,13 +1309,18 @@ hipError_t launch_conv_gemm_split(const ConvParams& p, int tile, hipStream_t s, 
   // (28-32 KB), so two rings fit each CU's LDS.  96x128 keeps four waves per
   // SIMD (127 VGPRs); 128x128 needs 149 and runs one block per CU (capped at
   // 128 it spills), so the caller prefers 96-row tiles where M allows.
+  // Few-row launches (small chunks) take 4-wave tiles with 3 K-steps in
+  // flight: 64x64, or 64 x 32 / 64 x 16 with the waves stacked along M.  Every
+  // tile runs the same K-steps and MFMA order: the same bits.
   hipError_t e;
-  if (tile == TILE_128x128)
-    e = launch_dma_x<TileCfgD<128, 128, 2, 4, 2>, false, true>(p, s);
-  else if (tile == TILE_96x128)
-    e = launch_dma_x<TileCfgD<96, 128, 2, 4, 2>, false, true>(p, s);
-  else
-    return hipErrorInvalidValue;
+  switch (tile) {
+    case TILE_128x128: e = launch_dma_x<TileCfgD<128, 128, 2, 4, 2>, false, true>(p, s); break;
+    case TILE_96x128: e = launch_dma_x<TileCfgD<96, 128, 2, 4, 2>, false, true>(p, s); break;
+    case TILE_64x64: e = launch_dma_x<TileCfgD<64, 64, 2, 2, 3>, false, true>(p, s); break;
+    case TILE_S64x32: e = launch_dma_x<TileCfgD<64, 32, 4, 1, 3>, false, true>(p, s); break;
+    case TILE_S64x16: e = launch_dma_x<TileCfgD<64, 16, 4, 1, 3>, false, true>(p, s); break;
+    default: return hipErrorInvalidValue;
+  }
   if (e != hipSuccess || p.splits <= 1) return e;
   return launch_fold(p, s, ln);
 }

@@ -617,11 +617,13 @@ int pick_splits(long long partial_floats, int tile, int M, long long rows, int k
 // A split GEMM normalises in its fold kernel; otherwise the LayerNorm kernel follows.
 int run_gemm(const Ctx& cx, const ConvParams& pin, const LnArgs* ln = nullptr) {
   ConvParams p = pin;
-  // split fp16: one kernel at every size (the bits must not depend on the
-  // tile), 96-row tiles where the padded weight rows cover them
+  // split fp16: one kernel family at every size (the same bits on every
+  // tile); the few-row tiles as in fp32, else 96-row tiles where the padded
+  // weight rows cover them (128x128 needs more registers)
   const bool x3 = p.w_lo != nullptr;
-  const int tile = !x3 ? pick_tile(p.M, p.rows)
-                   : (long long)((p.M + 95) / 96) * 96 <= round_up_i(p.M, 128) ? TILE_96x128 : TILE_128x128;
+  int tile = pick_tile(p.M, p.rows);
+  if (x3 && (tile == TILE_96x128 || tile == TILE_128x128))
+    tile = (long long)((p.M + 95) / 96) * 96 <= round_up_i(p.M, 128) ? TILE_96x128 : TILE_128x128;
   const int bm = gemm_tile_bm(tile);
   const int mt = (p.M + bm - 1) / bm;
   const bool f16 = cx.v->P.f16;
