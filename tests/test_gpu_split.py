@@ -218,3 +218,30 @@ def test_split_batched_64_streams_chunk_25():
         _compare(pcm_np[b], pre_np[b], g, f"split stream {b}", k)
     alone, _ = run_schedule(dec, chunk[37:38], [25], state=saved[37:38].clone())
     assert torch.equal(alone[0], pcm[37])
+
+
+def test_split_longform_16_streams_1500_frames_zipf():
+    """16 streams x 1500 frames in 25-frame chunks with Zipf-distributed codes:
+    stream 0 against the stored oracle values."""
+    print("\n[split full] 16 streams x 1500 frames in 25-frame chunks (Zipf codes)", flush=True)
+    w = S.workload("qwen3_b16_t1500_zipf")
+    dec, _ = decoder(MODEL, 1, 16, 25)
+    codes = S.workload_codes("qwen3_b16_t1500_zipf")
+    B = codes.shape[0]
+    st_a, st_b = dec.new_state(B), dec.new_state(B)
+    pre = torch.empty(B * 25 * HOP, device="cuda")
+    dec.set_tap("pre_tanh", pre)
+    pcm0, pre0 = [], []
+    for i, n in enumerate(w["schedule"]):
+        c = torch.from_numpy(np.ascontiguousarray(codes[:, i * 25:(i + 1) * 25])).cuda()
+        pcm = dec.decode(c, st_a, st_b)
+        st_a, st_b = st_b, st_a
+        pcm0.append(pcm[0].cpu())
+        pre0.append(pre.view(B, -1)[0].cpu())
+        assert torch.isfinite(pcm).all()
+        if i % 20 == 0:
+            print(f"  chunk {i}", flush=True)
+    dec.set_tap("pre_tanh", None)
+    assert dec.status() == 0
+    _compare(torch.cat(pcm0).numpy().astype(np.float64), torch.cat(pre0).numpy().astype(np.float64),
+             golden("qwen3_longform"), "split stream 0 of 16, 1500 frames")
