@@ -60,3 +60,30 @@ def test_direct_load_kernels_use_no_scratch(gemm_asm):
     assert len(sizes) >= 8
     for sym, n in sizes:
         assert int(n) == 0, f"{sym} spills to scratch ({n} bytes per lane)"
+
+
+def _vgprs(asm):
+    """{kernel symbol: VGPRs + AGPRs} from the code object metadata."""
+    out = {}
+    for block in asm.split("\n  - ")[1:]:
+        name = re.search(r"\.name:\s+(\S+)", block)
+        v = re.search(r"\.vgpr_count:\s+(\d+)", block)
+        a = re.search(r"\.agpr_count:\s+(\d+)", block)
+        if name and v:
+            out[name.group(1)] = int(v.group(1)) + (int(a.group(1)) if a else 0)
+    return out
+
+
+def test_hot_gemm_tiles_keep_four_waves_per_simd(gemm_asm):
+    """The big GEMM tiles run 8 waves per block and two blocks per CU, which
+    needs at most 128 registers per lane.  Measured exceptions: the split
+    (fp32-accurate) 128x128 tile needs about 150 and runs one block per CU."""
+    regs = _vgprs(gemm_asm)
+    hot = {k: v for k, v in regs.items()
+           if re.search(r"TileCfgD?ILi(96|128)ELi128E", k) and ("conv_gemm_kernel" in k or "dma_kernel" in k)}
+    assert len(hot) >= 16, sorted(regs)
+    for k, v in hot.items():
+        split_128 = "dma_kernel" in k and "ILi128ELi128E" in k and k.endswith("ELb0ELb0ELb1EEEv10ConvParams")
+        if split_128:
+            continue
+        assert v <= 128, f"{k}: {v} registers per lane (more than 128 halves the blocks per CU)"
