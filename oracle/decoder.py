@@ -301,10 +301,14 @@ def quantize_rows_int8(rows):
     consecutive values of a row (K a multiple of 32), as the phonon page's
     weight converter does: round the values to fp16; the scale is the largest
     magnitude of the 32 rounded values over 127, rounded to fp16; each value is
-    the nearest integer to value / scale, ties to even.  The scale and the
-    quotients are computed in fp32, the arithmetic the page's shaders use
-    (where floating point decides an integer, both implementations decide in
-    the same precision); a group of zeros gets scale 0 and values 0.
+    the nearest integer to value / scale, ties to even.  The page does this in
+    its offline weight converter and does not state the precision of the two
+    divisions; here both are correctly rounded fp32 divisions, as in the
+    device quantizer (where floating point decides an integer, both
+    implementations decide in the same precision).  On the Qwen3-shaped
+    decoder's weights float64 divisions give the same int8 values and scales
+    for every one of the 242,862,080 quantized values.  A group of zeros gets
+    scale 0 and values 0.
 
     Returns (q int8 [n][K], scale float16 [n][K/32])."""
     v = np.asarray(rows, dtype=np.float32).astype(np.float16).astype(np.float32)

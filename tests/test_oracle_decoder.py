@@ -76,7 +76,6 @@ def test_state_save_restore_resumes_exactly(mini):
     saved = st.copy()
     a, _ = O.decode_schedule(cfg, W, codes[13:], [27], state=st)
     b, _ = O.decode_schedule(cfg, W, codes[13:], [20, 7], state=saved)
-    np.testing.assert_array_equal(a[: 20 * cfg["hop"]], b[: 20 * cfg["hop"]]) if False else None
     np.testing.assert_allclose(a, whole[13 * cfg["hop"]:], rtol=0, atol=1e-12)
     np.testing.assert_allclose(b, whole[13 * cfg["hop"]:], rtol=0, atol=1e-12)
 
@@ -89,15 +88,27 @@ def test_reset_forgets_previous_utterance(mini):
     np.testing.assert_array_equal(got, whole)
 
 
-def test_window_limits_attention_reach(mini):
-    """Past the window, a frame influences later frames only through the conv
-    context and the stacked layers; changing frame 0 changes frame 1's audio."""
-    cfg, W, codes, whole = mini
+@pytest.mark.parametrize("window", [5, 6, 7])
+def test_window_limits_attention_reach(window):
+    """A frame at position t attends keys [t - W, t] (the W previous frames and
+    itself).  With the pre-conv's kernel k spreading a frame over k frames and
+    each of the L layers spreading it W further, a change of frame t0's codes
+    reaches the transformer output (the final LayerNorm) on exactly frames
+    t0 .. t0 + (k - 1) + L * W and on no other frame, bit for bit.  A window
+    one frame shorter or longer moves the last changed frame by L."""
+    cfg = dict(S.MINI, window=window)
+    W = O.cast_weights(S.make_weights(cfg, 3), np.float64)
+    codes = S.make_codes(cfg, 1, 40, 11)[0]
+    t0 = 5
     c2 = codes.copy()
-    c2[0] = (c2[0] + 5) % cfg["codebook_size"]
-    out = O.decode_whole(cfg, W, c2)
-    hop = cfg["hop"]
-    assert np.abs(out[hop: 2 * hop] - whole[hop: 2 * hop]).max() > 0
+    c2[t0] = (c2[t0] + 5) % cfg["codebook_size"]
+    a, b = {}, {}
+    O.decode_whole(cfg, W, codes, taps=a)
+    O.decode_whole(cfg, W, c2, taps=b)
+    changed = np.flatnonzero(np.any(a["final_ln"] != b["final_ln"], axis=1))
+    last = t0 + (cfg["pre_kernel"] - 1) + cfg["n_layers"] * window
+    assert last < codes.shape[0] - 1
+    np.testing.assert_array_equal(changed, np.arange(t0, last + 1))
 
 
 def test_float32_mode_close_to_float64(tiny):
