@@ -167,7 +167,9 @@ size_t vocoder_raw_weights_count(const vocoder_config* cfg);
 /* Bytes of the packed-weight buffer (library-internal layout). 0 if invalid. */
 size_t vocoder_packed_weights_bytes(const vocoder_config* cfg);
 
-/* Bytes of the workspace for max_batch streams x max_frames frames. 0 if invalid. */
+/* Bytes of the workspace for max_batch streams x max_frames frames (including
+ * room for one batch of states, the input copy of an in-place decode).  0 if
+ * invalid. */
 size_t vocoder_workspace_bytes(const vocoder_config* cfg);
 
 /* Bytes of one stream's state (a header plus every carried row).  A batch of
@@ -197,15 +199,22 @@ int vocoder_reset(vocoder* v, void* state, int batch, void* stream);
 
 /* Decode one chunk of n_frames frames for each of `batch` streams.
  *   codes     int32 [batch][n_frames][n_codebooks] (device)
- *   state_in  [batch][state_bytes] (device), read only
- *   state_out [batch][state_bytes] (device), written; must not overlap state_in
- *             (ping-pong two buffers across calls)
+ *   state_in  [batch][state_bytes] (device), read
+ *   state_out [batch][state_bytes] (device), written.  Either state_in itself
+ *             (an in-place decode: the state the decoder adapter keeps across
+ *             calls, "Edge TTS design", sections 2.3 and 4) or a buffer that
+ *             does not overlap it (ping-pong two buffers across calls).  In
+ *             place, the call first copies the batch's states into the
+ *             workspace and reads the old state from that copy (one extra pass
+ *             over batch * state_bytes); the results are bit for bit those of a
+ *             ping-pong call.
  *   pcm       float [batch][n_frames * hop] (device), written
  * Streams may sit at different positions.  A chunk of T frames emits exactly
  * T * hop samples per stream; any chunking of a stream gives the same samples
  * as decoding it whole (each output element is reduced in the same order).
  * Errors: VOCODER_EINVAL (null pointer, batch not in [1, max_batch], n_frames
- * not in [1, max_frames], overlapping states), VOCODER_EHIP.  Device-detected
+ * not in [1, max_frames], states that overlap without being the same buffer,
+ * a state pointer not 256-byte aligned), VOCODER_EHIP.  Device-detected
  * errors (VOCODER_ECODE: that chunk's PCM is unspecified and no out-of-range
  * codeword is read; VOCODER_ESTATE: the stream is decoded from a fresh state)
  * are reported by vocoder_get_status. */

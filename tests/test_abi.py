@@ -153,3 +153,40 @@ def test_int8_weights_shrink_the_packed_weights():
     assert vb.vocoder_packed_weights_bytes(bad) == 0
     with pytest.raises(ValueError):
         vb.make_config(dict(S.QWEN3, weights="int4"), 1, 1)
+
+
+def test_binding_rejects_bad_decode_buffers_before_any_call():
+    """The binding checks the tensors a decode call hands to the library as
+    raw pointers: type, layout, device, sizes and state overlap.  CPU tensors
+    stand in for device ones (device="cpu")."""
+    import torch
+
+    kw = dict(n_codebooks=16, state_bytes=512, hop=48, device="cpu", max_batch=4, max_frames=8)
+    codes = torch.zeros((2, 3, 16), dtype=torch.int32)
+    st = torch.zeros((4, 512), dtype=torch.uint8)
+    if st.data_ptr() % 256:
+        pytest.skip("host allocation not 256-byte aligned")
+    st_a, st_b = st[:2], st[2:]
+    pcm = torch.zeros((2, 3 * 48))
+    vb.check_decode_args(codes, st_a, st_b, pcm, **kw)       # ping-pong
+    vb.check_decode_args(codes, st_a, st_a, pcm, **kw)       # in place
+    vb.check_decode_args(codes, st_a, st_b, None, **kw)      # prefill: no pcm
+    bad = [
+        (codes.long(), st_a, st_b, pcm),                     # codes dtype
+        (codes[:, :, :8], st_a, st_b, pcm),                  # codebook count
+        (codes.transpose(0, 1), st_a, st_b, pcm),            # not contiguous
+        (torch.zeros((5, 3, 16), dtype=torch.int32), st, st, torch.zeros(5 * 3 * 48)),  # batch > max_batch
+        (torch.zeros((1, 9, 16), dtype=torch.int32), st_a, st_b, pcm),  # frames > max_frames
+        (codes, st_a.float(), st_b, pcm),                    # state dtype
+        (codes, torch.zeros((2, 256), dtype=torch.uint8), st_b, pcm),  # state width
+        (codes, st[:1], st_b, pcm),                          # too few states
+        (codes, st[:2], st[1:3], pcm),                       # partial overlap
+        (codes, st_a, st_b, pcm[:, :100]),                   # pcm too small (and not contiguous)
+        (codes, st_a, st_b, torch.zeros(2 * 3 * 47)),        # pcm too small
+        (codes, st_a, st_b, pcm.double()),                   # pcm dtype
+        (codes, st_a, st_b, pcm.to("meta")),                 # pcm on another device
+    ]
+    for i, args in enumerate(bad):
+        with pytest.raises(ValueError):
+            vb.check_decode_args(*args, **kw)
+            print("accepted case", i)

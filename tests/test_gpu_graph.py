@@ -117,7 +117,8 @@ def test_graph_reports_device_errors_and_rejects_bad_arguments():
     # host-side argument errors: nothing recorded
     rc = vb.vocoder_decode_chunk_graph(dec.handle, codes, 2, 9, st_a, st_b, pcm)
     assert rc == vb.VOCODER_EINVAL
-    rc = vb.vocoder_decode_chunk_graph(dec.handle, codes, 2, 4, st_a, st_a, pcm)
+    st3 = dec.new_state(3)
+    rc = vb.vocoder_decode_chunk_graph(dec.handle, codes, 2, 4, st3[0:2], st3[1:3], pcm)  # partial overlap
     assert rc == vb.VOCODER_EINVAL
     assert vb.vocoder_graph_cache_size(dec.handle) == n0
     # a code out of range, detected on the device, through a replayed graph

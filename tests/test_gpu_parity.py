@@ -209,7 +209,45 @@ def test_host_side_argument_errors():
     assert vb.vocoder_decode_chunk(h, codes, 3, 4, st, st2, pcm) == vb.VOCODER_EINVAL  # batch > max
     assert vb.vocoder_decode_chunk(h, codes, 1, 9, st, st2, pcm) == vb.VOCODER_EINVAL  # frames > max
     assert vb.vocoder_decode_chunk(h, codes, 1, 0, st, st2, pcm) == vb.VOCODER_EINVAL
-    assert vb.vocoder_decode_chunk(h, codes, 2, 4, st, st, pcm) == vb.VOCODER_EINVAL  # aliasing states
     assert vb.vocoder_decode_chunk(h, codes, 2, 4, st[0:2], st[1:3], pcm) == vb.VOCODER_EINVAL  # overlap
+    assert vb.vocoder_prefill(h, codes, 2, 4, st[0:2], st[1:3]) == vb.VOCODER_EINVAL
     assert vb.vocoder_decode_chunk(h, codes, 2, 4, st[0:2], st2[0:2], pcm) == vb.VOCODER_OK
+    assert vb.vocoder_decode_chunk(h, codes, 2, 4, st, st, pcm) == vb.VOCODER_OK  # in place
     assert dec.status() == vb.VOCODER_OK
+
+
+@pytest.mark.parametrize("model_name,precision,graph", [
+    ("mini", "f32", False),
+    ("mini", "f32", True),
+    ("mini", "f16", False),
+    ("mini", "split", False),
+    ("tiny", "f32", False),
+])
+def test_in_place_decode_equals_ping_pong(model_name, precision, graph):
+    """state_out == state_in: chunks of 1, 25, 25 frames on two streams give
+    the same PCM and the same final state, bit for bit, as decoding into a
+    second buffer (the decoder adapter keeping one state across calls)."""
+    base = S.MINI if model_name == "mini" else S.TINY
+    model = dict(base, precision=precision, name=f"{base['name']}_{precision}")
+    dec, _ = decoder(model, 9, 2, 25)
+    sched = [1, 25, 25]
+    codes = S.make_codes(model, 2, sum(sched), 53)
+    ref, st_ref = run_schedule(dec, codes, sched)
+    st = dec.new_state(2)
+    out, t0 = [], 0
+    for n in sched:
+        c = torch.from_numpy(np.ascontiguousarray(codes[:, t0:t0 + n])).cuda()
+        pcm = torch.empty((2, n * dec.hop), device="cuda")
+        out.append(dec.decode(c, st, st, pcm, graph=graph).clone())
+        t0 += n
+    torch.cuda.synchronize()
+    assert dec.status() == vb.VOCODER_OK
+    assert torch.equal(torch.cat(out, dim=1), ref)
+    assert torch.equal(st, st_ref)
+    # a prefill in place leaves the same state as one into a second buffer
+    st2, st3 = dec.new_state(2), dec.new_state(2)
+    c = torch.from_numpy(np.ascontiguousarray(codes[:, :25])).cuda()
+    dec.prefill(c, st2, st2)
+    dec.prefill(c, st3.clone(), st3)
+    torch.cuda.synchronize()
+    assert torch.equal(st2, st3)

@@ -103,7 +103,8 @@ def test_prefill_rejects_bad_arguments_and_reports_bad_codes():
     codes = torch.zeros((2, 8, model["n_codebooks"]), dtype=torch.int32, device="cuda")
     assert vb.vocoder_prefill(dec.handle, codes, 2, 9, st_a, st_b) == vb.VOCODER_EINVAL
     assert vb.vocoder_prefill(dec.handle, codes, 3, 8, st_a, st_b) == vb.VOCODER_EINVAL
-    assert vb.vocoder_prefill(dec.handle, codes, 2, 8, st_a, st_a) == vb.VOCODER_EINVAL
+    st3 = dec.new_state(3)
+    assert vb.vocoder_prefill(dec.handle, codes, 2, 8, st3[0:2], st3[1:3]) == vb.VOCODER_EINVAL  # overlap
     assert vb.vocoder_prefill(dec.handle, None, 2, 8, st_a, st_b) == vb.VOCODER_EINVAL
     codes[0, 7, 0] = -1
     dec.prefill(codes, st_a, st_b)

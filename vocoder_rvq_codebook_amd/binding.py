@@ -279,14 +279,72 @@ def vocoder_strerror(code: int) -> str:
 # --- convenience owner of the device buffers ---------------------------------
 
 
+def _device(device) -> torch.device:
+    """torch.device with an explicit index for a GPU ("cuda" -> the current one)."""
+    device = torch.device(device)
+    if device.type == "cuda" and device.index is None:
+        device = torch.device("cuda", torch.cuda.current_device())
+    return device
+
+
+def check_decode_args(codes, state_in, state_out, pcm, *, n_codebooks: int, state_bytes: int, hop: int,
+                      device, max_batch: int, max_frames: int) -> None:
+    """Raise ValueError unless the tensors of one decode (or prefill, pcm=None)
+    call are what the library will read and write: the library sees only raw
+    pointers, so a buffer of the wrong type, layout, device or size would be
+    read or written out of bounds on the device.
+
+    codes: int32, contiguous, [batch][frames][n_codebooks], 1 <= batch <=
+    max_batch, 1 <= frames <= max_frames.  States: uint8, contiguous,
+    [>= batch][state_bytes], 256-byte aligned, and either the same buffer
+    (in place) or disjoint.  pcm: float32, contiguous, >= batch * frames * hop
+    elements."""
+    device = _device(device)
+
+    def on_device(t, what):
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{what} must be a torch tensor")
+        if t.device != device:
+            raise ValueError(f"{what} is on {t.device}, the decoder on {device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{what} must be contiguous")
+
+    on_device(codes, "codes")
+    if codes.dtype != torch.int32 or codes.dim() != 3:
+        raise ValueError("codes must be an int32 [batch][frames][codebooks] tensor")
+    B, T, Q = codes.shape
+    if Q != n_codebooks:
+        raise ValueError(f"expected {n_codebooks} codebooks, got {Q}")
+    if not (1 <= B <= max_batch) or not (1 <= T <= max_frames):
+        raise ValueError(f"batch {B} / frames {T} outside [1, {max_batch}] / [1, {max_frames}]")
+    for t, what in ((state_in, "state_in"), (state_out, "state_out")):
+        on_device(t, what)
+        if t.dtype != torch.uint8 or t.dim() != 2 or t.shape[1] != state_bytes:
+            raise ValueError(f"{what} must be a uint8 [batch][{state_bytes}] tensor, got {t.dtype} "
+                             f"{tuple(t.shape)}")
+        if t.shape[0] < B:
+            raise ValueError(f"{what} holds {t.shape[0]} states, the call decodes {B}")
+        if t.data_ptr() % 256:
+            raise ValueError(f"{what} must be 256-byte aligned")
+    a, b, n = state_in.data_ptr(), state_out.data_ptr(), B * state_bytes
+    if a != b and a < b + n and b < a + n:
+        raise ValueError("state_out overlaps state_in without being the same buffer")
+    if pcm is not None:
+        on_device(pcm, "pcm")
+        if pcm.dtype != torch.float32:
+            raise ValueError("pcm must be float32")
+        if pcm.numel() < B * T * hop:
+            raise ValueError(f"pcm holds {pcm.numel()} samples, the call writes {B * T * hop}")
+
+
 class Decoder:
     """A decoder instance with its packed weights and workspace held as torch
-    device tensors.  States are [batch][state_bytes] uint8 tensors; decode
-    ping-pongs between two of them."""
+    device tensors.  States are [batch][state_bytes] uint8 tensors; a decode
+    reads one and writes another, or updates one in place."""
 
     def __init__(self, model: dict, raw_weights, max_batch: int, max_frames: int, device="cuda"):
         self.model = model
-        self.device = torch.device(device)
+        self.device = _device(device)
         self.cfg = make_config(model, max_batch, max_frames)
         n = vocoder_raw_weights_count(self.cfg)
         if n == 0:
@@ -317,24 +375,31 @@ class Decoder:
         return st
 
     def reset(self, state: torch.Tensor) -> None:
+        if (not isinstance(state, torch.Tensor) or state.device != self.device or not state.is_contiguous()
+                or state.dtype != torch.uint8 or state.dim() != 2 or state.shape[1] != self.state_bytes
+                or state.shape[0] < 1 or state.data_ptr() % 256):
+            raise ValueError(f"state must be a contiguous, 256-byte aligned uint8 [batch][{self.state_bytes}] "
+                             f"tensor on {self.device}")
         rc = vocoder_reset(self.handle, state, state.shape[0])
         if rc != VOCODER_OK:
             raise VocoderError(rc, "vocoder_reset")
 
+    def _check(self, codes, state_in, state_out, pcm):
+        check_decode_args(codes, state_in, state_out, pcm, n_codebooks=self.cfg.n_codebooks,
+                          state_bytes=self.state_bytes, hop=self.hop, device=self.device,
+                          max_batch=self.cfg.max_batch, max_frames=self.cfg.max_frames)
+
     def decode(self, codes: torch.Tensor, state_in: torch.Tensor, state_out: torch.Tensor,
                pcm: torch.Tensor | None = None, graph: bool = False) -> torch.Tensor:
-        """One chunk for codes.shape[0] streams.  graph=True replays a HIP graph
+        """One chunk for codes.shape[0] streams.  state_out may be state_in
+        itself (in place) or a disjoint buffer.  graph=True replays a HIP graph
         kept per (buffers, batch, frames): reuse the same code, state and PCM
         tensors across calls, and keep them alive while the decoder lives."""
-        B, T, Q = codes.shape
-        if codes.dtype != torch.int32 or not codes.is_contiguous():
-            raise ValueError("codes must be a contiguous int32 [batch][frames][codebooks] tensor")
-        if Q != self.cfg.n_codebooks:
-            raise ValueError(f"expected {self.cfg.n_codebooks} codebooks, got {Q}")
-        if state_in.shape[0] < B or state_out.shape[0] < B:
-            raise ValueError("state batch too small")
         if pcm is None:
-            pcm = torch.empty((B, T * self.hop), dtype=torch.float32, device=self.device)
+            self._check(codes, state_in, state_out, None)
+            pcm = torch.empty((codes.shape[0], codes.shape[1] * self.hop), dtype=torch.float32, device=self.device)
+        self._check(codes, state_in, state_out, pcm)
+        B, T = codes.shape[0], codes.shape[1]
         fn = vocoder_decode_chunk_graph if graph else vocoder_decode_chunk
         rc = fn(self.handle, codes, B, T, state_in, state_out, pcm)
         if rc != VOCODER_OK:
@@ -343,13 +408,8 @@ class Decoder:
 
     def prefill(self, codes: torch.Tensor, state_in: torch.Tensor, state_out: torch.Tensor) -> None:
         """Decode a reference prefix into state_out without producing audio."""
-        B, T, Q = codes.shape
-        if codes.dtype != torch.int32 or not codes.is_contiguous():
-            raise ValueError("codes must be a contiguous int32 [batch][frames][codebooks] tensor")
-        if Q != self.cfg.n_codebooks:
-            raise ValueError(f"expected {self.cfg.n_codebooks} codebooks, got {Q}")
-        if state_in.shape[0] < B or state_out.shape[0] < B:
-            raise ValueError("state batch too small")
+        self._check(codes, state_in, state_out, None)
+        B, T = codes.shape[0], codes.shape[1]
         rc = vocoder_prefill(self.handle, codes, B, T, state_in, state_out)
         if rc != VOCODER_OK:
             raise VocoderError(rc, "vocoder_prefill")

@@ -232,5 +232,7 @@ hipError_t launch_quantize_rows(const float* src, long long rows, int K, void* q
 hipError_t launch_dequant_rows(const void* q, const void* scale, long long values, void* dst, bool half,
                                hipStream_t s);
 hipError_t launch_fill(void* dst, size_t bytes, hipStream_t s);
+// dst[i] = src[i] for i < n floats (n a multiple of 4, both 16-byte aligned)
+hipError_t launch_copy(float* dst, const float* src, long long n, hipStream_t s);
 hipError_t launch_reset_headers(void* state, long long sstride, int batch, uint64_t cfg_hash,
                                 hipStream_t s);

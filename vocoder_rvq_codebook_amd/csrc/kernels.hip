@@ -546,6 +546,11 @@ __global__ void fill_kernel(uint32_t* __restrict__ dst, size_t words) {
     dst[i] = 0u;
 }
 
+__global__ void copy_kernel(f32x4* __restrict__ dst, const f32x4* __restrict__ src, long long n4) {
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (long long)gridDim.x * blockDim.x)
+    dst[i] = src[i];
+}
+
 __global__ void reset_headers_kernel(float* __restrict__ state, long long sstride, int batch, uint64_t hash) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= batch) return;
@@ -698,6 +703,16 @@ hipError_t launch_fill(void* dst, size_t bytes, hipStream_t s) {
   if (words == 0) return hipSuccess;
   const unsigned blocks = (unsigned)std::min<size_t>((words + 255) / 256, 65536);
   hipLaunchKernelGGL(fill_kernel, dim3(blocks), dim3(256), 0, s, (uint32_t*)dst, words);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy(float* dst, const float* src, long long n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (n % 4 || ((uintptr_t)dst & 15) || ((uintptr_t)src & 15)) return hipErrorInvalidValue;
+  const long long n4 = n / 4;
+  const unsigned blocks = (unsigned)std::min<long long>((n4 + 255) / 256, 8192);
+  hipLaunchKernelGGL(copy_kernel, dim3(blocks), dim3(256), 0, s, reinterpret_cast<f32x4*>(dst),
+                     reinterpret_cast<const f32x4*>(src), n4);
   return hipGetLastError();
 }
 

@@ -183,6 +183,7 @@ struct Plan {
   std::vector<long long> ws_up;
   long long ws_X0 = 0, ws_T = 0, ws_Xr = 0, ws_An = 0, ws_S[2] = {0, 0};
   long long ws_partial = 0, partial_floats = 0;  // split-K group partials
+  long long ws_snap = 0;                        // a batch of states: the input of an in-place decode
   // concurrent AMP blocks (chunks of at most conc_frames frames over the
   // batch): per extra block its own inner buffers and split-K partials, and
   // the middle block's output
@@ -395,6 +396,7 @@ bool make_plan(const vocoder_config* cp, Plan& P) {
     for (int j = 0; j < 2; ++j) P.ws_partial_aux[j] = Wk(P.partial_aux_floats);
   }
   if (P.max_q8_values > 0) P.ws_wdeq = Wk(P.f16 ? (P.max_q8_values + 1) / 2 : P.max_q8_values);
+  P.ws_snap = Wk((long long)c.max_batch * P.state_floats);
   P.ws_floats = ws;
   // int8 weights are quantized at create time from a float repack staged in
   // the workspace
@@ -881,6 +883,8 @@ int vocoder_reset(vocoder* v, void* state, int batch, void* stream) {
 namespace {
 
 // Host-side argument checks shared by the eager and the graph entry points.
+// state_out may be state_in itself (an in-place decode) but must not overlap
+// it otherwise.
 bool decode_args_ok(const vocoder* v, const int32_t* codes, int batch, int n_frames, const void* state_in,
                     const void* state_out, const float* pcm, bool need_pcm = true) {
   if (!v || !codes || !state_in || !state_out || (need_pcm && !pcm)) return false;
@@ -888,6 +892,7 @@ bool decode_args_ok(const vocoder* v, const int32_t* codes, int batch, int n_fra
   const vocoder_config& c = P.cfg;
   if (batch < 1 || batch > c.max_batch || n_frames < 1 || n_frames > c.max_frames) return false;
   if (((uintptr_t)state_in & 255) || ((uintptr_t)state_out & 255)) return false;
+  if (state_in == state_out) return true;
   const char* a = (const char*)state_in;
   const char* b = (const char*)state_out;
   const size_t n = (size_t)batch * P.state_floats * 4;
@@ -903,6 +908,18 @@ int decode_launches(vocoder* v, const int32_t* codes, int batch, int n_frames, c
                     void* state_out, float* pcm, void* stream, bool prefill = false) {
   const Plan& P = v->P;
   const vocoder_config& c = P.cfg;
+  // In place (state_out == state_in): every kernel below reads the old state
+  // while others write the new one, so the batch's states are first copied to
+  // the workspace and read from there.
+  if (state_in == state_out) {
+    float* snap = v->ws + P.ws_snap;
+    const long long n = (long long)batch * P.state_floats;
+    {
+      Prof pr(v, (hipStream_t)stream, "state_snapshot", 0, 8.0 * n);
+      HIP_OK(launch_copy(snap, (const float*)state_in, n, (hipStream_t)stream));
+    }
+    state_in = snap;
+  }
   Ctx cx;
   cx.quiet = prefill;
   cx.partial = v->ws + P.ws_partial;
@@ -925,7 +942,7 @@ int decode_launches(vocoder* v, const int32_t* codes, int batch, int n_frames, c
 
   {
   Prof pr(v, cx.s, "begin", 0, 4.0 * B * (double)T * P.half * 2);
-  HIP_OK(launch_begin(state_in, state_out, cx.sstride, B, T, v->hash,
+  HIP_OK(launch_begin(cx.sin_, cx.sout, cx.sstride, B, T, v->hash,
                       reinterpret_cast<const double*>(pk + P.inv_freq), P.half, rope, pos, status, cx.s));
   }
   {
