@@ -52,6 +52,7 @@ extern "C" {
 #define VOCODER_ESTATE (-2)       /* state header does not match this decoder (device-detected) */
 #define VOCODER_EHIP (-3)         /* a HIP call or kernel launch failed */
 #define VOCODER_ECODE (-4)        /* a code outside [0, codebook_size) (device-detected) */
+#define VOCODER_ESCRATCH (-5)     /* vocoder_decode_chunk_noalloc: the chunk's buffers exceed its static scratch */
 
 #define VOCODER_MAX_UP 4
 #define VOCODER_MAX_STAGES 8
@@ -240,6 +241,33 @@ int vocoder_decode_chunk(vocoder* v, const int32_t* codes, int batch, int n_fram
  * vocoder_decode_chunk, and VOCODER_EHIP if recording or instantiation fails. */
 int vocoder_decode_chunk_graph(vocoder* v, const int32_t* codes, int batch, int n_frames,
                                const void* state_in, void* state_out, float* pcm, void* stream);
+
+/* Bytes of the static device scratch of vocoder_decode_chunk_noalloc (per GPU). */
+#define VOCODER_NOALLOC_SCRATCH_BYTES (256u << 20)
+
+/* vocoder_decode_chunk for callers that cannot allocate device memory at all
+ * at call time (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments, checks, results (bit for bit) and
+ * error reporting as vocoder_decode_chunk, but the call's buffers
+ * (activations, split-K partials, the copy of the states of an in-place call)
+ * come from a fixed static device array of VOCODER_NOALLOC_SCRATCH_BYTES that
+ * the library holds on each GPU it runs on until the process ends, laid out
+ * for this call's batch x n_frames, instead of from the handle's workspace
+ * (which still holds the status word).  The call allocates nothing and
+ * creates no events (profiling does not apply to it); taps do.  At the
+ * Qwen3-TTS-12Hz shape a chunk needs about 25 MB per frame of batch x
+ * n_frames plus one state (6 MB) per stream, so one stream's chunks of up to
+ * 10 frames fit; a larger chunk returns VOCODER_ESCRATCH before any launch.
+ * Launches whose split-K partials would not fit the compact layout are not
+ * split and int8 weights are dequantized per tile: the same bits either way.
+ * Every call on one GPU, from any handle, shares that GPU's scratch, and
+ * nothing in it needs to start at zero: calls that overlap in time on one
+ * GPU (on different streams, or from different threads) race and must be
+ * ordered by the caller.  Errors: as vocoder_decode_chunk, VOCODER_ESCRATCH,
+ * and VOCODER_EHIP if the scratch's device address could not be obtained
+ * when the handle was created. */
+int vocoder_decode_chunk_noalloc(vocoder* v, const int32_t* codes, int batch, int n_frames,
+                                 const void* state_in, void* state_out, float* pcm, void* stream);
 
 /* The int8 weight quantizer vocoder_create applies (see VOCODER_WEIGHTS_INT8),
  * on a caller's matrix: src fp32 [rows][K] (device, K a multiple of 32) ->

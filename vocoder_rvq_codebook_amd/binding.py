@@ -20,6 +20,7 @@ VOCODER_EINVAL = -1
 VOCODER_ESTATE = -2
 VOCODER_EHIP = -3
 VOCODER_ECODE = -4
+VOCODER_ESCRATCH = -5
 
 MAX_UP, MAX_STAGES, MAX_RES, MAX_DIL = 4, 8, 4, 4
 
@@ -99,6 +100,8 @@ def lib():
         L.vocoder_decode_chunk.restype = i32
         L.vocoder_decode_chunk_graph.argtypes = [vp, vp, i32, i32, vp, vp, vp, vp]
         L.vocoder_decode_chunk_graph.restype = i32
+        L.vocoder_decode_chunk_noalloc.argtypes = [vp, vp, i32, i32, vp, vp, vp, vp]
+        L.vocoder_decode_chunk_noalloc.restype = i32
         L.vocoder_graph_cache_size.argtypes = [vp]
         L.vocoder_graph_cache_size.restype = i32
         L.vocoder_quantize_int8.argtypes = [vp, ctypes.c_longlong, i32, vp, vp, vp]
@@ -214,6 +217,11 @@ def vocoder_decode_chunk(handle, codes, batch, n_frames, state_in, state_out, pc
 def vocoder_decode_chunk_graph(handle, codes, batch, n_frames, state_in, state_out, pcm, stream=None) -> int:
     return lib().vocoder_decode_chunk_graph(handle, _ptr(codes), int(batch), int(n_frames), _ptr(state_in),
                                             _ptr(state_out), _ptr(pcm), _stream(stream))
+
+
+def vocoder_decode_chunk_noalloc(handle, codes, batch, n_frames, state_in, state_out, pcm, stream=None) -> int:
+    return lib().vocoder_decode_chunk_noalloc(handle, _ptr(codes), int(batch), int(n_frames), _ptr(state_in),
+                                              _ptr(state_out), _ptr(pcm), _stream(stream))
 
 
 def vocoder_graph_cache_size(handle) -> int:
@@ -390,17 +398,21 @@ class Decoder:
                           max_batch=self.cfg.max_batch, max_frames=self.cfg.max_frames)
 
     def decode(self, codes: torch.Tensor, state_in: torch.Tensor, state_out: torch.Tensor,
-               pcm: torch.Tensor | None = None, graph: bool = False) -> torch.Tensor:
+               pcm: torch.Tensor | None = None, graph: bool = False, noalloc: bool = False) -> torch.Tensor:
         """One chunk for codes.shape[0] streams.  state_out may be state_in
         itself (in place) or a disjoint buffer.  graph=True replays a HIP graph
         kept per (buffers, batch, frames): reuse the same code, state and PCM
-        tensors across calls, and keep them alive while the decoder lives."""
+        tensors across calls, and keep them alive while the decoder lives.
+        noalloc=True runs vocoder_decode_chunk_noalloc (the call's buffers in
+        the library's static scratch; pass pcm to allocate nothing here either)."""
         if pcm is None:
             self._check(codes, state_in, state_out, None)
             pcm = torch.empty((codes.shape[0], codes.shape[1] * self.hop), dtype=torch.float32, device=self.device)
         self._check(codes, state_in, state_out, pcm)
         B, T = codes.shape[0], codes.shape[1]
-        fn = vocoder_decode_chunk_graph if graph else vocoder_decode_chunk
+        if graph and noalloc:
+            raise ValueError("graph and noalloc are separate entry points")
+        fn = vocoder_decode_chunk_graph if graph else vocoder_decode_chunk_noalloc if noalloc else vocoder_decode_chunk
         rc = fn(self.handle, codes, B, T, state_in, state_out, pcm)
         if rc != VOCODER_OK:
             raise VocoderError(rc, fn.__name__)

@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -149,6 +150,25 @@ struct StageP {
   long long rate = 1;                      // rows per frame at the output
 };
 
+// Float offsets of the per-call buffers inside a workspace laid out for
+// `rows` = batch x frames frame-rows (layout_workspace).
+struct WsLayout {
+  long long status = 0, pos = 0, rope = 0, emb = 0, h = 0, u = 0, qkv = 0, att = 0, ffn = 0;
+  long long up[VOCODER_MAX_UP] = {0, 0, 0, 0};
+  long long X0 = 0, T = 0, Xr = 0, An = 0, S[2] = {0, 0};
+  long long A[VOCODER_MAX_RES] = {0, 0, 0, 0};
+  long long partial = 0, partial_floats = 0;  // split-K group partials
+  // concurrent AMP blocks (chunks of at most conc_frames frames over the
+  // batch): per extra block its own inner buffers and split-K partials, and
+  // the middle block's output
+  long long conc_frames = 0;
+  long long conc_T[2] = {0, 0}, conc_Xr[2] = {0, 0}, conc_An[2] = {0, 0}, conc_B1 = 0;
+  long long partial_aux[2] = {0, 0}, partial_aux_floats = 0;
+  long long wdeq = 0;   // an int8 layer expanded to the GEMM operand type (0: none, dequantize per tile)
+  long long snap = 0;   // a batch of states: the input of an in-place decode
+  long long floats = 0;
+};
+
 struct Plan {
   vocoder_config cfg{};
   int d = 0, hd = 0, half = 0, hop = 0;
@@ -177,21 +197,13 @@ struct Plan {
   // state
   std::vector<Slot> slots;
   long long state_floats = 0;
-  // workspace (float offsets)
-  long long ws_status = 0, ws_pos = 0, ws_rope = 0, ws_emb = 0, ws_h = 0, ws_u = 0, ws_qkv = 0, ws_att = 0,
-            ws_ffn = 0;
-  std::vector<long long> ws_up;
-  long long ws_X0 = 0, ws_T = 0, ws_Xr = 0, ws_An = 0, ws_S[2] = {0, 0};
-  long long ws_partial = 0, partial_floats = 0;  // split-K group partials
-  long long ws_snap = 0;                        // a batch of states: the input of an in-place decode
-  // concurrent AMP blocks (chunks of at most conc_frames frames over the
-  // batch): per extra block its own inner buffers and split-K partials, and
-  // the middle block's output
-  long long conc_frames = 0;
-  long long ws_conc_T[2] = {0, 0}, ws_conc_Xr[2] = {0, 0}, ws_conc_An[2] = {0, 0}, ws_conc_B1 = 0;
-  long long ws_partial_aux[2] = {0, 0}, partial_aux_floats = 0;
-  std::vector<long long> ws_A;
+  // workspace layout of the handle (max_batch x max_frames) and its size,
+  // which also covers the float repack staged there by an int8 create
+  WsLayout ws;
   long long ws_floats = 0;
+  // largest split-K partial of any GEMM per frame-row of a chunk: groups x
+  // (GEMM rows per frame) x M
+  long long partial_per_row = 0;
   // frames at the end of a chunk that determine every carried row after the
   // transformer (prefill decodes only these through the upsampling stack)
   int tail_frames = 0;
@@ -207,6 +219,64 @@ int add_slot(Plan& P, int H, int C, long long rate) {
   P.slots.push_back(s);
   P.state_floats += align_up((long long)H * C);
   return (int)P.slots.size() - 1;
+}
+
+// Lay out the per-call buffers of decodes of up to `batch` streams x `frames`
+// frames.  compact: the layout of the static scratch of the no-allocation
+// entry point -- split-K partial room in proportion to the rows (launches
+// whose partials do not fit are not split: the same bits) and no room for an
+// expanded int8 layer (int8 weights are dequantized per tile: the same bits);
+// otherwise the handle's workspace layout.  Needs P's layers and stages.
+void layout_workspace(const Plan& P, long long batch, long long frames, bool compact, WsLayout& L) {
+  const vocoder_config& c = P.cfg;
+  const int d = P.d, De = c.embed_dim, F = c.ffn_dim;
+  const long long Rr = batch * frames;
+  L = WsLayout{};
+  long long ws = 0;
+  auto Wk = [&](long long n) { long long o = ws; ws += align_up(n); return o; };
+  L.status = Wk(64);
+  L.pos = Wk(batch);
+  L.rope = Wk(Rr * std::max(P.half, 1) * 2);
+  L.emb = Wk(Rr * De);
+  L.h = Wk(Rr * d);
+  L.u = Wk(Rr * d);
+  L.qkv = Wk(Rr * 3 * d);
+  L.att = Wk(Rr * d);
+  L.ffn = Wk(Rr * F);
+  long long ur = 1;
+  for (int i = 0; i < c.n_up; ++i) {
+    ur *= c.up_strides[i];
+    L.up[i] = Wk(Rr * ur * d);
+  }
+  long long big = Rr * ur * c.voc_ch0;  // conv_pre output
+  for (const StageP& S : P.stages) big = std::max(big, Rr * S.rate * S.c);
+  L.X0 = Wk(big);
+  for (int j = 0; j < c.n_res; ++j) L.A[j] = Wk(big);
+  L.T = Wk(big);
+  L.Xr = Wk(big);
+  L.An = Wk(big);
+  L.S[0] = Wk(big);
+  L.S[1] = Wk(big);
+  // split-K partials: used only by launches with few output tiles, which are
+  // small; 32 M floats (128 MB) bounds the split factor of the rest
+  L.partial_floats = compact ? std::min<long long>(32LL << 20, Rr * P.partial_per_row) : 32LL << 20;
+  L.partial = Wk(L.partial_floats);
+  if (c.n_res >= 2 && c.n_res <= 3) {
+    L.conc_frames = std::min<long long>(Rr, VOC_CONC_FRAMES);
+    long long bigc = 0;
+    for (const StageP& S : P.stages) bigc = std::max(bigc, L.conc_frames * S.rate * S.c);
+    for (int j = 0; j < 2; ++j) {
+      L.conc_T[j] = Wk(bigc);
+      L.conc_Xr[j] = Wk(bigc);
+      L.conc_An[j] = Wk(bigc);
+    }
+    L.conc_B1 = Wk(bigc);
+    L.partial_aux_floats = compact ? std::min<long long>(8LL << 20, Rr * P.partial_per_row) : 8LL << 20;
+    for (int j = 0; j < 2; ++j) L.partial_aux[j] = Wk(L.partial_aux_floats);
+  }
+  if (P.max_q8_values > 0 && !compact) L.wdeq = Wk(P.f16 ? (P.max_q8_values + 1) / 2 : P.max_q8_values);
+  L.snap = Wk(batch * P.state_floats);
+  L.floats = ws;
 }
 
 bool make_plan(const vocoder_config* cp, Plan& P) {
@@ -351,53 +421,32 @@ bool make_plan(const vocoder_config* cp, Plan& P) {
   P.raw_count = raw;
   P.packed_floats = pk;
 
-  // workspace, sized for max_batch x max_frames
-  const long long Rr = (long long)c.max_batch * c.max_frames;
-  long long ws = 0;
-  auto Wk = [&](long long n) { long long o = ws; ws += align_up(n); return o; };
-  P.ws_status = Wk(64);
-  P.ws_pos = Wk(c.max_batch);
-  P.ws_rope = Wk(Rr * std::max(P.half, 1) * 2);
-  P.ws_emb = Wk(Rr * De);
-  P.ws_h = Wk(Rr * d);
-  P.ws_u = Wk(Rr * d);
-  P.ws_qkv = Wk(Rr * 3 * d);
-  P.ws_att = Wk(Rr * d);
-  P.ws_ffn = Wk(Rr * F);
-  long long ur = 1;
-  for (int i = 0; i < c.n_up; ++i) {
-    ur *= c.up_strides[i];
-    P.ws_up.push_back(Wk(Rr * ur * d));
-  }
-  long long big = Rr * ur * C0;  // conv_pre output
-  for (const StageP& S : P.stages) big = std::max(big, Rr * S.rate * S.c);
-  P.ws_X0 = Wk(big);
-  for (int j = 0; j < c.n_res; ++j) P.ws_A.push_back(Wk(big));
-  P.ws_T = Wk(big);
-  P.ws_Xr = Wk(big);
-  P.ws_An = Wk(big);
-  P.ws_S[0] = Wk(big);
-  P.ws_S[1] = Wk(big);
-  // split-K partials: used only by launches with few output tiles, which are
-  // small; 32 M floats (128 MB) bounds the split factor of the rest
-  P.partial_floats = 32LL << 20;
-  P.ws_partial = Wk(P.partial_floats);
-  if (c.n_res >= 2 && c.n_res <= 3) {
-    P.conc_frames = std::min<long long>(Rr, VOC_CONC_FRAMES);
-    long long bigc = 0;
-    for (const StageP& S : P.stages) bigc = std::max(bigc, P.conc_frames * S.rate * S.c);
-    for (int j = 0; j < 2; ++j) {
-      P.ws_conc_T[j] = Wk(bigc);
-      P.ws_conc_Xr[j] = Wk(bigc);
-      P.ws_conc_An[j] = Wk(bigc);
+  {
+    auto need = [&](const GemmW& g, long long rows_per_frame) {
+      const long long ngroups = ((long long)g.k * g.cin + VOC_GROUP_K - 1) / VOC_GROUP_K;
+      P.partial_per_row = std::max(P.partial_per_row, ngroups * rows_per_frame * g.M);
+    };
+    need(P.pre, 1);
+    for (const LayerP& L : P.layers) {
+      need(L.qkv, 1); need(L.o, 1); need(L.fc1, 1); need(L.fc2, 1);
     }
-    P.ws_conc_B1 = Wk(bigc);
-    P.partial_aux_floats = 8LL << 20;
-    for (int j = 0; j < 2; ++j) P.ws_partial_aux[j] = Wk(P.partial_aux_floats);
+    long long r = 1;
+    for (int i = 0; i < c.n_up; ++i) {
+      need(P.ups[i], r);
+      r *= c.up_strides[i];
+    }
+    need(P.conv_pre, r);
+    for (const StageP& S : P.stages) {
+      need(S.up, S.rate / S.r);
+      for (const AmpP& A : S.amp) {
+        need(A.conv1, S.rate);
+        need(A.conv2, S.rate);
+      }
+    }
   }
-  if (P.max_q8_values > 0) P.ws_wdeq = Wk(P.f16 ? (P.max_q8_values + 1) / 2 : P.max_q8_values);
-  P.ws_snap = Wk((long long)c.max_batch * P.state_floats);
-  P.ws_floats = ws;
+  // workspace, sized for max_batch x max_frames
+  layout_workspace(P, c.max_batch, c.max_frames, false, P.ws);
+  P.ws_floats = P.ws.floats;
   // int8 weights are quantized at create time from a float repack staged in
   // the workspace
   if (c.weight_format == VOCODER_WEIGHTS_INT8) P.ws_floats = std::max(P.ws_floats, align_up(P.max_gemm_values));
@@ -462,6 +511,8 @@ struct vocoder {
     double flops, bytes;
   };
   bool prof = false;
+  bool no_events = false;  // a no-allocation call: no profiling events
+  float* scratch = nullptr;  // device address of the static scratch on the handle's device (or null)
   std::vector<hipEvent_t> events;
   std::vector<Rec> recs;
   std::vector<std::string> prof_names;
@@ -495,8 +546,8 @@ namespace {
 // Brackets one kernel launch with HIP events while profiling is on.
 class Prof {
  public:
-  Prof(vocoder* v, hipStream_t s, const std::string& name, double flops, double bytes) : v_(v), s_(s) {
-    if (!v->prof || v->capturing) return;
+  Prof(vocoder* v, hipStream_t s, const char* name, double flops, double bytes) : v_(v), s_(s) {
+    if (!v->prof || v->capturing || v->no_events) return;
     int id = -1;
     for (size_t i = 0; i < v->prof_names.size(); ++i)
       if (v->prof_names[i] == name) id = (int)i;
@@ -682,7 +733,7 @@ int run_gemm(const Ctx& cx, const ConvParams& pin, const LnArgs* ln = nullptr) {
 }
 
 void tap(const Ctx& cx, const char* name, const float* src, long long count) {
-  if (cx.v->capturing || cx.quiet) return;
+  if (cx.v->capturing || cx.quiet || cx.v->taps.empty()) return;
   auto it = cx.v->taps.find(name);
   if (it == cx.v->taps.end() || !it->second.first) return;
   if ((size_t)count > it->second.second) return;
@@ -704,7 +755,7 @@ int repack_gemm(vocoder* v, const float* raw, const GemmW& g, bool transposed, h
   const bool slab = (v->P.f16 || g.split) && g.cin % 32 == 0;
   const long long lo = g.split ? g.lo_halves() : 0;
   const float sc = std::ldexp(1.f, SPLIT_W_EXP);
-  int* flag = reinterpret_cast<int*>(v->ws + v->P.ws_status);  // cleared before the repacks
+  int* flag = reinterpret_cast<int*>(v->ws + v->P.ws.status);  // cleared before the repacks
   if (transposed) {
     HIP_OK(launch_repack_convT(raw + g.raw_w, dst, g.cin, g.cout, g.phases, g.Mpad, half, slab, s, lo, sc, flag));
     HIP_OK(launch_expand_vec(raw + g.raw_b, pk + g.bias, g.cout, g.phases, g.Mpad, s));
@@ -726,6 +777,39 @@ int copy_d2d(float* dst, const float* src, long long n, hipStream_t s) {
     int _r = (x);                  \
     if (_r != VOCODER_OK) return _r; \
   } while (0)
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Static scratch of the no-allocation entry point: the per-call buffers of a
+// vocoder_decode_chunk_noalloc call, laid out for that call's batch x frames
+// (layout_workspace, compact).  Each GPU the library runs on holds its own
+// copy until the process ends; host code uses the device address looked up
+// once per device (never the array's name, which on the host is only a
+// stand-in).  Every no-allocation call on a GPU shares that GPU's copy.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[VOCODER_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex scratch_mu;
+float* scratch_addr[SCRATCH_MAX_DEVICES] = {};
+bool scratch_looked_up[SCRATCH_MAX_DEVICES] = {};
+
+// The device address of `scratch` on the current device (looked up on the
+// first call for that device), or null if it could not be obtained.
+float* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= SCRATCH_MAX_DEVICES) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_looked_up[dev]) {
+    scratch_looked_up[dev] = true;
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess && ptr) scratch_addr[dev] = (float*)ptr;
+  }
+  return scratch_addr[dev];
+}
 
 }  // namespace
 
@@ -776,7 +860,7 @@ int vocoder_create(const vocoder_config* cfg, const float* raw_weights, void* pa
 
   if (launch_fill(pk, (size_t)P.packed_floats * 4, s) != hipSuccess) return fail(VOCODER_EHIP);
   // the split repacks flag weights out of range in the status word
-  if (launch_fill(v->ws + P.ws_status, 256, s) != hipSuccess) return fail(VOCODER_EHIP);
+  if (launch_fill(v->ws + P.ws.status, 256, s) != hipSuccess) return fail(VOCODER_EHIP);
   if ((rc = copy_d2d(pk + P.codebooks, raw + P.raw_codebooks,
                      (long long)c.n_codebooks * c.codebook_size * c.embed_dim, s))) return fail(rc);
   if ((rc = repack_gemm(v, raw, P.pre, false, s))) return fail(rc);
@@ -799,7 +883,7 @@ int vocoder_create(const vocoder_config* cfg, const float* raw_weights, void* pa
       // follows the whole stacked hi plane)
       if (launch_repack_conv(raw + raw_w[t], dst, d, d, d, 1, half, false, s,
                              L.qkv.split ? L.qkv.lo_halves() : 0, std::ldexp(1.f, SPLIT_W_EXP),
-                             reinterpret_cast<int*>(v->ws + P.ws_status)) != hipSuccess)
+                             reinterpret_cast<int*>(v->ws + P.ws.status)) != hipSuccess)
         return fail(VOCODER_EHIP);
       if ((rc = copy_d2d(pk + L.qkv.bias + (long long)t * d, raw + raw_b[t], d, s))) return fail(rc);
     }
@@ -853,18 +937,21 @@ int vocoder_create(const vocoder_config* cfg, const float* raw_weights, void* pa
   if (hipStreamSynchronize(s) != hipSuccess) return fail(VOCODER_EHIP);
   if (P.split) {
     int range = 0;
-    if (hipMemcpy(&range, v->ws + P.ws_status, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess)
+    if (hipMemcpy(&range, v->ws + P.ws.status, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess)
       return fail(VOCODER_EHIP);
     if (range) return fail(VOCODER_EINVAL);  // a weight beyond the split's range
   }
-  if (launch_fill(v->ws + P.ws_status, 256, s) != hipSuccess) return fail(VOCODER_EHIP);
-  if (P.conc_frames > 0) {
+  if (launch_fill(v->ws + P.ws.status, 256, s) != hipSuccess) return fail(VOCODER_EHIP);
+  if (P.ws.conc_frames > 0) {
     bool ok = hipEventCreateWithFlags(&v->ev_fork, hipEventDisableTiming) == hipSuccess;
     for (int j = 0; j < 2 && ok; ++j)
       ok = hipStreamCreateWithFlags(&v->aux[j], hipStreamNonBlocking) == hipSuccess &&
            hipEventCreateWithFlags(&v->ev_join[j], hipEventDisableTiming) == hipSuccess;
     if (!ok) return fail(VOCODER_EHIP);
   }
+  // the no-allocation entry point's scratch on this (the handle's) device;
+  // if it cannot be had, that entry point reports VOCODER_EHIP
+  v->scratch = scratch_on_current_device();
   *out = v;
   return VOCODER_OK;
 }
@@ -904,15 +991,18 @@ bool decode_args_ok(const vocoder* v, const int32_t* codes, int batch, int n_fra
 // memset, so the sequence can be recorded into a HIP graph as it stands.
 // prefill: produce state_out only (no PCM, no taps), taking the stack after
 // the transformer through the chunk's last tail_frames frames alone.
-int decode_launches(vocoder* v, const int32_t* codes, int batch, int n_frames, const void* state_in,
-                    void* state_out, float* pcm, void* stream, bool prefill = false) {
+// L / wsb: the layout and base of the per-call buffers (the handle's
+// workspace, or the static scratch of the no-allocation entry point); the
+// status word is always the handle's.
+int decode_launches(vocoder* v, const WsLayout& L, float* wsb, const int32_t* codes, int batch, int n_frames,
+                    const void* state_in, void* state_out, float* pcm, void* stream, bool prefill = false) {
   const Plan& P = v->P;
   const vocoder_config& c = P.cfg;
   // In place (state_out == state_in): every kernel below reads the old state
   // while others write the new one, so the batch's states are first copied to
   // the workspace and read from there.
   if (state_in == state_out) {
-    float* snap = v->ws + P.ws_snap;
+    float* snap = wsb + L.snap;
     const long long n = (long long)batch * P.state_floats;
     {
       Prof pr(v, (hipStream_t)stream, "state_snapshot", 0, 8.0 * n);
@@ -922,9 +1012,9 @@ int decode_launches(vocoder* v, const int32_t* codes, int batch, int n_frames, c
   }
   Ctx cx;
   cx.quiet = prefill;
-  cx.partial = v->ws + P.ws_partial;
-  cx.partial_floats = P.partial_floats;
-  cx.wdeq = P.ws_wdeq ? v->ws + P.ws_wdeq : nullptr;
+  cx.partial = wsb + L.partial;
+  cx.partial_floats = L.partial_floats;
+  cx.wdeq = L.wdeq ? wsb + L.wdeq : nullptr;
   cx.v = v;
   cx.s = (hipStream_t)stream;
   cx.sin_ = (const float*)state_in;
@@ -934,11 +1024,11 @@ int decode_launches(vocoder* v, const int32_t* codes, int batch, int n_frames, c
   cx.T = n_frames;
   const int B = batch, T = n_frames, d = P.d;
   const int R = B * T;
-  float* ws = v->ws;
+  float* ws = wsb;
   const float* pk = v->packed;
-  int* status = reinterpret_cast<int*>(ws + P.ws_status);
-  int* pos = reinterpret_cast<int*>(ws + P.ws_pos);
-  float* rope = ws + P.ws_rope;
+  int* status = reinterpret_cast<int*>(v->ws + P.ws.status);
+  int* pos = reinterpret_cast<int*>(ws + L.pos);
+  float* rope = ws + L.rope;
 
   {
   Prof pr(v, cx.s, "begin", 0, 4.0 * B * (double)T * P.half * 2);
@@ -952,7 +1042,7 @@ int decode_launches(vocoder* v, const int32_t* codes, int batch, int n_frames, c
   }
 
   // RVQ embedding sum
-  float* emb = ws + P.ws_emb;
+  float* emb = ws + L.emb;
   const Slot& spre = P.slots[P.slot_pre];
   {
   Prof pr(v, cx.s, "gather", 0, (double)R * c.n_codebooks * (4.0 + 4.0 * c.embed_dim) + 4.0 * R * c.embed_dim);
@@ -964,8 +1054,8 @@ int decode_launches(vocoder* v, const int32_t* codes, int batch, int n_frames, c
   // Each LayerNorm runs with the GEMM that produces its input (the pre-conv
   // or a residual projection): the next layer's first norm, or the final
   // norm, whose last row feeds the first transposed conv's history.
-  float* h = ws + P.ws_h;
-  float* u = ws + P.ws_u;
+  float* h = ws + L.h;
+  float* u = ws + L.u;
   auto ln_after = [&](int l) {
     if (l < c.n_layers) return LnArgs{pk + P.layers[l].ln1_g, pk + P.layers[l].ln1_b, c.ln_eps, d, u, T, nullptr, 0, 0};
     const Slot& so = P.slots[c.n_up > 0 ? P.slot_ups[0] : P.slot_conv_pre];
@@ -982,9 +1072,9 @@ int decode_launches(vocoder* v, const int32_t* codes, int batch, int n_frames, c
   tap(cx, "pre_conv", h, (long long)R * d);
 
   // transformer
-  float* qkv = ws + P.ws_qkv;
-  float* att = ws + P.ws_att;
-  float* ffn = ws + P.ws_ffn;
+  float* qkv = ws + L.qkv;
+  float* att = ws + L.att;
+  float* ffn = ws + L.ffn;
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerP& L = P.layers[l];
     {
@@ -1048,7 +1138,7 @@ int decode_launches(vocoder* v, const int32_t* codes, int batch, int n_frames, c
   long long nin = F;
   for (int i = 0; i < c.n_up; ++i) {
     const GemmW& g = P.ups[i];
-    float* y = ws + P.ws_up[i];
+    float* y = ws + L.up[i];
     ConvParams p = base_params(cx, g, x, (int)(B * nin), (int)nin, 1, P.slot_ups[i]);
     const int next = i + 1 < c.n_up ? P.slot_ups[i + 1] : P.slot_conv_pre;
     add_out(cx, p, y, nullptr, next);
@@ -1061,7 +1151,7 @@ int decode_launches(vocoder* v, const int32_t* codes, int batch, int n_frames, c
   }
   // conv_pre into the first stage's input
   int sbuf = 0;
-  float* S_in = ws + P.ws_S[sbuf];
+  float* S_in = ws + L.S[sbuf];
   {
     ConvParams p = base_params(cx, P.conv_pre, x, (int)(B * nin), (int)nin, 1, P.slot_conv_pre);
     add_out(cx, p, S_in, nullptr, P.stages[0].slot_up);
@@ -1070,21 +1160,21 @@ int decode_launches(vocoder* v, const int32_t* codes, int batch, int n_frames, c
   tap(cx, "conv_pre", S_in, B * nin * c.voc_ch0);
 
   // BigVGAN stages
-  float* X0 = ws + P.ws_X0;
-  float* Tb = ws + P.ws_T;
-  float* Xr = ws + P.ws_Xr;
-  float* An = ws + P.ws_An;
+  float* X0 = ws + L.X0;
+  float* Tb = ws + L.T;
+  float* Xr = ws + L.Xr;
+  float* An = ws + L.An;
   for (int si = 0; si < c.n_stages; ++si) {
     const StageP& S = P.stages[si];
     const bool last_stage = si + 1 == c.n_stages;
-    float* S_out = ws + P.ws_S[sbuf ^ 1];
+    float* S_out = ws + L.S[sbuf ^ 1];
     // transposed conv: raw output + the first Snake of every AMP block
     {
       ConvParams p = base_params(cx, S.up, S_in, (int)(B * nin), (int)nin, 1, S.slot_up);
       add_out(cx, p, X0, nullptr, -1);
       // Snake outputs are read only as GEMM operands: fp16 in fp16 mode
       for (int j = 0; j < c.n_res; ++j)
-        add_out(cx, p, ws + P.ws_A[j], pk + S.up_alpha[j], S.amp[(size_t)j * c.n_dil].slot1, 0, P.f16);
+        add_out(cx, p, ws + L.A[j], pk + S.up_alpha[j], S.amp[(size_t)j * c.n_dil].slot1, 0, P.f16);
       CHECK(run_gemm(cx, p));
     }
     nin *= S.r;
@@ -1101,7 +1191,7 @@ int decode_launches(vocoder* v, const int32_t* codes, int batch, int n_frames, c
     // sums the multi-receptive-field mean in the sequential order, ((block 0
     // + block 1) + block 2) / 3.  Longer chunks fill the GPU one block at a
     // time and run the blocks in order.
-    const bool conc = P.conc_frames > 0 && (long long)B * T <= P.conc_frames && v->aux[0] && v->aux[1];
+    const bool conc = L.conc_frames > 0 && (long long)B * T <= L.conc_frames && v->aux[0] && v->aux[1];
     if (conc) {
       HIP_OK(hipEventRecord(v->ev_fork, cx.s));
       for (int j = 0; j + 1 < c.n_res; ++j) HIP_OK(hipStreamWaitEvent(v->aux[j], v->ev_fork, 0));
@@ -1114,16 +1204,16 @@ int decode_launches(vocoder* v, const int32_t* codes, int batch, int n_frames, c
       float* an = An;
       if (side) {
         bc.s = v->aux[j];
-        bc.partial = ws + P.ws_partial_aux[j];
-        bc.partial_floats = P.partial_aux_floats;
+        bc.partial = ws + L.partial_aux[j];
+        bc.partial_floats = L.partial_aux_floats;
         bc.wdeq = nullptr;  // the int8 kernels dequantize per tile
-        tb = ws + P.ws_conc_T[j];
-        xr = ws + P.ws_conc_Xr[j];
-        an = ws + P.ws_conc_An[j];
+        tb = ws + L.conc_T[j];
+        xr = ws + L.conc_Xr[j];
+        an = ws + L.conc_An[j];
       }
       for (int i = 0; i < c.n_dil; ++i) {
         const AmpP& A = S.amp[(size_t)j * c.n_dil + i];
-        const float* a_in = i == 0 ? ws + P.ws_A[j] : an;
+        const float* a_in = i == 0 ? ws + L.A[j] : an;
         // conv(k, d) of Snake_1(x), then Snake_2
         {
           ConvParams p = base_params(bc, A.conv1, a_in, rows, (int)nin, c.dilations[i], A.slot1);
@@ -1150,11 +1240,11 @@ int decode_launches(vocoder* v, const int32_t* codes, int batch, int n_frames, c
             const bool fin = p.mrf_mode == MRF_LAST || p.mrf_mode == MRF_ONLY;
             if (!fin) {
               // concurrent: block 0 into S_out, block 1 into its own buffer
-              add_out(bc, p, side && j == 1 ? ws + P.ws_conc_B1 : S_out, nullptr, -1, 1);
+              add_out(bc, p, side && j == 1 ? ws + L.conc_B1 : S_out, nullptr, -1, 1);
             } else {
               if (conc) {
                 for (int jj = 0; jj + 1 < c.n_res; ++jj) HIP_OK(hipStreamWaitEvent(cx.s, v->ev_join[jj], 0));
-                if (c.n_res == 3) p.mrf2 = ws + P.ws_conc_B1;
+                if (c.n_res == 3) p.mrf2 = ws + L.conc_B1;
               }
               if (!last_stage)
                 add_out(bc, p, S_out, nullptr, P.stages[si + 1].slot_up, 1);
@@ -1198,7 +1288,7 @@ extern "C" {
 int vocoder_decode_chunk(vocoder* v, const int32_t* codes, int batch, int n_frames, const void* state_in,
                          void* state_out, float* pcm, void* stream) {
   if (!decode_args_ok(v, codes, batch, n_frames, state_in, state_out, pcm)) return VOCODER_EINVAL;
-  return decode_launches(v, codes, batch, n_frames, state_in, state_out, pcm, stream);
+  return decode_launches(v, v->P.ws, v->ws, codes, batch, n_frames, state_in, state_out, pcm, stream);
 }
 
 int vocoder_decode_chunk_graph(vocoder* v, const int32_t* codes, int batch, int n_frames, const void* state_in,
@@ -1217,7 +1307,8 @@ int vocoder_decode_chunk_graph(vocoder* v, const int32_t* codes, int batch, int 
   if (!v->capture_stream) HIP_OK(hipStreamCreateWithFlags(&v->capture_stream, hipStreamNonBlocking));
   HIP_OK(hipStreamBeginCapture(v->capture_stream, hipStreamCaptureModeThreadLocal));
   v->capturing = true;
-  const int rc = decode_launches(v, codes, batch, n_frames, state_in, state_out, pcm, v->capture_stream);
+  const int rc =
+      decode_launches(v, v->P.ws, v->ws, codes, batch, n_frames, state_in, state_out, pcm, v->capture_stream);
   v->capturing = false;
   hipGraph_t graph = nullptr;
   const hipError_t ec = hipStreamEndCapture(v->capture_stream, &graph);
@@ -1241,6 +1332,19 @@ int vocoder_decode_chunk_graph(vocoder* v, const int32_t* codes, int batch, int 
   return VOCODER_OK;
 }
 
+int vocoder_decode_chunk_noalloc(vocoder* v, const int32_t* codes, int batch, int n_frames, const void* state_in,
+                                 void* state_out, float* pcm, void* stream) {
+  if (!decode_args_ok(v, codes, batch, n_frames, state_in, state_out, pcm)) return VOCODER_EINVAL;
+  WsLayout L;
+  layout_workspace(v->P, batch, n_frames, true, L);
+  if ((unsigned long long)L.floats * 4 > (unsigned long long)VOCODER_NOALLOC_SCRATCH_BYTES) return VOCODER_ESCRATCH;
+  if (!v->scratch) return VOCODER_EHIP;
+  v->no_events = true;
+  const int rc = decode_launches(v, L, v->scratch, codes, batch, n_frames, state_in, state_out, pcm, stream);
+  v->no_events = false;
+  return rc;
+}
+
 int vocoder_quantize_int8(const float* src, long long rows, int K, int8_t* q, uint16_t* scale, void* stream) {
   if (!src || !q || !scale || rows < 0 || K <= 0 || K % 32 != 0) return VOCODER_EINVAL;
   HIP_OK(launch_quantize_rows(src, rows, K, q, scale, (hipStream_t)stream));
@@ -1252,7 +1356,7 @@ int vocoder_graph_cache_size(const vocoder* v) { return v ? (int)v->graphs.size(
 int vocoder_prefill(vocoder* v, const int32_t* codes, int batch, int n_frames, const void* state_in,
                     void* state_out, void* stream) {
   if (!decode_args_ok(v, codes, batch, n_frames, state_in, state_out, nullptr, false)) return VOCODER_EINVAL;
-  return decode_launches(v, codes, batch, n_frames, state_in, state_out, nullptr, stream, true);
+  return decode_launches(v, v->P.ws, v->ws, codes, batch, n_frames, state_in, state_out, nullptr, stream, true);
 }
 
 int vocoder_prefill_tail_frames(const vocoder* v) { return v ? v->P.tail_frames : 0; }
@@ -1302,8 +1406,8 @@ int vocoder_get_status(vocoder* v, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   int st = 0;
   HIP_OK(hipStreamSynchronize(s));
-  HIP_OK(hipMemcpy(&st, v->ws + v->P.ws_status, sizeof(int), hipMemcpyDeviceToHost));
-  HIP_OK(launch_fill(v->ws + v->P.ws_status, 256, s));
+  HIP_OK(hipMemcpy(&st, v->ws + v->P.ws.status, sizeof(int), hipMemcpyDeviceToHost));
+  HIP_OK(launch_fill(v->ws + v->P.ws.status, 256, s));
   HIP_OK(hipStreamSynchronize(s));
   if (st & VOC_STATUS_CODE) return VOCODER_ECODE;
   if (st & VOC_STATUS_STATE) return VOCODER_ESTATE;
@@ -1329,6 +1433,7 @@ const char* vocoder_strerror(int status) {
     case VOCODER_ESTATE: return "state does not belong to this decoder";
     case VOCODER_EHIP: return "HIP error";
     case VOCODER_ECODE: return "code out of range";
+    case VOCODER_ESCRATCH: return "chunk needs more than the static scratch of the no-allocation entry point";
   }
   return "unknown status";
 }
