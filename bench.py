@@ -1,6 +1,6 @@
 """Throughput of the streaming code2wav decoder on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--precision f32|f16|split] [--weights float|int8] [--graph] [--no-cpu-baseline] [--no-split-line]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--precision f32|f16|split] [--weights float|int8] [--graph] [--no-cpu-baseline] [--split-line] [--peaks-only]
 
 A step decodes one 25-frame chunk (2 s of audio) for each of 64 independent
 streams whose states were first warmed (untimed) to different positions: the
@@ -36,9 +36,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="qwen3_b64_chunk25")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-split-line", action="store_true",
-                    help="fp32 batched run: skip the secondary measurement of the split-fp16 precision")
-    ap.add_argument("--cpu-frames", type=int, default=100)
+    ap.add_argument("--split-line", action="store_true",
+                    help="fp32 batched run: also time the split-fp16 precision on the same workload")
+    ap.add_argument("--cpu-streams", type=int, default=4,
+                    help="streams of the timed step whose chunks the CPU oracle decodes for cpu_baseline")
     ap.add_argument("--profile-chunk", type=int, default=0,
                     help="chunk-schedule workloads: add per-kernel device times of the chunks of this length")
     ap.add_argument("--weights", choices=["float", "int8"], default="float",
@@ -49,6 +50,8 @@ def parse():
                     help="matrix-product operands: f32; fp16 with fp32 sums (the half-precision decoder); or "
                          "split (fp32 values, each product as three fp16 MFMA products of hi/lo halves)")
     # measurement helpers (each replaces the timed run)
+    ap.add_argument("--peaks-only", action="store_true",
+                    help="run only the roofline microbenchmarks (fp32/fp16 MFMA loops, HBM read and copy)")
     ap.add_argument("--counters", action="store_true",
                     help="decode exactly one batched step from fresh states, for rocprofv3 --pmc runs")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -143,6 +146,60 @@ def traffic_summary(gemm_fetch, gemm_write, copy_fetch, copy_write, copy_bytes):
         json.dump(rec, f, indent=1)
 
 
+def measure_peaks(torch, vb, reps=5):
+    """The roofline denominators measured on this GPU by the library's
+    microbenchmark kernels (HIP events on the current stream, best of `reps`
+    after a warm-up): dense fp32 and fp16 MFMA rates from register-only MFMA
+    loops, and HBM rates of a streaming read (2 GiB) and a copy (1 GiB each
+    way)."""
+    stream = torch.cuda.current_stream()
+
+    def best(fn):
+        fn()
+        torch.cuda.synchronize()
+        out = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1) / 1e3)
+        return min(out)
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks, iters = 4 * cus, 16384
+    sink = torch.empty(blocks * 256, device="cuda")
+    res = {}
+    for dtype, key in ((0, "mfma_f32_tflops"), (1, "mfma_f16_tflops")):
+        def run(dtype=dtype):
+            if vb.vocoder_peak_mfma(dtype, sink, blocks, iters) != vb.VOCODER_OK:
+                raise SystemExit("vocoder_peak_mfma failed")
+        res[key] = round(vb.vocoder_peak_mfma_flops(dtype, blocks, iters) / best(run) / 1e12, 2)
+    n_read = (2 << 30) // 4
+    src = torch.ones(n_read, device="cuda")
+    rblocks = 8 * cus
+    rsink = torch.empty(rblocks * 256, device="cuda")
+
+    def read():
+        if vb.vocoder_stream_read(src, n_read, rsink, rblocks) != vb.VOCODER_OK:
+            raise SystemExit("vocoder_stream_read failed")
+    res["hbm_read_gbs"] = round(4.0 * n_read / best(read) / 1e9, 1)
+    n_copy = (1 << 30) // 4
+    a, b = src[:n_copy], src[n_copy:2 * n_copy]
+
+    def copy():
+        if vb.vocoder_stream_copy(a, b, n_copy, rblocks) != vb.VOCODER_OK:
+            raise SystemExit("vocoder_stream_copy failed")
+    res["hbm_copy_gbs"] = round(8.0 * n_copy / best(copy) / 1e9, 1)
+    del src, sink, rsink
+    torch.cuda.empty_cache()
+    res["method"] = (f"register-only MFMA loops ({blocks} workgroups x 4 waves x 4 independent chains), "
+                     f"stream read of 2 GiB and copy of 1 GiB (16-byte grid-stride, {rblocks} workgroups); "
+                     f"best of {reps} after a warm-up, HIP events")
+    return res
+
+
 def warm_states(dec, codes, batch, torch):
     """Bring stream b to position batched_warmup_frames(b) (untimed)."""
     import synthetic as S
@@ -169,8 +226,12 @@ def warm_states(dec, codes, batch, torch):
     return st_a, st_b, warm
 
 
-def cpu_baseline(model, W, codes_1, frames):
-    """The float32 oracle on the host cores, one stream, `frames` frames from a fresh state."""
+def cpu_baseline(model, W, chunks, warm):
+    """The float32 oracle on the host cores, on a bounded sample of the timed
+    step: the 25-frame chunks of its first len(chunks) streams (the same codes
+    the GPU decodes), each decoded from a fresh state rather than after its
+    untimed warm-up (which sets only the attention window's fill and the
+    conv histories; the convolutions are 99 % of the work either way)."""
     from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import decoder as O
@@ -180,8 +241,10 @@ def cpu_baseline(model, W, codes_1, frames):
         used = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
         Wf = O.cast_weights(W, np.float32)
         t0 = time.perf_counter()
-        O.decode_whole(model, Wf, codes_1[:frames], dtype=np.float32)
+        for c in chunks:
+            O.decode_whole(model, Wf, c, dtype=np.float32)
         el = time.perf_counter() - t0
+    frames = sum(c.shape[0] for c in chunks)
     audio = frames * FRAME_SECONDS
     cpu = "unknown"
     try:
@@ -190,8 +253,10 @@ def cpu_baseline(model, W, codes_1, frames):
     except OSError:
         pass
     return {"value": audio / el, "unit": "audio-s/s", "cores": int(used), "kind": "oracle", "cpu_model": cpu,
-            "sample": f"1 stream x {frames} frames ({audio:g} s of audio) from a fresh state, float32 numpy "
-                      f"oracle, {el:.1f} s wall"}
+            "sample": f"the timed 25-frame chunks of streams 0-{len(chunks) - 1} of the 64-stream step "
+                      f"({frames} frames, {audio:g} s of audio; the GPU decodes them after warm-ups to positions "
+                      f"{', '.join(str(w) for w in warm[:len(chunks)])}, the oracle from fresh states), "
+                      f"float32 numpy oracle, {el:.1f} s wall"}
 
 
 def stream_latency(args, wl, torch, S, Decoder, vb):
@@ -339,6 +404,11 @@ def main():
     import synthetic as S
     from vocoder_rvq_codebook_amd import Decoder, binding as vb
 
+    if args.peaks_only:
+        torch.cuda.set_device(0)
+        print(json.dumps({"peaks_measured": measure_peaks(torch, vb)}), flush=True)
+        return
+
     if args.copy_bytes:
         src = torch.ones(args.copy_bytes // 4, device="cuda")
         dst = torch.empty_like(src)
@@ -360,6 +430,7 @@ def main():
     W = S.make_weights(model, wl["weight_seed"])
     codes = S.workload_codes(args.workload)
     torch.cuda.set_device(0)
+    peaks = None if args.counters else measure_peaks(torch, vb)
     dec = Decoder(model, torch.from_numpy(S.flatten_weights(model, W)), B, T)
     if args.counters:
         st_a, st_b = dec.new_state(B), dec.new_state(B)
@@ -435,10 +506,14 @@ def main():
         "roofline": {"kernel": dom_name, "bound": "mfma", "achieved": round(dom_tflops, 3),
                      "peak": peak, "unit": "TFLOP/s",
                      "frac": round(dom_tflops / peak, 4),
+                     "peak_measured": peaks["mfma_f32_tflops" if args.precision == "f32" else "mfma_f16_tflops"],
+                     "frac_of_measured": round(dom_tflops / peaks["mfma_f32_tflops" if args.precision == "f32"
+                                                                  else "mfma_f16_tflops"], 4),
                      "avg_launch_ms": round(dom_ms, 4), "traffic": traffic_for(dom_name)},
+        "peaks_measured": peaks,
         "kernels": kernels,
     }
-    if args.precision == "f32" and args.weights == "float" and not args.no_split_line:
+    if args.precision == "f32" and args.weights == "float" and args.split_line:
         # the same workload with fp32-accurate products on the fp16 MFMA, timed
         # the same way in a child process (its own device memory); `value` above
         # stays the fp32 MFMA path's
@@ -446,7 +521,8 @@ def main():
         torch.cuda.empty_cache()
         out["split16"] = split_line(args)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(model, W, codes[0], args.cpu_frames)
+        out["cpu_baseline"] = cpu_baseline(model, W, [codes[b, warm[b]:warm[b] + T] for b in range(args.cpu_streams)],
+                                           warm)
     print(json.dumps(out), flush=True)
 
 

@@ -336,6 +336,26 @@ typedef struct vocoder_kernel_stat {
 int vocoder_profile_begin(vocoder* v);
 int vocoder_profile_end(vocoder* v, void* stream, vocoder_kernel_stat* out, int max_entries, int* n_entries);
 
+/* Roofline microbenchmarks: kernels of their own that measure, on the GPU at
+ * hand, the two denominators the decoder's kernels are judged against (the
+ * benchmark reports them beside the vendor's peaks).  None needs a handle.
+ *
+ * vocoder_peak_mfma: `blocks` workgroups of 4 waves, each wave issuing `iters`
+ * rounds of 4 independent dependent-chain MFMAs on operands held in
+ * registers -- v_mfma_f32_16x16x4_f32 (dtype 0) or v_mfma_f32_16x16x32_f16
+ * (dtype 1) -- with no memory traffic but one float per thread written to
+ * `out` (device, blocks * 256 floats).  iters: a positive multiple of 8.
+ * vocoder_peak_mfma_flops gives the FLOPs such a launch performs.
+ * vocoder_stream_read: sum n floats of `src` (device, 16-byte aligned, n a
+ * multiple of 4) with `blocks` workgroups of 256 threads, grid-stride 16-byte
+ * loads, one float per thread to `out` (blocks * 256 floats).
+ * vocoder_stream_copy: dst[i] = src[i] for n floats (both 16-byte aligned).
+ * All enqueue on `stream`.  Errors: VOCODER_EINVAL, VOCODER_EHIP. */
+double vocoder_peak_mfma_flops(int dtype, int blocks, int iters);
+int vocoder_peak_mfma(int dtype, float* out, int blocks, int iters, void* stream);
+int vocoder_stream_read(const float* src, long long n, float* out, int blocks, void* stream);
+int vocoder_stream_copy(const float* src, float* dst, long long n, int blocks, void* stream);
+
 /* Free the host handle (device buffers stay the caller's). */
 void vocoder_destroy(vocoder* v);
 

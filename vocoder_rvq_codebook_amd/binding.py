@@ -122,6 +122,14 @@ def lib():
         L.vocoder_profile_begin.restype = i32
         L.vocoder_profile_end.argtypes = [vp, vp, ctypes.POINTER(VocoderKernelStat), i32, ctypes.POINTER(i32)]
         L.vocoder_profile_end.restype = i32
+        L.vocoder_peak_mfma_flops.argtypes = [i32, i32, i32]
+        L.vocoder_peak_mfma_flops.restype = ctypes.c_double
+        L.vocoder_peak_mfma.argtypes = [i32, vp, i32, i32, vp]
+        L.vocoder_peak_mfma.restype = i32
+        L.vocoder_stream_read.argtypes = [vp, ctypes.c_longlong, vp, i32, vp]
+        L.vocoder_stream_read.restype = i32
+        L.vocoder_stream_copy.argtypes = [vp, vp, ctypes.c_longlong, i32, vp]
+        L.vocoder_stream_copy.restype = i32
         L.vocoder_destroy.argtypes = [vp]
         L.vocoder_destroy.restype = None
         L.vocoder_strerror.argtypes = [i32]
@@ -270,6 +278,22 @@ def vocoder_profile_end(handle, stream=None, max_entries: int = 64):
         raise VocoderError(rc, "vocoder_profile_end")
     return {arr[i].name.decode(): dict(launches=arr[i].launches, total_ms=arr[i].total_ms, flops=arr[i].flops,
                                        bytes=arr[i].bytes) for i in range(min(n.value, max_entries))}
+
+
+def vocoder_peak_mfma_flops(dtype: int, blocks: int, iters: int) -> float:
+    return lib().vocoder_peak_mfma_flops(int(dtype), int(blocks), int(iters))
+
+
+def vocoder_peak_mfma(dtype: int, out, blocks: int, iters: int, stream=None) -> int:
+    return lib().vocoder_peak_mfma(int(dtype), _ptr(out), int(blocks), int(iters), _stream(stream))
+
+
+def vocoder_stream_read(src, n: int, out, blocks: int, stream=None) -> int:
+    return lib().vocoder_stream_read(_ptr(src), int(n), _ptr(out), int(blocks), _stream(stream))
+
+
+def vocoder_stream_copy(src, dst, n: int, blocks: int, stream=None) -> int:
+    return lib().vocoder_stream_copy(_ptr(src), _ptr(dst), int(n), int(blocks), _stream(stream))
 
 
 def vocoder_destroy(handle) -> None:
