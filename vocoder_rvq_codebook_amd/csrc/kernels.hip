@@ -336,40 +336,77 @@ __global__ __launch_bounds__(POST_ROWS) void conv_post_kernel(
 // order -- the operations and order of conv_post_kernel, so the same bits.
 // A block covers POST_T input rows and emits the POST_T-(K-1) samples whose
 // rows it holds; a tap reaching before the stream's chunk is summed from the
-// history slot in place.
+// history slot in place.  The rows are staged through LDS one channel slab at
+// a time (slab channels of every row: a 128-byte line per row for 32-channel
+// slabs), with loads that cover whole lines, so each line is fetched from HBM
+// once instead of being revisited by one lane across its row.
 constexpr int POST_T = 256;
+constexpr int POST_SLAB_F4 = 8;  // float4 per row of the widest slab (32 channels)
 
 template <int K>
 __global__ __launch_bounds__(POST_T) void conv_post_rows_kernel(
     const float* __restrict__ x, const float* __restrict__ hin, long long sstride, int H,
-    const float* __restrict__ w, const float* __restrict__ bias, int C, int rows, int nin,
+    const float* __restrict__ w, const float* __restrict__ bias, int C, int slab, int rows, int nin,
     float* __restrict__ pcm, float* __restrict__ pre) {
   extern __shared__ float sm[];
-  float* ws = sm;          // [K][C]
-  float* ys = sm + K * C;  // [POST_T][K]: tap sums of each row
+  const int ld = slab + 4;   // padded slab row (floats)
+  float* ws = sm;            // [K][C]
+  float* ys = sm + K * C;    // [POST_T][K]: tap sums of each row
+  float* xs = ys + POST_T * K;  // [POST_T][ld]: one channel slab of the block's rows
   constexpr int OUT = POST_T - (K - 1);
   const int t = threadIdx.x;
   const int g_out0 = blockIdx.x * OUT;
+  const int row0 = g_out0 - (K - 1);
   for (int i = t; i < K * C; i += POST_T) ws[i] = w[i];
-  __syncthreads();
-  const int gr = g_out0 - (K - 1) + t;  // input row of this thread
-  if (gr >= 0 && gr < rows) {
-    float dot[K];
+  const int gr = row0 + t;  // input row of this thread
+  const bool mine = gr >= 0 && gr < rows;
+  float dot[K];
 #pragma unroll
-    for (int j = 0; j < K; ++j) dot[j] = 0.f;
-    const float* xr = x + (size_t)gr * C;
-#pragma unroll 4
-    for (int c = 0; c < C; c += 4) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(xr + c);
+  for (int j = 0; j < K; ++j) dot[j] = 0.f;
+  // slab c0's loads go to registers (thread t: float4 t, t + POST_T, ... of
+  // the slab's [POST_T][slab] tile) while the previous slab is summed from LDS
+  const int q4 = slab / 4;  // float4 per row per slab, at most POST_SLAB_F4
+  f32x4 buf[POST_SLAB_F4];
+  auto load = [&](int c0) {
 #pragma unroll
-      for (int j = 0; j < K; ++j) {
-        const f32x4 wv = *reinterpret_cast<const f32x4*>(ws + j * C + c);
-        dot[j] = fmaf(wv.x, v.x, dot[j]);
-        dot[j] = fmaf(wv.y, v.y, dot[j]);
-        dot[j] = fmaf(wv.z, v.z, dot[j]);
-        dot[j] = fmaf(wv.w, v.w, dot[j]);
+    for (int u = 0; u < POST_SLAB_F4; ++u) {
+      if (u >= q4) break;
+      const int i = t + u * POST_T, r = i / q4, q = i - r * q4;
+      const int g = row0 + r;
+      buf[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      if (g >= 0 && g < rows) buf[u] = ld4(x + (size_t)g * C + c0 + 4 * q);
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int u = 0; u < POST_SLAB_F4; ++u) {
+      if (u >= q4) break;
+      const int i = t + u * POST_T, r = i / q4, q = i - r * q4;
+      st4(xs + r * ld + 4 * q, buf[u]);
+    }
+  };
+  load(0);
+  for (int c0 = 0; c0 < C; c0 += slab) {
+    store();
+    __syncthreads();
+    if (c0 + slab < C) load(c0 + slab);
+    if (mine) {
+      const float* xr = xs + t * ld;
+      for (int c = 0; c < slab; c += 4) {
+        const f32x4 v = ld4(xr + c);
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+          const f32x4 wv = ld4(ws + j * C + c0 + c);
+          dot[j] = fmaf(wv.x, v.x, dot[j]);
+          dot[j] = fmaf(wv.y, v.y, dot[j]);
+          dot[j] = fmaf(wv.z, v.z, dot[j]);
+          dot[j] = fmaf(wv.w, v.w, dot[j]);
+        }
       }
     }
+    __syncthreads();
+  }
+  if (mine) {
 #pragma unroll
     for (int j = 0; j < K; ++j) ys[t * K + j] = dot[j];
   }
@@ -633,10 +670,11 @@ hipError_t launch_conv_post(const float* x, const float* hin, long long sstride,
                             const float* bias, int C, int k, int rows, int nin, float* pcm, float* pre_tanh,
                             hipStream_t s) {
   if (k == 7 && C % 4 == 0) {
-    const size_t smem7 = ((size_t)7 * C + (size_t)POST_T * 7) * sizeof(float);
+    const int slab = C % 32 == 0 ? 32 : C % 16 == 0 ? 16 : C % 8 == 0 ? 8 : 4;
+    const size_t smem7 = ((size_t)7 * C + (size_t)POST_T * 7 + (size_t)POST_T * (slab + 4)) * sizeof(float);
     if (smem7 > 64 * 1024) return hipErrorInvalidValue;
     hipLaunchKernelGGL(conv_post_rows_kernel<7>, dim3(cdiv(rows, POST_T - 6)), dim3(POST_T), smem7, s, x, hin,
-                       sstride, H, w, bias, C, rows, nin, pcm, pre_tanh);
+                       sstride, H, w, bias, C, slab, rows, nin, pcm, pre_tanh);
     return hipGetLastError();
   }
   const size_t smem = ((size_t)k * C + (size_t)(POST_ROWS + k - 1) * (C + 1)) * sizeof(float);
