@@ -9,7 +9,7 @@ import torch
 
 import synthetic as S
 from oracle import decoder as O
-from tests.gpu_util import PCM_MAX_ABS, REL_L2, check_close, decoder, oracle_stream, run_schedule
+from tests.gpu_util import PCM_MAX_ABS, REL_L2, check_close, decoder, oracle_stream, rel_l2, run_schedule
 from tests.test_gpu_full import HOP, _compare, _warm, golden
 from tests.test_gpu_parity import _stage_names, _tap_rows
 from vocoder_rvq_codebook_amd import binding as vb
@@ -140,19 +140,42 @@ def test_split_refuses_weights_beyond_its_range():
     assert torch.isfinite(pcm).all()
 
 
-def test_fp16_matrix_unit_keeps_subnormal_inputs():
-    """The inputs are split unscaled, so their lo halves are often fp16
-    subnormals: the fp16 matrix product must keep them (and their products)
-    exactly, not flush them."""
-    a = torch.zeros(64, 64, dtype=torch.float16, device="cuda")
-    b = torch.zeros(64, 64, dtype=torch.float16, device="cuda")
-    a[0, 0] = 2.0 ** -20       # subnormal inputs (fp16 normals start at 2^-14)
-    a[1, 1] = 3 * 2.0 ** -24   # the smallest subnormal times 3
-    b[0, 0] = 1.0
-    b[1, 1] = 2.0 ** 8
-    c = torch.matmul(a, b).float()
-    assert c[0, 0].item() == 2.0 ** -20
-    assert c[1, 1].item() == 3 * 2.0 ** -16
+def test_split_kernel_keeps_subnormal_input_halves():
+    """The split GEMM splits its fp32 inputs unscaled, so small activations
+    have fp16-subnormal lo halves: the tiny decoder's embedding sums (std 0.08)
+    feed its pre-conv (64 input channels, a split layer) with more than 90 % of
+    lo halves subnormal.  Through the library's own split kernel, the pre-conv
+    output matches the float64 convolution of the same (bitwise) inputs to
+    fp32 accuracy.  Dropping the subnormal lo halves would move it by 1.6e-4,
+    far past the 2e-6 bar."""
+    model = split(S.TINY)
+    dec, W = decoder(model, 0, 1, 32)
+    codes = S.workload_codes("tiny_b1_t32")
+    T, d = codes.shape[1], model["model_dim"]
+    emb = torch.empty(T * model["embed_dim"], device="cuda")
+    h = torch.empty(T * d, device="cuda")
+    dec.set_tap("embed", emb)
+    dec.set_tap("pre_conv", h)
+    vb.vocoder_profile_begin(dec.handle)
+    run_schedule(dec, codes, [T])
+    prof = vb.vocoder_profile_end(dec.handle)
+    dec.set_tap("embed", None)
+    dec.set_tap("pre_conv", None)
+    assert dec.status() == 0
+    assert _split_launches(prof) > 0
+    e = emb.cpu().numpy().reshape(T, -1)
+    np.testing.assert_array_equal(e, O.rvq_embed_sum(W["codebooks"], codes[0]))
+    hi = e.astype(np.float16).astype(np.float32)
+    lo = (e - hi).astype(np.float16)
+    sub = (lo != 0) & (np.abs(lo.astype(np.float32)) < 2.0 ** -14)
+    assert sub.mean() > 0.9
+    w64, b64 = W["pre_conv.weight"].astype(np.float64), W["pre_conv.bias"].astype(np.float64)
+    ref, _ = O.causal_conv1d(e.astype(np.float64), w64, b64, 1)
+    r = rel_l2(h.cpu().numpy().reshape(T, d), ref)
+    print(f"  split pre-conv rel-L2 {r:.3g}")
+    assert r < 2e-6
+    flushed, _ = O.causal_conv1d(hi.astype(np.float64) + np.where(sub, 0, lo).astype(np.float64), w64, b64, 1)
+    assert rel_l2(flushed, ref) > 20 * 2e-6
 
 
 # ---- the full decoder shape -------------------------------------------------
@@ -244,4 +267,4 @@ def test_split_longform_16_streams_1500_frames_zipf():
     dec.set_tap("pre_tanh", None)
     assert dec.status() == 0
     _compare(torch.cat(pcm0).numpy().astype(np.float64), torch.cat(pre0).numpy().astype(np.float64),
-             golden("qwen3_longform"), "split stream 0 of 16, 1500 frames")
+             golden("qwen3_longform"), "split stream 0 of 16, 1500 frames", 0)
