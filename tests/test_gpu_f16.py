@@ -142,6 +142,13 @@ def test_f16_full_size_250_frames(f16_whole_250):
     check_close(pcm[idx], g16["pcm"], "f16 250 frames pcm vs fp16-operand oracle", rel=F16_FULL_PCM)
     check_close(pre[idx], g64["pre"], "f16 250 frames pre-tanh vs float64 decoder", rel=F16_VS_F64_PRE)
     check_close(pcm[idx], g64["pcm"], "f16 250 frames pcm vs float64 decoder", rel=F16_VS_F64_PCM)
+    # every sample, against both stored decodes
+    for key, ref, bar_pre, bar_pcm in (("fp16-operand oracle", g16, F16_FULL_PRE, F16_FULL_PCM),
+                                       ("float64 decoder", g64, F16_VS_F64_PRE, F16_VS_F64_PCM)):
+        check_close(pre, ref["pre32"].astype(np.float64), f"f16 250 frames pre-tanh vs {key} (every sample)",
+                    rel=bar_pre)
+        check_close(pcm, ref["pcm32"].astype(np.float64), f"f16 250 frames pcm vs {key} (every sample)",
+                    rel=bar_pcm)
     assert abs(np.linalg.norm(pre) / g16["pre_norm"][0] - 1) < F16_FULL_PRE
     assert np.all(np.abs(pcm) <= 1.0)
 

@@ -141,6 +141,10 @@ def test_int8_full_size_250_frames(int8_whole_250):
     idx = g["idx"]
     check_close(pcm[idx], g["pcm"], "int8 250 frames pcm", rel=REL_L2, max_abs=PCM_MAX_ABS)
     check_close(pre[idx], g["pre"], "int8 250 frames pre-tanh", rel=REL_L2)
+    # every sample
+    check_close(pcm, g["pcm32"].astype(np.float64), "int8 250 frames pcm (every sample)", rel=REL_L2,
+                max_abs=PCM_MAX_ABS)
+    check_close(pre, g["pre32"].astype(np.float64), "int8 250 frames pre-tanh (every sample)", rel=REL_L2)
     assert abs(np.linalg.norm(pre) / g["pre_norm"][0] - 1) < 1e-5
 
 
