@@ -73,38 +73,73 @@ __device__ __forceinline__ float gelu1(float v) {
 __device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 __device__ __forceinline__ void st4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
 
-// Epilogue of output rows m..m+3 (GEMM columns) of GEMM row g, given the
-// reduced sum `acc`: bias, activation, residual, multi-receptive-field mean,
-// then up to four stores, each optionally through Snake and each optionally
-// also written to the stream's state tail.  Shared by the GEMM and the
-// split-K reduction, so both give the same bits.  Returns the first output's
-// value (as stored when it is fp32).
-__device__ __forceinline__ f32x4 epilogue4(const ConvParams& p, int m, int g, f32x4 acc) {
+// Values of the epilogue of output rows m..m+3 (GEMM columns) of GEMM row g
+// read from tensors other than the GEMM's own: the residual and the
+// multi-receptive-field partial sums.  Loaded apart from the arithmetic so
+// that a thread can issue the loads of several elements before its first
+// store (a store may alias any of them, so the compiler keeps them in order).
+struct EpiLoads {
+  f32x4 resid, mrf, mrf2;
+};
+
+__device__ __forceinline__ size_t epi_oidx(const ConvParams& p, int m, int g) {
+  const int ph = m / p.cout;
+  return ((size_t)g * p.phases + ph) * p.cout + (m - ph * p.cout);
+}
+
+__device__ __forceinline__ EpiLoads epilogue_loads(const ConvParams& p, int m, int g) {
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  const size_t oidx = epi_oidx(p, m, g);
+  const int mrf_mode = p.mrf_mode;
+  EpiLoads e;
+  e.resid = p.resid ? ld4(p.resid + oidx) : z;
+  e.mrf = (mrf_mode == MRF_ACCUM || mrf_mode == MRF_LAST) ? ld4(p.mrf + oidx) : z;
+  e.mrf2 = (mrf_mode == MRF_LAST && p.mrf2) ? ld4(p.mrf2 + oidx) : z;
+  return e;
+}
+
+// Per-column parameters (bias; each output's Snake alpha) read from the
+// weights in global memory.
+struct EpiColsGlobal {
+  const ConvParams& p;
+  int m;
+  __device__ __forceinline__ f32x4 bias() const { return ld4(p.bias + m); }
+  __device__ __forceinline__ f32x4 alpha(int o) const { return ld4(p.out[o].alpha + m); }
+};
+
+// Epilogue of output rows m..m+3 of GEMM row g, given the reduced sum `acc`
+// and the loaded values `e`: bias, activation, residual, multi-receptive-
+// field mean, then up to four stores, each optionally through Snake and each
+// optionally also written to the stream's state tail.  Shared by the GEMM
+// and the split-K reduction, so both give the same bits.  Returns the first
+// output's value (as stored when it is fp32).
+template <class Cols>
+__device__ __forceinline__ f32x4 epilogue_apply(const ConvParams& p, int m, int g, f32x4 acc, const EpiLoads& e,
+                                                const Cols& cols) {
   const int nout_rows = p.nin * p.phases;
   const int ph = m / p.cout;
   const int c = m - ph * p.cout;
-  f32x4 v = acc * p.acc_scale + ld4(p.bias + m);
+  f32x4 v = acc * p.acc_scale + cols.bias();
   if (p.act == ACT_GELU) {
     v.x = gelu1(v.x); v.y = gelu1(v.y); v.z = gelu1(v.z); v.w = gelu1(v.w);
   }
   const size_t orow = (size_t)g * p.phases + ph;
   const size_t oidx = orow * p.cout + c;
-  if (p.resid) v = v + ld4(p.resid + oidx);
+  if (p.resid) v = v + e.resid;
   f32x4 sm = v;
   // (fields read into scalars first: reading them in place let the optimizer
   // copy part of the argument block to private memory in some kernels)
   const int mrf_mode = p.mrf_mode;
-  const float* mrf = p.mrf;
   const float* mrf2 = p.mrf2;
   const float mrf_div = p.mrf_div;
   if (mrf_mode == MRF_FIRST) {
     sm = v;
   } else if (mrf_mode == MRF_ACCUM) {
-    sm = ld4(mrf + oidx) + v;
+    sm = e.mrf + v;
   } else if (mrf_mode == MRF_LAST) {
     // ((block 0 + block 1) + this block): the order of the running sum
-    f32x4 acc = ld4(mrf + oidx);
-    if (mrf2) acc = acc + ld4(mrf2 + oidx);
+    f32x4 acc = e.mrf;
+    if (mrf2) acc = acc + e.mrf2;
     sm = (acc + v) / mrf_div;
   } else if (mrf_mode == MRF_ONLY) {
     sm = v / mrf_div;
@@ -118,7 +153,7 @@ __device__ __forceinline__ f32x4 epilogue4(const ConvParams& p, int m, int g, f3
     const EpiOut& eo = p.out[o];
     f32x4 val = eo.src ? sm : v;
     if (eo.alpha) {
-      const f32x4 a = ld4(eo.alpha + m);
+      const f32x4 a = cols.alpha(o);
       val.x = snake1(val.x, a.x); val.y = snake1(val.y, a.y);
       val.z = snake1(val.z, a.z); val.w = snake1(val.w, a.w);
     }
@@ -135,6 +170,10 @@ __device__ __forceinline__ f32x4 epilogue4(const ConvParams& p, int m, int g, f3
     if (o == 0) first = val;
   }
   return first;
+}
+
+__device__ __forceinline__ f32x4 epilogue4(const ConvParams& p, int m, int g, f32x4 acc) {
+  return epilogue_apply(p, m, g, acc, epilogue_loads(p, m, g), EpiColsGlobal{p, m});
 }
 
 // Reduction values per accumulation group (see the two-level accumulation
@@ -159,16 +198,34 @@ __device__ __forceinline__ f32x4 fold_groups(const ConvParams& p, int m, int g, 
   return acc;
 }
 
+// Per-column parameters staged in LDS by epilogue_tile: row 0 the bias, row
+// 1 + o output o's Snake alpha, BM floats each, for the tile's columns.
+struct EpiColsLds {
+  const float* P;
+  int c;   // column within the tile
+  int bm;  // floats per row
+  __device__ __forceinline__ f32x4 bias() const { return ld4(P + c); }
+  __device__ __forceinline__ f32x4 alpha(int o) const { return ld4(P + (1 + o) * bm + c); }
+};
+
+// LDS floats epilogue_tile needs: the [BN][BM] tile and 5 rows of BM column
+// parameters.
+template <class C>
+constexpr int epi_lds_floats() { return C::BM * C::BN + 5 * C::BM; }
+
 // Epilogue of a whole tile through LDS.  The accumulators go to an fp32
 // [BN][BM] tile in LDS (16-byte chunks of 4 GEMM columns, chunk c of row r
 // stored at c ^ (r & 7): conflict-free both for the fragment writes, 8 rows
-// of one chunk, and for the row reads, 8 chunks of one row); then thread t
-// runs the epilogue of chunks t, t + NT, ... in row-major order, so a wave's
-// loads and stores cover whole rows instead of 16-row columns.  Each element
-// gets the same epilogue on the same value: the same bits as epilogue4 called
-// from the fragments.  The caller has synchronised the block: T may overwrite
-// LDS that every wave has finished reading.
-template <class C>
+// of one chunk, and for the row reads, 8 chunks of one row), and the tile's
+// bias and Snake alphas to 5 rows after it; then thread t runs the epilogue
+// of chunks t, t + NT, ... in row-major order, so a wave's loads and stores
+// cover whole rows instead of 16-row columns.  The chunks are taken in
+// batches of up to MAXB: every residual and multi-receptive-field load of a
+// batch is issued before its first store, so a batch waits on memory once.
+// Each element gets the same epilogue on the same values: the same bits as
+// epilogue4 called from the fragments.  The caller has synchronised the
+// block: LDS may be overwritten once every wave has finished reading it.
+template <class C, int MAXB = 4>
 __device__ __forceinline__ void epilogue_tile(const ConvParams& p, float* T, const f32x4 (&acc)[C::FM][C::FN],
                                               int m0, int g0, int wm, int wn, int lane, int tid) {
   constexpr int CH = C::BM / 4;
@@ -182,11 +239,48 @@ __device__ __forceinline__ void epilogue_tile(const ConvParams& p, float* T, con
       const int c = (wm * C::WTM + i * 16) / 4 + q;
       st4(T + (r * CH + (c ^ (r & 7))) * 4, acc[i][j]);
     }
+  if constexpr (MAXB == 1) {
+    // one chunk at a time, column parameters read from the weights
+    __syncthreads();
+    for (int idx = tid; idx < C::BN * CH; idx += C::NT) {
+      const int r = idx / CH, c = idx - r * CH;
+      const int g = g0 + r, m = m0 + 4 * c;
+      if (g < p.rows && m < p.M) epilogue4(p, m, g, ld4(T + (r * CH + (c ^ (r & 7))) * 4));
+    }
+    return;
+  }
+  float* P = T + C::BM * C::BN;
+#pragma unroll
+  for (int o = 0; o < 5; ++o) {
+    const float* src = o == 0 ? p.bias : (o - 1 < p.nout ? p.out[o - 1].alpha : nullptr);
+    if (!src) continue;
+    for (int c = tid; c < CH; c += C::NT)
+      if (m0 + 4 * c < p.M) st4(P + o * C::BM + 4 * c, ld4(src + m0 + 4 * c));
+  }
   __syncthreads();
-  for (int idx = tid; idx < C::BN * CH; idx += C::NT) {
-    const int r = idx / CH, c = idx - r * CH;
-    const int g = g0 + r, m = m0 + 4 * c;
-    if (g < p.rows && m < p.M) epilogue4(p, m, g, ld4(T + (r * CH + (c ^ (r & 7))) * 4));
+  constexpr int ITERS = (C::BN * CH + C::NT - 1) / C::NT;
+  constexpr int NB = (ITERS + MAXB - 1) / MAXB;  // batches
+  constexpr int EB = (ITERS + NB - 1) / NB;  // chunks per batch
+#pragma unroll
+  for (int u0 = 0; u0 < ITERS; u0 += EB) {
+    EpiLoads e[EB];
+    bool on[EB];
+#pragma unroll
+    for (int u = 0; u < EB; ++u) {
+      const int idx = tid + (u0 + u) * C::NT;
+      const int r = idx / CH, c = idx - r * CH;
+      const int g = g0 + r, m = m0 + 4 * c;
+      on[u] = u0 + u < ITERS && idx < C::BN * CH && g < p.rows && m < p.M;
+      if (on[u]) e[u] = epilogue_loads(p, m, g);
+    }
+#pragma unroll
+    for (int u = 0; u < EB; ++u) {
+      if (!on[u]) continue;
+      const int idx = tid + (u0 + u) * C::NT;
+      const int r = idx / CH, c = idx - r * CH;
+      epilogue_apply(p, m0 + 4 * c, g0 + r, ld4(T + (r * CH + (c ^ (r & 7))) * 4), e[u],
+                     EpiColsLds{P, 4 * c, C::BM});
+    }
   }
 }
 
@@ -201,7 +295,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(4))) void
   // double-buffered A and B tiles; after the K loop the same LDS holds the
   // epilogue's [BN][BM] tile
   constexpr int AB_FLOATS = 2 * (C::BM + C::BN) * C::LDK;
-  constexpr int T_FLOATS = SPLIT ? 0 : C::BM * C::BN;
+  constexpr int T_FLOATS = SPLIT ? 0 : epi_lds_floats<C>();
   __shared__ __attribute__((aligned(16))) float smem[AB_FLOATS > T_FLOATS ? AB_FLOATS : T_FLOATS];
   constexpr int A_OFF = 0, B_OFF = 2 * C::BM * C::LDK;  // buffer b of A at A_OFF + b * BM * LDK
 
@@ -855,7 +949,8 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_f16_dma_kernel(const ConvPara
   constexpr int B_LANES = B_PER_WAVE >= 64 ? 64 : B_PER_WAVE;
   static_assert(B_SLOTS % C::WAVES == 0 && (B_PER_WAVE <= 64 || B_PER_WAVE % 64 == 0), "B chunks per wave");
   constexpr int OPS = A_PLANES + B_DMAS;  // vector-memory operations per wave per K-step (at least)
-  __shared__ __attribute__((aligned(16))) char lds[C::NS * STAGE];
+  constexpr int LDS_BYTES = C::NS * STAGE > epi_lds_floats<C>() * 4 ? C::NS * STAGE : epi_lds_floats<C>() * 4;
+  __shared__ __attribute__((aligned(16))) char lds[SPLIT ? C::NS * STAGE : LDS_BYTES];
   const _Float16* W = reinterpret_cast<const _Float16*>(p.w);
 
   const int tid = threadIdx.x;
@@ -1088,9 +1183,9 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_f16_dma_kernel(const ConvPara
 
   // every wave has left the K loop (no LDS reads or loads outstanding): the
   // ring becomes the epilogue's tile
-  static_assert(C::BN * C::BM * 4 <= C::NS * STAGE, "epilogue tile fits the ring");
   __syncthreads();
-  epilogue_tile<C>(p, reinterpret_cast<float*>(lds), acc, m0, g0, wm, wn, lane, tid);
+  // (the split's registers leave no room for a batch: one chunk at a time)
+  epilogue_tile<C, X3 ? 1 : 4>(p, reinterpret_cast<float*>(lds), acc, m0, g0, wm, wn, lane, tid);
 }
 
 template <class C, bool HALF, bool Q8>
