@@ -180,6 +180,10 @@ bool gemm_f16_direct(bool int8, int cin, int tile);
 // normalise each row in one kernel (the same bits as the reduction followed
 // by the LayerNorm kernel); null otherwise.
 hipError_t launch_conv_gemm(const ConvParams& p, int tile, hipStream_t s, const LnArgs* ln = nullptr);
+// Few-row fp32 GEMM (at most 16 GEMM rows, cin a multiple of 16, float or
+// int8 weights): whether a launch fits it.
+bool conv_gemm_rows_ok(const ConvParams& p);
+hipError_t launch_conv_gemm_rows(const ConvParams& p, hipStream_t s);
 // fp16-operand GEMM: p.w points at fp16 weights [Mpad][k][cin]; tiles 128x128, 96x128, 64x64
 hipError_t launch_conv_gemm_f16(const ConvParams& p, int tile, hipStream_t s, const LnArgs* ln = nullptr);
 // split-fp16 GEMM (fp32 accuracy from three fp16 products per pair): p.w and

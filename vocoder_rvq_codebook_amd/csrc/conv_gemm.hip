@@ -20,9 +20,11 @@
 // folds them in order, so results are bitwise independent of batch, chunking,
 // tile shape and split.
 
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
+
 
 namespace {
 
@@ -530,6 +532,84 @@ __global__ __launch_bounds__(64 * NV) void splitk_reduce_ln_kernel(const ConvPar
   f32x4 v = {0.f, 0.f, 0.f, 0.f};
   if (m < p.M) v = epilogue4(p, m, g, fold_groups(p, m, g, ngroups));
   layernorm_block<NV>(ln, v, g, red);
+}
+
+// ---------------------------------------------------------------------------
+// Few-row GEMM (at most 16 GEMM rows: the transformer, upsampling and conv_pre
+// linears of short chunks), fp32.  These launches stream their weights once
+// and do almost no arithmetic.  A block owns 16 output columns (M) and every
+// accumulation group of them; wave w computes groups w, w + waves, ...,
+// reading its weight rows straight from global memory into MFMA operand
+// registers (no LDS staging; 8 16-wide slabs of loads in flight, 4 for int8
+// weights), and stores each group's partial sum to LDS.  After one barrier
+// the first wave sums the partials in group order from zero and runs the
+// epilogue: no split-K partials in HBM and no fold launch.  Operands, MFMAs
+// and their order are those of conv_gemm_kernel (lane l holds A[l%16][k] and
+// B[k][l%16] for the 4 consecutive k of lane group l/16 in a 16-wide slab,
+// the slab's 4 MFMAs take them in turn, each group's chain starts from
+// zero), and the fold is fold_groups': the same bits as every other tile.
+// ---------------------------------------------------------------------------
+template <bool Q8>
+__global__ __launch_bounds__(1024) void conv_gemm_rows_kernel(const ConvParams p, int ngroups) {
+  constexpr int SLABS = Q8 ? 4 : 8;  // 16-wide slabs of loads in flight per wave
+  extern __shared__ f32x4 red[];     // [ngroups][64]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int m0 = blockIdx.x * 16;
+  const int lr = lane & 15, lk = (lane >> 4) * 4;
+  const int cin = p.cin, ktaps = p.k, dil = p.dil;
+  const int K = ktaps * cin;
+  // B: this lane's GEMM row (rows past the end clamp to the last row; their
+  // outputs are never stored), and its history row for taps that reach
+  // before the chunk
+  const int g = min(lr, p.rows - 1);
+  const int b = g / p.nin;
+  const int n = g - b * p.nin;
+  const float* bx = p.x + (size_t)g * cin + lk;
+  const float* bh = p.hin ? p.hin + (size_t)b * p.sstride + (ptrdiff_t)(p.hin_rows + n) * cin + lk : bx;
+  // A: weight row m0 + lr (packed rows are padded to a multiple of 128)
+  const size_t arow = (size_t)(m0 + lr) * K + lk;
+  const float* wa = p.w + arow;
+  const int8_t* wq = reinterpret_cast<const int8_t*>(p.w) + arow;
+  const _Float16* wsc = reinterpret_cast<const _Float16*>(p.wscale) + (size_t)(m0 + lr) * (K / 32);
+
+  for (int grp = wave; grp < ngroups; grp += nw) {
+    const int k0 = grp * GROUP_K;
+    const int nslab = (min(k0 + GROUP_K, K) - k0) / 16;
+    f32x4 part;
+    for (int s0 = 0; s0 < nslab; s0 += SLABS) {
+      f32x4 a[SLABS], bv[SLABS];
+#pragma unroll
+      for (int u = 0; u < SLABS; ++u) {
+        if (s0 + u >= nslab) break;
+        const int kb = k0 + (s0 + u) * 16;  // a slab lies inside one tap (cin % 16 == 0)
+        const int tap = kb / cin;
+        const int shift = (ktaps - 1 - tap) * dil;
+        if constexpr (Q8)
+          a[u] = dequant4(*reinterpret_cast<const int*>(wq + kb), (float)wsc[(kb + lk) >> 5]);
+        else
+          a[u] = ld4(wa + kb);
+        bv[u] = ld4((n >= shift ? bx : bh) + (kb - tap * cin) - (ptrdiff_t)shift * cin);
+      }
+#pragma unroll
+      for (int u = 0; u < SLABS; ++u) {
+        if (s0 + u >= nslab) break;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (s0 + u == 0 && q == 0)
+            part = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u][q], bv[u][q], (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          else
+            part = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u][q], bv[u][q], part, 0, 0, 0);
+        }
+      }
+    }
+    red[grp * 64 + lane] = part;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < ngroups; ++j) acc += red[j * 64 + lane];
+  const int m = m0 + lk;
+  if (m < p.M && lr < p.rows) epilogue4(p, m, lr, acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -1347,9 +1427,10 @@ hipError_t launch_blocks_f16(const ConvParams& p, int tile, hipStream_t s) {
        : bk == 32 ? launch_cfg<TileCfgH<BM, BN, WM, WN, 32, 32, IG>, true>(p, s)                    \
                   : launch_cfg<TileCfgH<BM, BN, WM, WN, 16, 16, -1>, true>(p, s)
   if (gemm_f16_direct(p.wscale != nullptr, p.cin, tile)) {
-    // direct-to-LDS loads, 4 (fp16 rows) or 3 (fp32 rows) K-steps in flight
+    // direct-to-LDS loads, 4 (128x128 with fp16 rows) or 3 K-steps in flight
+    // (the 96x128 tile with fp16 rows measured 0.8 % faster with 3 than 4)
     if (tile == TILE_128x128) return launch_dma<TileCfgD<128, 128, 2, 4, 4>, TileCfgD<128, 128, 2, 4, 3>>(p, s);
-    return launch_dma<TileCfgD<96, 128, 2, 4, 4>, TileCfgD<96, 128, 2, 4, 3>>(p, s);
+    return launch_dma<TileCfgD<96, 128, 2, 4, 3>, TileCfgD<96, 128, 2, 4, 3>>(p, s);
   }
   switch (tile) {
     case TILE_128x128:
@@ -1391,6 +1472,24 @@ hipError_t launch_gemm(const ConvParams& p, int tile, bool half, hipStream_t s, 
 
 hipError_t launch_conv_gemm(const ConvParams& p, int tile, hipStream_t s, const LnArgs* ln) {
   return launch_gemm(p, tile, false, s, ln);
+}
+
+bool conv_gemm_rows_ok(const ConvParams& p) {
+  if (p.rows < 1 || p.rows > 16 || p.cin % 16 != 0 || p.M % 4 != 0 || p.x_half || p.w_lo) return false;
+  const long long ngroups = ((long long)p.k * p.cin + GROUP_K - 1) / GROUP_K;
+  return ngroups * 64 * 16 <= 64 * 1024;
+}
+
+hipError_t launch_conv_gemm_rows(const ConvParams& p, hipStream_t s) {
+  if (!conv_gemm_rows_ok(p)) return hipErrorInvalidValue;
+  const int ngroups = (p.k * p.cin + GROUP_K - 1) / GROUP_K;
+  const dim3 grid((unsigned)((p.M + 15) / 16)), block(64 * std::min(ngroups, 16));
+  const size_t smem = (size_t)ngroups * 64 * sizeof(f32x4);
+  if (p.wscale)
+    hipLaunchKernelGGL((conv_gemm_rows_kernel<true>), grid, block, smem, s, p, ngroups);
+  else
+    hipLaunchKernelGGL((conv_gemm_rows_kernel<false>), grid, block, smem, s, p, ngroups);
+  return hipGetLastError();
 }
 
 hipError_t launch_conv_gemm_f16(const ConvParams& p, int tile, hipStream_t s, const LnArgs* ln) {

@@ -680,6 +680,20 @@ int run_gemm(const Ctx& cx, const ConvParams& pin, const LnArgs* ln = nullptr) {
   const int bm = gemm_tile_bm(tile);
   const int mt = (p.M + bm - 1) / bm;
   const bool f16 = cx.v->P.f16;
+  if (!f16 && !x3 && !ln && conv_gemm_rows_ok(p)) {
+    // few rows (short chunks): one launch, no split-K partials, the same bits.
+    // (A launch whose output feeds a LayerNorm keeps the split-K path, whose
+    // fold normalises: measured faster than this kernel plus a LayerNorm.)
+    if (p.hin_rows < (p.k - 1) * p.dil) return VOCODER_EINVAL;
+    const double K = (double)p.k * p.cin;
+    double bytes = (p.wscale ? 1.0625 : 4.0) * p.M * K + 4.0 * p.rows * K;
+    for (int o = 0; o < p.nout; ++o)
+      if (p.out[o].dst) bytes += (p.out[o].half ? 2.0 : 4.0) * (double)p.rows * p.M;
+    if (p.resid) bytes += 4.0 * p.rows * p.M;
+    Prof pr(cx.v, cx.s, p.wscale ? "conv_gemm_rows16_q8" : "conv_gemm_rows16", 2.0 * p.M * K * p.rows, bytes);
+    HIP_OK(launch_conv_gemm_rows(p, cx.s));
+    return VOCODER_OK;
+  }
   if (p.wscale && cx.wdeq && (tile == TILE_128x128 || tile == TILE_96x128)) {
     // int8 weights of a many-row launch: expand the layer once into the
     // workspace (q * scale, rounded to fp16 in fp16 mode, exactly what the
