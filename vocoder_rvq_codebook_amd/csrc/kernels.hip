@@ -275,6 +275,138 @@ __global__ __launch_bounds__(ATT_THREADS) void attention_kernel(
   }
 }
 
+// The same attention for a compile-time head size HD (a multiple of 4), with
+// the compute loops vectorised: key rows padded to HD + 4 floats so that a
+// lane reads its key in 16-byte pieces, and each wave's softmax weights
+// staged in LDS so that the value loop reads them as broadcasts instead of
+// lane shuffles, with a fixed trip count.  Every score, max, sum and
+// accumulation takes the same operations in the same order as
+// attention_kernel: the same bits.
+template <int HD>
+__global__ __launch_bounds__(ATT_THREADS) void attention_hd_kernel(
+    const float* __restrict__ qkv, const float* __restrict__ ks, const float* __restrict__ vs, long long sstride,
+    const int* __restrict__ pos, int T, int n_heads, int W, const float* __restrict__ tab,
+    float* __restrict__ ks_out, float* __restrict__ vs_out, float* __restrict__ out) {
+  static_assert(HD % 8 == 0 && HD <= 256, "head size");
+  constexpr int LDK = HD + 4;
+  constexpr int NU = (HD + 63) / 64;  // output channels per lane
+  extern __shared__ float smem[];
+  const int d = n_heads * HD;
+  const int t0 = blockIdx.x * ATT_QT, h = blockIdx.y, b = blockIdx.z;
+  const int p0 = pos[b];
+  const int nq = min(ATT_QT, T - t0);
+  const int nk = nq + W;
+  const int es = (W + 4) & ~3;            // softmax weights per wave (W + 1, rounded up to 4)
+  float* Ks = smem;                       // [(QT + W)][LDK]
+  float* Vs = Ks + (ATT_QT + W) * LDK;    // [(QT + W)][HD]
+  float* Qs = Vs + (ATT_QT + W) * HD;     // [QT][HD]
+  float* Es = Qs + ATT_QT * HD;           // [waves][es]
+  const int tid = threadIdx.x;
+  constexpr int half = HD / 2, half4 = half / 4;
+  for (int idx = tid; idx < nk * half4; idx += ATT_THREADS) {
+    const int r = idx / half4, c = (idx - r * half4) * 4;
+    const int j = t0 + r;  // concat index: j < W state row, else new frame j - W
+    f32x4 k1 = {0.f, 0.f, 0.f, 0.f}, k2 = k1, v1 = k1, v2 = k1;
+    if (j < W) {
+      if (p0 - W + j >= 0) {
+        const size_t o = (size_t)b * sstride + (size_t)j * d + h * HD + c;
+        k1 = *reinterpret_cast<const f32x4*>(ks + o);
+        k2 = *reinterpret_cast<const f32x4*>(ks + o + half);
+        v1 = *reinterpret_cast<const f32x4*>(vs + o);
+        v2 = *reinterpret_cast<const f32x4*>(vs + o + half);
+      }
+    } else if (j - W < T) {
+      const int t = j - W;
+      const size_t grow = (size_t)b * T + t;
+      const float* row = qkv + grow * 3 * d + h * HD + c;
+      k1 = *reinterpret_cast<const f32x4*>(row + d);
+      k2 = *reinterpret_cast<const f32x4*>(row + d + half);
+      v1 = *reinterpret_cast<const f32x4*>(row + 2 * d);
+      v2 = *reinterpret_cast<const f32x4*>(row + 2 * d + half);
+      rope4(k1, k2, tab, grow, half, c);
+      if (W > 0 && t >= t0 && t < t0 + nq && t >= T - W) {
+        const size_t o = (size_t)b * sstride + (size_t)(W - T + t) * d + h * HD + c;
+        *reinterpret_cast<f32x4*>(ks_out + o) = k1;
+        *reinterpret_cast<f32x4*>(ks_out + o + half) = k2;
+        *reinterpret_cast<f32x4*>(vs_out + o) = v1;
+        *reinterpret_cast<f32x4*>(vs_out + o + half) = v2;
+      }
+    }
+    *reinterpret_cast<f32x4*>(Ks + r * LDK + c) = k1;
+    *reinterpret_cast<f32x4*>(Ks + r * LDK + c + half) = k2;
+    *reinterpret_cast<f32x4*>(Vs + r * HD + c) = v1;
+    *reinterpret_cast<f32x4*>(Vs + r * HD + c + half) = v2;
+  }
+  for (int idx = tid; idx < nq * half4; idx += ATT_THREADS) {
+    const int r = idx / half4, c = (idx - r * half4) * 4;
+    const size_t grow = (size_t)b * T + t0 + r;
+    const float* row = qkv + grow * 3 * d + h * HD + c;
+    f32x4 q1 = *reinterpret_cast<const f32x4*>(row);
+    f32x4 q2 = *reinterpret_cast<const f32x4*>(row + half);
+    rope4(q1, q2, tab, grow, half, c);
+    *reinterpret_cast<f32x4*>(Qs + r * HD + c) = q1;
+    *reinterpret_cast<f32x4*>(Qs + r * HD + c + half) = q2;
+  }
+  __syncthreads();
+  const int lane = tid & 63, wave = tid >> 6;
+  const float scale = 1.0f / sqrtf((float)HD);
+  float* Ew = Es + wave * es;
+  for (int tl = wave; tl < nq; tl += ATT_THREADS / 64) {
+    const long long P = (long long)p0 + t0 + tl;
+    const f32x4* q4 = reinterpret_cast<const f32x4*>(Qs + tl * HD);
+    float e[4];
+    float m = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int o = lane + 64 * u;
+      e[u] = -INFINITY;
+      if (o <= W && P - W + o >= 0) {
+        const f32x4* k4 = reinterpret_cast<const f32x4*>(Ks + (tl + o) * LDK);
+        float sc = 0.f;
+#pragma unroll
+        for (int c4 = 0; c4 < HD / 4; ++c4) {
+          const f32x4 qq = q4[c4], kk = k4[c4];
+          sc += qq.x * kk.x;
+          sc += qq.y * kk.y;
+          sc += qq.z * kk.z;
+          sc += qq.w * kk.w;
+        }
+        e[u] = sc * scale;
+        m = fmaxf(m, e[u]);
+      }
+    }
+    m = wave_max(m);
+    float part = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int o = lane + 64 * u;
+      e[u] = (o <= W && P - W + o >= 0) ? expf(e[u] - m) : 0.f;
+      part += e[u];
+      if (o <= W) Ew[o] = e[u];
+    }
+    const float denom = wave_sum(part);
+    float acc[NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) acc[u] = 0.f;
+    const float* vrow = Vs + tl * HD;
+#pragma unroll 8
+    for (int o = 0; o <= W; ++o) {
+      const float pw = Ew[o];
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const int c = lane + 64 * u;
+        if (c < HD) acc[u] += pw * vrow[o * HD + c];
+      }
+    }
+    float* orow = out + ((size_t)b * T + t0 + tl) * d + h * HD;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int c = lane + 64 * u;
+      if (c < HD) orow[c] = acc[u] / denom;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Final conv C -> 1 (kernel k, causal, history from the state) and tanh.
 // A block owns POST_ROWS consecutive output samples: it stages those input
@@ -655,9 +787,33 @@ hipError_t launch_layernorm(const float* x, const float* g, const float* b, floa
   return hipGetLastError();
 }
 
+template <int HD>
+hipError_t launch_attention_hd(const float* qkv, const float* k_state, const float* v_state, long long sstride,
+                               const int* pos, int batch, int T, int n_heads, int W, const float* rope_tab,
+                               float* k_state_out, float* v_state_out, float* out, hipStream_t s) {
+  const size_t smem = ((size_t)(ATT_QT + W) * (HD + 4) + (size_t)(ATT_QT + W) * HD + (size_t)ATT_QT * HD +
+                       (size_t)(ATT_THREADS / 64) * ((W + 4) & ~3)) *
+                      sizeof(float);
+  if (smem > 64 * 1024 || W > 255) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(attention_hd_kernel<HD>, dim3(cdiv(T, ATT_QT), n_heads, batch), dim3(ATT_THREADS), smem, s, qkv,
+                     k_state, v_state, sstride, pos, T, n_heads, W, rope_tab, k_state_out, v_state_out, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_attention(const float* qkv, const float* k_state, const float* v_state, long long sstride,
                             const int* pos, int batch, int T, int n_heads, int hd, int W, const float* rope_tab,
                             float* k_state_out, float* v_state_out, float* out, hipStream_t s) {
+  switch (hd) {
+    case 16: return launch_attention_hd<16>(qkv, k_state, v_state, sstride, pos, batch, T, n_heads, W, rope_tab,
+                                            k_state_out, v_state_out, out, s);
+    case 32: return launch_attention_hd<32>(qkv, k_state, v_state, sstride, pos, batch, T, n_heads, W, rope_tab,
+                                            k_state_out, v_state_out, out, s);
+    case 64: return launch_attention_hd<64>(qkv, k_state, v_state, sstride, pos, batch, T, n_heads, W, rope_tab,
+                                            k_state_out, v_state_out, out, s);
+    case 128: return launch_attention_hd<128>(qkv, k_state, v_state, sstride, pos, batch, T, n_heads, W, rope_tab,
+                                              k_state_out, v_state_out, out, s);
+    default: break;
+  }
   const size_t smem = ((size_t)(ATT_QT + W) * (hd + 1) + (size_t)(ATT_QT + W) * hd + (size_t)ATT_QT * hd) *
                       sizeof(float);
   if (smem > 64 * 1024 || hd % 8) return hipErrorInvalidValue;
