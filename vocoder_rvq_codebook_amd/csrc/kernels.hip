@@ -85,8 +85,23 @@ __global__ void state_shift_kernel(const Slot* __restrict__ slots, const float* 
 // ---------------------------------------------------------------------------
 // RVQ gather-sum: e[row] = sum over q (ascending) of codebooks[q][codes[row][q]],
 // one fp32 add per codebook.  A code outside [0, V) flags the status word and
-// contributes nothing (its row is never read).
+// contributes nothing.  With Q a multiple of 8 the codebooks are taken 8 at a
+// time, branch-free: their 8 codes in two 16-byte loads, then the 8 codeword
+// pieces (an out-of-range code reads row 0 of its codebook, in bounds, and
+// its value is dropped), then the adds in order; a row waits on memory twice
+// per 8 codebooks instead of twice per codebook.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ void gather_add(f32x4& e, f32x4 w, int q) {
+  if (q == 0) {
+    e = w;
+  } else {
+    e.x = __fadd_rn(e.x, w.x);
+    e.y = __fadd_rn(e.y, w.y);
+    e.z = __fadd_rn(e.z, w.z);
+    e.w = __fadd_rn(e.w, w.w);
+  }
+}
+
 __global__ void gather_kernel(const int32_t* __restrict__ codes, const float* __restrict__ cb, int Q, int V,
                               int D, int rows, int T, float* __restrict__ out, float* __restrict__ hist, int H,
                               long long sstride, int* __restrict__ status) {
@@ -98,20 +113,34 @@ __global__ void gather_kernel(const int32_t* __restrict__ codes, const float* __
   const int32_t* cr = codes + (size_t)row * Q;
   f32x4 e = {0.f, 0.f, 0.f, 0.f};
   bool bad = false;
-  for (int q = 0; q < Q; ++q) {
-    const int code = cr[q];
-    if (code < 0 || code >= V) {
-      bad = true;
-      continue;
+  if (Q % 8 == 0) {
+    for (int q0 = 0; q0 < Q; q0 += 8) {
+      const int4 c0 = *reinterpret_cast<const int4*>(cr + q0);
+      const int4 c1 = *reinterpret_cast<const int4*>(cr + q0 + 4);
+      const int code[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      bool ok[8];
+      f32x4 w[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        ok[u] = code[u] >= 0 && code[u] < V;
+        w[u] = ld4(cb + ((size_t)(q0 + u) * V + (ok[u] ? code[u] : 0)) * D + c);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (ok[u])
+          gather_add(e, w[u], q0 + u);
+        else
+          bad = true;
+      }
     }
-    const f32x4 w = ld4(cb + ((size_t)q * V + code) * D + c);
-    if (q == 0) {
-      e = w;
-    } else {
-      e.x = __fadd_rn(e.x, w.x);
-      e.y = __fadd_rn(e.y, w.y);
-      e.z = __fadd_rn(e.z, w.z);
-      e.w = __fadd_rn(e.w, w.w);
+  } else {
+    for (int q = 0; q < Q; ++q) {
+      const int code = cr[q];
+      if (code < 0 || code >= V) {
+        bad = true;
+        continue;
+      }
+      gather_add(e, ld4(cb + ((size_t)q * V + code) * D + c), q);
     }
   }
   if (bad && c == 0) atomicOr(status, VOC_STATUS_CODE);
