@@ -70,12 +70,15 @@ DTYPES = {"f32": "f32", "f16": "f16", "split": "f16x3"}
 
 def _kernel_family(name):
     import re
-    # direct-to-LDS fp16 GEMM: TileCfgD<BM, BN, waves_m, waves_n, stages>, split-K, fp16 rows[, split fp16]
-    m = re.search(r"TileCfgD<(\d+), (\d+), \d+, \d+, \d+>, (true|false), (?:true|false)(, true)?", name)
+    # direct-to-LDS fp16 GEMM: TileCfgD<BM, BN, waves_m, waves_n, stages>, split-K, fp16 rows[, split fp16[,
+    # slab windows]]
+    m = re.search(r"TileCfgD<(\d+), (\d+), \d+, \d+, \d+>, (true|false), (?:true|false)(?:, (true|false))?"
+                  r"(?:, (true|false))?", name)
     if m:
         split = "_splitk" if m.group(3) == "true" else ""
-        kind = "x3" if m.group(4) else "f16_dma"
-        return f"conv_gemm_{kind}_{m.group(1)}x{m.group(2)}_bk32{split}"
+        kind = "x3" if m.group(4) == "true" else "f16_dma"
+        win = "_win" if m.group(5) == "true" else ""
+        return f"conv_gemm_{kind}_{m.group(1)}x{m.group(2)}_bk32{split}{win}"
     m = re.search(r"TileCfg(H?)<(\d+), (\d+), \d+, \d+, (\d+)(?:, -?\d+)*\s*>(?:, (true|false))?"
                   r"(?:, (true|false))?", name)
     if m:

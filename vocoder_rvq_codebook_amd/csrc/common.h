@@ -175,6 +175,9 @@ int gemm_tile_bk(int tile, int cin, bool half);
 // the fp16-operand GEMM of this tile loads its operands straight into LDS
 // (float or fp16 weights, channel count a multiple of 32, 128x128 or 96x128)
 bool gemm_f16_direct(bool int8, int cin, int tile);
+// ... and stages each 32-channel slab's input rows once for all its taps
+// (fp16 rows, k >= 3, unsplit, history in the state; p.splits already set)
+bool gemm_f16_window(const ConvParams& p, int tile);
 // ln: for a split launch (p.splits > 1) whose first output (fp32, one phase,
 // M = ln.d) feeds a LayerNorm, fold the partials, run the epilogue and
 // normalise each row in one kernel (the same bits as the reduction followed

@@ -225,11 +225,12 @@ constexpr int epi_lds_floats() { return C::BM * C::BN + 5 * C::BM; }
 // batches of up to MAXB: every residual and multi-receptive-field load of a
 // batch is issued before its first store, so a batch waits on memory once.
 // Each element gets the same epilogue on the same values: the same bits as
-// epilogue4 called from the fragments.  The caller has synchronised the
-// block: LDS may be overwritten once every wave has finished reading it.
+// epilogue4 called from the fragments.  Rows from g_end on are not written.
+// The caller has synchronised the block: LDS may be overwritten once every
+// wave has finished reading it.
 template <class C, int MAXB = 4>
 __device__ __forceinline__ void epilogue_tile(const ConvParams& p, float* T, const f32x4 (&acc)[C::FM][C::FN],
-                                              int m0, int g0, int wm, int wn, int lane, int tid) {
+                                              int m0, int g0, int g_end, int wm, int wn, int lane, int tid) {
   constexpr int CH = C::BM / 4;
   static_assert(CH % 8 == 0, "row chunks: a multiple of 8");
   const int lr = lane & 15, q = lane >> 4;
@@ -247,7 +248,7 @@ __device__ __forceinline__ void epilogue_tile(const ConvParams& p, float* T, con
     for (int idx = tid; idx < C::BN * CH; idx += C::NT) {
       const int r = idx / CH, c = idx - r * CH;
       const int g = g0 + r, m = m0 + 4 * c;
-      if (g < p.rows && m < p.M) epilogue4(p, m, g, ld4(T + (r * CH + (c ^ (r & 7))) * 4));
+      if (g < g_end && m < p.M) epilogue4(p, m, g, ld4(T + (r * CH + (c ^ (r & 7))) * 4));
     }
     return;
   }
@@ -272,7 +273,7 @@ __device__ __forceinline__ void epilogue_tile(const ConvParams& p, float* T, con
       const int idx = tid + (u0 + u) * C::NT;
       const int r = idx / CH, c = idx - r * CH;
       const int g = g0 + r, m = m0 + 4 * c;
-      on[u] = u0 + u < ITERS && idx < C::BN * CH && g < p.rows && m < p.M;
+      on[u] = u0 + u < ITERS && idx < C::BN * CH && g < g_end && m < p.M;
       if (on[u]) e[u] = epilogue_loads(p, m, g);
     }
 #pragma unroll
@@ -502,7 +503,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(4))) void
   if (SPLIT) return;
 
   // (the K loop ended on a block barrier: every wave is done with As and Bs)
-  epilogue_tile<C>(p, smem, acc, m0, g0, wm, wn, lane, tid);
+  epilogue_tile<C>(p, smem, acc, m0, g0, p.rows, wm, wn, lane, tid);
 }
 
 // Fold the split-K group partials of one output element (4 consecutive M)
@@ -967,6 +968,16 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
 // slots are masked), so a wave's vmcnt tells when its own share of a stage has
 // landed; a barrier then makes every wave's share visible.  History rows of
 // an fp16 input come from the fp32 state and are converted through registers.
+//
+// WIN (fp16 rows, no split, k >= 3): the K-steps of one 32-channel slab are
+// its k taps, and tap t of output row r reads input row r + t*dil of the
+// window that starts (k-1)*dil rows before the tile.  So each slab's window,
+// BN + (k-1)*dil rows of 32 halves, is staged once (two window buffers, slab
+// parity) and each tap reads its rows at offset t*dil; only the weights go
+// through the per-step ring.  That holds while every row of the tile belongs
+// to one stream, so these tiles never cross a stream: each stream's rows are
+// covered by their own ceil(nin / BN) tiles.  The MFMA operands and their
+// order are unchanged, hence the bits.
 // ---------------------------------------------------------------------------
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int NS_>
 struct TileCfgD {
@@ -1009,7 +1020,24 @@ __device__ __forceinline__ void wait_vm_lgkm() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
 }
 
+// the same for a wave-uniform count n, 0 <= n <= N
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm_upto(int n) {
+  if constexpr (N > 0) {
+    if (n >= N) {
+      wait_vm_lgkm<N>();
+      return;
+    }
+    wait_vm_lgkm_upto<N - 1>(n);
+  } else {
+    wait_vm_lgkm<0>();
+  }
+}
+
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// rows of halo a window may carry: (k-1)*dil at most
+constexpr int WIN_HALO = 64;
 
 // X3: split-fp16 operands (fp32 rows only).  The weights come as hi and lo
 // fp16 planes w1 + w2 (of the weights times a power of two), both staged.
@@ -1017,20 +1045,26 @@ __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "
 // x2 = fp16(x - x1).  Every fragment pair takes three MFMAs into the same
 // accumulator, always in this order: w2 x1, w1 x2, w1 x1 (w2 x2, below 2^-22
 // of the product, is dropped); the epilogue scales the sum back.
-template <class C, bool SPLIT, bool XH, bool X3 = false>
+template <class C, bool SPLIT, bool XH, bool X3 = false, bool WIN = false>
 __global__ __launch_bounds__(C::NT) void conv_gemm_f16_dma_kernel(const ConvParams p) {
   static_assert(!(X3 && XH), "the split takes fp32 rows");
+  static_assert(!WIN || (XH && !SPLIT && !X3 && C::NS <= 4), "windows: fp16 rows, whole K, k >= NS - 1");
   constexpr int A_BYTES = C::A_SLOTS * 16;
   constexpr int A_PLANES = X3 ? 2 : 1;
-  constexpr int STAGE = C::template stage_bytes<XH>() + (A_PLANES - 1) * A_BYTES;
+  constexpr int STAGE = WIN ? A_BYTES : C::template stage_bytes<XH>() + (A_PLANES - 1) * A_BYTES;
+  constexpr int WROWS = C::BN + WIN_HALO;               // window rows at most
+  constexpr int WIN_BYTES = WROWS * 64;                 // 32 halves a row
+  constexpr int WD = (WROWS * 4 + C::NT - 1) / C::NT;  // window loads per wave per slab, at most
+  constexpr int WOFF = C::NS * STAGE;                   // window buffers after the ring
+  constexpr int RING = WOFF + (WIN ? 2 * WIN_BYTES : 0);
   constexpr int B_SLOTS = C::template b_slots<XH>();
   constexpr int B_PER_WAVE = C::template b_per_wave<XH>();
   constexpr int B_DMAS = B_PER_WAVE >= 64 ? B_PER_WAVE / 64 : 1;  // loads per wave per K-step
   constexpr int B_LANES = B_PER_WAVE >= 64 ? 64 : B_PER_WAVE;
   static_assert(B_SLOTS % C::WAVES == 0 && (B_PER_WAVE <= 64 || B_PER_WAVE % 64 == 0), "B chunks per wave");
   constexpr int OPS = A_PLANES + B_DMAS;  // vector-memory operations per wave per K-step (at least)
-  constexpr int LDS_BYTES = C::NS * STAGE > epi_lds_floats<C>() * 4 ? C::NS * STAGE : epi_lds_floats<C>() * 4;
-  __shared__ __attribute__((aligned(16))) char lds[SPLIT ? C::NS * STAGE : LDS_BYTES];
+  constexpr int LDS_BYTES = RING > epi_lds_floats<C>() * 4 ? RING : epi_lds_floats<C>() * 4;
+  __shared__ __attribute__((aligned(16))) char lds[SPLIT ? RING : LDS_BYTES];
   const _Float16* W = reinterpret_cast<const _Float16*>(p.w);
 
   const int tid = threadIdx.x;
@@ -1055,7 +1089,15 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_f16_dma_kernel(const ConvPara
   const int mt = tile_id % mtiles;
   const int nt = tile_id / mtiles;
   const int m0 = mt * C::BM;
-  const int g0 = nt * C::BN;
+  int g0 = nt * C::BN, g_end = p.rows;
+  int wstream = 0, wn0 = 0;  // WIN: the tile's stream and its first row in it
+  if (WIN) {
+    const int tpb = (p.nin + C::BN - 1) / C::BN;
+    wstream = nt / tpb;
+    wn0 = (nt - wstream * tpb) * C::BN;
+    g0 = wstream * p.nin + wn0;
+    g_end = (wstream + 1) * p.nin;
+  }
 
   const int cin = p.cin;
   const int ktaps = p.k, dil = p.dil;
@@ -1104,6 +1146,35 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_f16_dma_kernel(const ConvPara
     bh[h] = p.hin ? p.hin + (size_t)b * p.sstride + (ptrdiff_t)(p.hin_rows + n) * cin + col
                   : reinterpret_cast<const float*>(bx[h]);
   }
+  // WIN: a wave's loads of a slab window are the 64-chunk pieces wave,
+  // wave + WAVES, ... of its (BN + halo) * 4 chunks; chunk i holds (swizzled
+  // as the B tiles) a piece of window row i / 4, frame wn0 + i / 4 - halo of
+  // the tile's stream
+  const int halo = (ktaps - 1) * dil;
+  const int wchunks = (C::BN + halo) * 4;
+  const bool whist = wn0 < halo;  // some window rows come from the state
+  const _Float16* wx[WD];
+  const float* wh[WD];
+  bool wx_on[WD], w_on[WD];
+  int wcount = 0;
+  if (WIN) {
+#pragma unroll
+    for (int h = 0; h < WD; ++h) {
+      const int piece = wave + h * C::WAVES;
+      const int idx = piece * 64 + lane;
+      if (piece * 64 < wchunks) wcount = h + 1;
+      w_on[h] = idx < wchunks;
+      const int j = min(idx, wchunks - 1) >> 2;
+      const int c = (idx & 3) ^ ((j >> 1) & 3);
+      const int n = wn0 + j - halo;
+      wx_on[h] = n >= 0;
+      // rows past the stream's end feed only rows the epilogue drops
+      wx[h] = reinterpret_cast<const _Float16*>(p.x) + ((size_t)wstream * p.nin + min(max(n, 0), p.nin - 1)) * cin + c * 8;
+      wh[h] = p.hin ? p.hin + (size_t)wstream * p.sstride + (ptrdiff_t)(p.hin_rows + min(n, -1)) * cin + c * 8
+                    : nullptr;
+    }
+    wcount = __builtin_amdgcn_readfirstlane(wcount);
+  }
 
   // issue the loads of K-step s into ring stage st.  Channel-major K order
   // (one 32-channel slab of one tap per step), as conv_gemm_f16_kernel; steps
@@ -1118,8 +1189,32 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_f16_dma_kernel(const ConvPara
     }
     const int shift = (ktaps - 1 - tap) * dil;
     const uint32_t sbase = (uint32_t)(st * STAGE);
+    if constexpr (WIN) {
+      // a slab's window goes with its first tap, before that step's weights
+      if (tap == 0) {
+        const uint32_t wbase = lds0 + WOFF + (uint32_t)((c0 / C::BK) & 1) * WIN_BYTES;
+#pragma unroll
+        for (int h = 0; h < WD; ++h) {
+          if (h >= wcount) break;
+          const uint32_t dst = wbase + (uint32_t)(wave + h * C::WAVES) * 1024;
+          if (!w_on[h]) continue;
+          if (wx_on[h]) {
+            lds_dma16(wx[h] + c0, dst);
+          } else {
+            const float* src = wh[h] + c0;
+            const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
+            const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 4);
+            *reinterpret_cast<f16x8*>(lds + (dst - lds0) + lane * 16) = to_half8(lo, hi);
+          }
+        }
+        // a tile with state rows drains its loads here, so the counts the
+        // K loop waits for still bound what is in flight
+        if (whist) wait_vm_lgkm<0>();
+      }
+    }
     // weights packed in the same slab order: step s is slab s
     if (a_on) lds_dma16(a_src + (ptrdiff_t)s * C::BK, a_dst + sbase);
+    if constexpr (WIN) return;
     if (X3 && a_on) lds_dma16(a_lo_src + (ptrdiff_t)s * C::BK, a_dst + sbase + A_BYTES);
 #pragma unroll
     for (int h = 0; h < B_DMAS; ++h) {
@@ -1154,7 +1249,8 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_f16_dma_kernel(const ConvPara
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  auto mma_step = [&](int st, f32x4 (&part)[C::FM][C::FN], auto first) __attribute__((always_inline)) {
+  // (wrd: WIN, byte offset of this lane's first B fragment in the window)
+  auto mma_step = [&](int st, f32x4 (&part)[C::FM][C::FN], auto first, int wrd) __attribute__((always_inline)) {
     const char* S = lds + st * STAGE;
     f16x8 af[C::FM], bf[C::FN];
     f16x8 al[X3 ? C::FM : 1];  // weight lo halves (split)
@@ -1165,7 +1261,9 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_f16_dma_kernel(const ConvPara
     }
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) {
-      if constexpr (XH) {
+      if constexpr (WIN) {
+        bf[j] = *reinterpret_cast<const f16x8*>(lds + wrd + j * 16 * 64);
+      } else if constexpr (XH) {
         bf[j] = *reinterpret_cast<const f16x8*>(S + b_rd + j * 16 * 64);
       } else if constexpr (!X3) {  // (the split reads its B fragments below)
         const f32x4 lo = *reinterpret_cast<const f32x4*>(S + b_rd0 + j * 16 * 128);
@@ -1216,6 +1314,7 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_f16_dma_kernel(const ConvPara
     if (s_begin + t < nsteps) issue(s_begin + t, t);
 
   int st = 0;  // ring stage of step s
+  int m_tap = 0, m_cb = 0;  // WIN: tap and slab of step s (no split: s_begin = 0)
   for (int gs = s_begin; gs < nsteps; gs += GROUP_STEPS) {
     const int ge = min(gs + GROUP_STEPS, nsteps);
     f32x4 part[C::FM][C::FN];
@@ -1223,7 +1322,20 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_f16_dma_kernel(const ConvPara
       // this wave's loads of step s have landed once at most (steps issued
       // after it) x OPS operations remain; then every wave's have
       const int later = min(C::NS - 2, nsteps - 1 - s);
-      if constexpr (C::NS >= 4) {
+      int wrd = 0;
+      if constexpr (WIN) {
+        // issued after step s's weights: the weights of `later` steps, and
+        // the window of a slab whose first tap is among them (k >= NS - 1:
+        // one at most)
+        const int nafter = later + (later >= 1 && ktaps - m_tap <= later ? wcount : 0);
+        wait_vm_lgkm_upto<C::NS - 2 + WD>(__builtin_amdgcn_readfirstlane(nafter));
+        const int row0 = wn * C::WTN + lr + m_tap * dil;
+        wrd = WOFF + (m_cb & 1) * WIN_BYTES + (row0 * 4 + (q ^ ((row0 >> 1) & 3))) * 16;
+        if (++m_tap == ktaps) {
+          m_tap = 0;
+          ++m_cb;
+        }
+      } else if constexpr (C::NS >= 4) {
         if (later >= 2) wait_vm_lgkm<2 * OPS>();
         else if (later == 1) wait_vm_lgkm<OPS>();
         else wait_vm_lgkm<0>();
@@ -1235,9 +1347,9 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_f16_dma_kernel(const ConvPara
       // refill the stage every wave finished reading at step s - 1
       if (s + C::NS - 1 < nsteps) issue(s + C::NS - 1, st == 0 ? C::NS - 1 : st - 1);
       if (s == gs)
-        mma_step(st, part, std::true_type{});
+        mma_step(st, part, std::true_type{}, wrd);
       else
-        mma_step(st, part, std::false_type{});
+        mma_step(st, part, std::false_type{}, wrd);
       st = st == C::NS - 1 ? 0 : st + 1;
     }
     if (SPLIT) {
@@ -1265,7 +1377,7 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_f16_dma_kernel(const ConvPara
   // ring becomes the epilogue's tile
   __syncthreads();
   // (the split's registers leave no room for a batch: one chunk at a time)
-  epilogue_tile<C, X3 ? 1 : 4>(p, reinterpret_cast<float*>(lds), acc, m0, g0, wm, wn, lane, tid);
+  epilogue_tile<C, X3 ? 1 : 4>(p, reinterpret_cast<float*>(lds), acc, m0, g0, g_end, wm, wn, lane, tid);
 }
 
 template <class C, bool HALF, bool Q8>
@@ -1314,12 +1426,32 @@ hipError_t launch_fold(const ConvParams& p, hipStream_t s, const LnArgs* ln) {
   return hipGetLastError();
 }
 
+// Slab windows (WIN) for fp16 rows: whole K, k >= 3 taps with at most
+// WIN_HALO rows of history that the state holds, whole streams, and per-stream
+// tiles that waste at most 1/16 of their rows.
+bool dma_win_ok(const ConvParams& p, int bn) {
+  if (!p.x_half || p.w_lo || p.splits > 1 || p.k < 3 || p.dil < 1 || p.nin < 1 || p.rows % p.nin != 0) return false;
+  const int halo = (p.k - 1) * p.dil;
+  if (halo > WIN_HALO || !p.hin || p.hin_rows < halo) return false;
+  const long long tpb = (p.nin + bn - 1) / bn;
+  return tpb * bn * 16 <= (long long)p.nin * 17;
+}
+
 template <class C, bool XH, bool X3 = false>
 hipError_t launch_dma_x(const ConvParams& p, hipStream_t s) {
   const int mtiles = (p.M + C::BM - 1) / C::BM;
   const int ntiles = (p.rows + C::BN - 1) / C::BN;
   const long long tiles = (long long)mtiles * ntiles;
   if (tiles <= 0) return hipSuccess;
+  if constexpr (XH && !X3) {
+    if (dma_win_ok(p, C::BN)) {
+      const long long wt = (long long)mtiles * (p.rows / p.nin) * ((p.nin + C::BN - 1) / C::BN);
+      if (wt > 0x7fffffffLL) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((conv_gemm_f16_dma_kernel<C, false, true, false, true>), dim3((unsigned)wt), dim3(C::NT), 0,
+                         s, p);
+      return hipGetLastError();
+    }
+  }
   if (p.splits <= 1) {
     if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL((conv_gemm_f16_dma_kernel<C, false, XH, X3>), dim3((unsigned)tiles), dim3(C::NT), 0, s, p);
@@ -1375,6 +1507,10 @@ int half_bk(int cin) { return cin % 64 == 0 ? 64 : cin % 32 == 0 ? 32 : 16; }
 
 bool gemm_f16_direct(bool int8, int cin, int tile) {
   return !int8 && cin % 32 == 0 && (tile == TILE_128x128 || tile == TILE_96x128);
+}
+
+bool gemm_f16_window(const ConvParams& p, int tile) {
+  return gemm_f16_direct(p.wscale != nullptr, p.cin, tile) && dma_win_ok(p, gemm_tile_bn(tile));
 }
 
 int gemm_tile_bk(int tile, int cin, bool half) {
