@@ -83,7 +83,8 @@ def test_hot_gemm_tiles_keep_four_waves_per_simd(gemm_asm):
            if re.search(r"TileCfgD?ILi(96|128)ELi128E", k) and ("conv_gemm_kernel" in k or "dma_kernel" in k)}
     assert len(hot) >= 16, sorted(regs)
     for k, v in hot.items():
-        split_128 = "dma_kernel" in k and "ILi128ELi128E" in k and k.endswith("ELb0ELb0ELb1EEEv10ConvParams")
+        # <split-K = false, fp16 rows = false, split fp16 = true[, windows = false]>
+        split_128 = "dma_kernel" in k and "ILi128ELi128E" in k and re.search(r"ELb0ELb0ELb1E(?:Lb0E)?EEv10ConvParams$", k)
         if split_128:
             continue
         assert v <= 128, f"{k}: {v} registers per lane (more than 128 halves the blocks per CU)"

@@ -972,9 +972,10 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
 // WIN (fp16 rows, no split, k >= 3): the K-steps of one 32-channel slab are
 // its k taps, and tap t of output row r reads input row r + t*dil of the
 // window that starts (k-1)*dil rows before the tile.  So each slab's window,
-// BN + (k-1)*dil rows of 32 halves, is staged once (two window buffers, slab
-// parity) and each tap reads its rows at offset t*dil; only the weights go
-// through the per-step ring.  That holds while every row of the tile belongs
+// BN + (k-1)*dil rows of 32 halves, is staged once (in buffer slab % WNB) and
+// each tap reads its rows at offset t*dil; only the weights go through the
+// per-step ring.  A window is loaded NS - 1 steps ahead, over the buffer of
+// slab - WNB, whose last tap every wave has passed once (WNB - 1) * k >= NS - 1.  That holds while every row of the tile belongs
 // to one stream, so these tiles never cross a stream: each stream's rows are
 // covered by their own ceil(nin / BN) tiles.  The MFMA operands and their
 // order are unchanged, hence the bits.
@@ -1048,7 +1049,9 @@ constexpr int WIN_HALO = 64;
 template <class C, bool SPLIT, bool XH, bool X3 = false, bool WIN = false>
 __global__ __launch_bounds__(C::NT) void conv_gemm_f16_dma_kernel(const ConvParams p) {
   static_assert(!(X3 && XH), "the split takes fp32 rows");
-  static_assert(!WIN || (XH && !SPLIT && !X3 && C::NS <= 4), "windows: fp16 rows, whole K, k >= NS - 1");
+  // (k >= 3 taps: WNB = 2 buffers serve NS <= 4, 3 serve NS <= 7)
+  static_assert(!WIN || (XH && !SPLIT && !X3 && C::NS <= 7), "windows: fp16 rows, whole K");
+  constexpr int WNB = C::NS <= 4 ? 2 : 3;
   constexpr int A_BYTES = C::A_SLOTS * 16;
   constexpr int A_PLANES = X3 ? 2 : 1;
   constexpr int STAGE = WIN ? A_BYTES : C::template stage_bytes<XH>() + (A_PLANES - 1) * A_BYTES;
@@ -1056,7 +1059,7 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_f16_dma_kernel(const ConvPara
   constexpr int WIN_BYTES = WROWS * 64;                 // 32 halves a row
   constexpr int WD = (WROWS * 4 + C::NT - 1) / C::NT;  // window loads per wave per slab, at most
   constexpr int WOFF = C::NS * STAGE;                   // window buffers after the ring
-  constexpr int RING = WOFF + (WIN ? 2 * WIN_BYTES : 0);
+  constexpr int RING = WOFF + (WIN ? WNB * WIN_BYTES : 0);
   constexpr int B_SLOTS = C::template b_slots<XH>();
   constexpr int B_PER_WAVE = C::template b_per_wave<XH>();
   constexpr int B_DMAS = B_PER_WAVE >= 64 ? B_PER_WAVE / 64 : 1;  // loads per wave per K-step
@@ -1192,7 +1195,7 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_f16_dma_kernel(const ConvPara
     if constexpr (WIN) {
       // a slab's window goes with its first tap, before that step's weights
       if (tap == 0) {
-        const uint32_t wbase = lds0 + WOFF + (uint32_t)((c0 / C::BK) & 1) * WIN_BYTES;
+        const uint32_t wbase = lds0 + WOFF + (uint32_t)((c0 / C::BK) % WNB) * WIN_BYTES;
 #pragma unroll
         for (int h = 0; h < WD; ++h) {
           if (h >= wcount) break;
@@ -1325,12 +1328,13 @@ __global__ __launch_bounds__(C::NT) void conv_gemm_f16_dma_kernel(const ConvPara
       int wrd = 0;
       if constexpr (WIN) {
         // issued after step s's weights: the weights of `later` steps, and
-        // the window of a slab whose first tap is among them (k >= NS - 1:
-        // one at most)
-        const int nafter = later + (later >= 1 && ktaps - m_tap <= later ? wcount : 0);
-        wait_vm_lgkm_upto<C::NS - 2 + WD>(__builtin_amdgcn_readfirstlane(nafter));
+        // the windows of the slabs whose first tap is among them (later <= 5
+        // and k >= 3: two at most)
+        const int starts = (m_tap + later >= ktaps) + (m_tap + later >= 2 * ktaps);
+        const int nafter = later + starts * wcount;
+        wait_vm_lgkm_upto<C::NS - 2 + 2 * WD>(__builtin_amdgcn_readfirstlane(nafter));
         const int row0 = wn * C::WTN + lr + m_tap * dil;
-        wrd = WOFF + (m_cb & 1) * WIN_BYTES + (row0 * 4 + (q ^ ((row0 >> 1) & 3))) * 16;
+        wrd = WOFF + (m_cb % WNB) * WIN_BYTES + (row0 * 4 + (q ^ ((row0 >> 1) & 3))) * 16;
         if (++m_tap == ktaps) {
           m_tap = 0;
           ++m_cb;
@@ -1437,17 +1441,18 @@ bool dma_win_ok(const ConvParams& p, int bn) {
   return tpb * bn * 16 <= (long long)p.nin * 17;
 }
 
-template <class C, bool XH, bool X3 = false>
+template <class C, bool XH, bool X3 = false, class CW = C>
 hipError_t launch_dma_x(const ConvParams& p, hipStream_t s) {
   const int mtiles = (p.M + C::BM - 1) / C::BM;
   const int ntiles = (p.rows + C::BN - 1) / C::BN;
   const long long tiles = (long long)mtiles * ntiles;
   if (tiles <= 0) return hipSuccess;
   if constexpr (XH && !X3) {
-    if (dma_win_ok(p, C::BN)) {
-      const long long wt = (long long)mtiles * (p.rows / p.nin) * ((p.nin + C::BN - 1) / C::BN);
+    static_assert(CW::BM == C::BM && CW::BN == C::BN, "window tile");
+    if (dma_win_ok(p, CW::BN)) {
+      const long long wt = (long long)mtiles * (p.rows / p.nin) * ((p.nin + CW::BN - 1) / CW::BN);
       if (wt > 0x7fffffffLL) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((conv_gemm_f16_dma_kernel<C, false, true, false, true>), dim3((unsigned)wt), dim3(C::NT), 0,
+      hipLaunchKernelGGL((conv_gemm_f16_dma_kernel<CW, false, true, false, true>), dim3((unsigned)wt), dim3(CW::NT), 0,
                          s, p);
       return hipGetLastError();
     }
@@ -1463,10 +1468,10 @@ hipError_t launch_dma_x(const ConvParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// fp16 rows (CH) or fp32 rows (CF) as the B operand
-template <class CH, class CF>
+// fp16 rows (CH; CW with slab windows) or fp32 rows (CF) as the B operand
+template <class CH, class CF, class CW>
 hipError_t launch_dma(const ConvParams& p, hipStream_t s) {
-  return p.x_half ? launch_dma_x<CH, true>(p, s) : launch_dma_x<CF, false>(p, s);
+  return p.x_half ? launch_dma_x<CH, true, false, CW>(p, s) : launch_dma_x<CF, false>(p, s);
 }
 
 // int8 weights (p.wscale set) or float weights
@@ -1564,9 +1569,12 @@ hipError_t launch_blocks_f16(const ConvParams& p, int tile, hipStream_t s) {
                   : launch_cfg<TileCfgH<BM, BN, WM, WN, 16, 16, -1>, true>(p, s)
   if (gemm_f16_direct(p.wscale != nullptr, p.cin, tile)) {
     // direct-to-LDS loads, 4 (128x128 with fp16 rows) or 3 K-steps in flight
-    // (the 96x128 tile with fp16 rows measured 0.8 % faster with 3 than 4)
-    if (tile == TILE_128x128) return launch_dma<TileCfgD<128, 128, 2, 4, 4>, TileCfgD<128, 128, 2, 4, 3>>(p, s);
-    return launch_dma<TileCfgD<96, 128, 2, 4, 3>, TileCfgD<96, 128, 2, 4, 3>>(p, s);
+    // (the 96x128 tile with fp16 rows measured 0.8 % faster with 3 than 4);
+    // with slab windows 4 in either (5 measured slower: 128 x 128 by 0.3 %,
+    // 96 x 128 by 2.5 %; 4 against 3 for 96 x 128: 1.2 % faster)
+    if (tile == TILE_128x128)
+      return launch_dma<TileCfgD<128, 128, 2, 4, 4>, TileCfgD<128, 128, 2, 4, 3>, TileCfgD<128, 128, 2, 4, 4>>(p, s);
+    return launch_dma<TileCfgD<96, 128, 2, 4, 3>, TileCfgD<96, 128, 2, 4, 3>, TileCfgD<96, 128, 2, 4, 4>>(p, s);
   }
   switch (tile) {
     case TILE_128x128:
