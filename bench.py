@@ -106,9 +106,9 @@ def trace_summary(path, steps):
         a[0] += 1
         a[1] += d
     print(f"last {steps} decode calls of {path}")
-    print(f"{'kernel':28s} {'launches':>9s} {'total ms':>10s} {'avg ms':>9s}")
+    print(f"{'kernel':36s} {'launches':>9s} {'total ms':>10s} {'avg ms':>9s}")
     for k, (n, t) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
-        print(f"{k:28s} {n:9d} {t:10.3f} {t / n:9.4f}")
+        print(f"{k:36s} {n:9d} {t:10.3f} {t / n:9.4f}")
 
 
 def traffic_summary(gemm_fetch, gemm_write, copy_fetch, copy_write, copy_bytes):
@@ -372,6 +372,35 @@ def stream_latency(args, wl, torch, S, Decoder, vb):
     print(json.dumps(out), flush=True)
 
 
+def roofline(name, k, ms, tflops, gbs, mfma_peak, peaks, precision):
+    """Roofline of the dominant kernel family: its bound is the roof with the
+    longer lower-bound time for the family's algorithmic work, its FLOPs at the
+    MFMA peak against its algorithmic bytes at the HBM peak (the bound is
+    "hbm" when the family's FLOPs per byte fall below the ridge point, peak
+    FLOP/s over peak bytes/s); `achieved` and `frac` are that roof's, and the
+    other roof's fraction is reported beside it.  (The split mode's MFMAs run
+    three products per counted one, so its MFMA time is three times its FLOPs
+    at the peak.)"""
+    intensity = k["flops"] / k["bytes"] if k["bytes"] else float("inf")
+    ridge = mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
+    mfma_meas = peaks["mfma_f32_tflops" if precision == "f32" else "mfma_f16_tflops"]
+    if intensity * (3 if precision == "split" else 1) < ridge:
+        r = {"kernel": name, "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(gbs / HBM_PEAK_GBS, 4), "peak_measured": peaks["hbm_read_gbs"],
+             "frac_of_measured": round(gbs / peaks["hbm_read_gbs"], 4),
+             "mfma": {"achieved": round(tflops, 3), "peak": mfma_peak, "unit": "TFLOP/s",
+                      "frac": round(tflops / mfma_peak, 4)}}
+    else:
+        r = {"kernel": name, "bound": "mfma", "achieved": round(tflops, 3), "peak": mfma_peak, "unit": "TFLOP/s",
+             "frac": round(tflops / mfma_peak, 4), "peak_measured": mfma_meas,
+             "frac_of_measured": round(tflops / mfma_meas, 4),
+             "hbm": {"achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+    r.update({"flop_per_byte": round(intensity, 1), "ridge_flop_per_byte": round(ridge, 1),
+              "avg_launch_ms": round(ms, 4), "traffic": traffic_for(name)})
+    return r
+
+
 def traffic_for(kernel):
     """HBM bytes per launch of `kernel` from the committed counter summary, if it
     was taken on the current kernel source; else None."""
@@ -478,6 +507,8 @@ def main():
     dom_name, dom = max(prof.items(), key=lambda kv: kv[1]["total_ms"])
     dom_ms = dom["total_ms"] / dom["launches"]
     dom_tflops = dom["flops"] / dom["launches"] / (dom_ms * 1e-3) / 1e12
+    dom_gbs = dom["bytes"] / dom["launches"] / (dom_ms * 1e-3) / 1e9
+    roof = roofline(dom_name, dom, dom_ms, dom_tflops, dom_gbs, peak, peaks, args.precision)
     kernels = {k: {"launches_per_step": v["launches"] / args.steps, "ms_per_step": v["total_ms"] / args.steps,
                    "tflops": (v["flops"] / (v["total_ms"] * 1e-3) / 1e12) if v["flops"] else None,
                    "gbs": v["bytes"] / (v["total_ms"] * 1e-3) / 1e9}
@@ -506,13 +537,7 @@ def main():
                    "samples_per_frame": dec.hop, "warm_positions": sorted(set(warm))},
         "tflops": round(flops_step / (elapsed / args.steps) / 1e12, 3),
         "mfma_frac": round(flops_step / (elapsed / args.steps) / 1e12 / peak, 4),
-        "roofline": {"kernel": dom_name, "bound": "mfma", "achieved": round(dom_tflops, 3),
-                     "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(dom_tflops / peak, 4),
-                     "peak_measured": peaks["mfma_f32_tflops" if args.precision == "f32" else "mfma_f16_tflops"],
-                     "frac_of_measured": round(dom_tflops / peaks["mfma_f32_tflops" if args.precision == "f32"
-                                                                  else "mfma_f16_tflops"], 4),
-                     "avg_launch_ms": round(dom_ms, 4), "traffic": traffic_for(dom_name)},
+        "roofline": roof,
         "peaks_measured": peaks,
         "kernels": kernels,
     }
