@@ -724,12 +724,14 @@ int run_gemm(const Ctx& cx, const ConvParams& pin, const LnArgs* ln = nullptr) {
   else if (f16) bytes -= 2.0 * p.M * K;             // fp16 weights
   const bool fuse_ln = ln && p.splits > 1;
   if (fuse_ln) bytes += 8.0 * p.rows * ln->d;
-  char name[48];
-  const bool direct = f16 && gemm_f16_direct(p.wscale != nullptr, p.cin, tile);
-  const bool window = direct && gemm_f16_window(p, tile);
-  snprintf(name, sizeof(name), "conv_gemm_%s%s%dx%d_bk%d%s", x3 ? "x3_" : direct ? "f16_dma_" : f16 ? "f16_" : "",
-           p.wscale ? "q8_" : "", bm, gemm_tile_bn(tile), direct || x3 ? 32 : gemm_tile_bk(tile, p.cin, f16),
-           p.splits > 1 ? (fuse_ln ? "_splitk_ln" : "_splitk") : window ? "_win" : "");
+  char name[48] = "";
+  if (cx.v->prof && !cx.v->capturing && !cx.v->no_events) {  // (named only while profiling: host time per launch)
+    const bool direct = f16 && gemm_f16_direct(p.wscale != nullptr, p.cin, tile);
+    const bool window = direct && gemm_f16_window(p, tile);
+    snprintf(name, sizeof(name), "conv_gemm_%s%s%dx%d_bk%d%s", x3 ? "x3_" : direct ? "f16_dma_" : f16 ? "f16_" : "",
+             p.wscale ? "q8_" : "", bm, gemm_tile_bn(tile), direct || x3 ? 32 : gemm_tile_bk(tile, p.cin, f16),
+             p.splits > 1 ? (fuse_ln ? "_splitk_ln" : "_splitk") : window ? "_win" : "");
+  }
   {
     Prof pr(cx.v, cx.s, name, flops, bytes);
     if (x3)
