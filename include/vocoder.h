@@ -165,8 +165,10 @@ typedef struct vocoder vocoder;
  * Returns 0 if the config is invalid. */
 size_t vocoder_raw_weights_count(const vocoder_config* cfg);
 
-/* Bytes of the packed-weight buffer (library-internal layout). 0 if invalid. */
+/* Bytes of the packed-weight buffer (library-internal layout). 0 if invalid.
+ * vocoder_weights_bytes is the same call under a second, shorter name. */
 size_t vocoder_packed_weights_bytes(const vocoder_config* cfg);
+size_t vocoder_weights_bytes(const vocoder_config* cfg);
 
 /* Bytes of the workspace for max_batch streams x max_frames frames (including
  * room for one batch of states, the input copy of an in-place decode).  0 if

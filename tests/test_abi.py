@@ -51,6 +51,7 @@ def test_qwen3_sizes():
     kv = 8 * 2 * 72 * 1024 * 4
     assert kv < st < kv + 2_000_000 and st % 256 == 0
     assert vb.vocoder_packed_weights_bytes(cfg) >= 4 * S.n_params(S.QWEN3)
+    assert vb.vocoder_weights_bytes(cfg) == vb.vocoder_packed_weights_bytes(cfg)
     ws = vb.vocoder_workspace_bytes(cfg)
     assert ws % 256 == 0 and ws > 64 * 25 * 1920 * 96 * 4
 

@@ -88,8 +88,8 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         P = ctypes.POINTER(VocoderConfig)
         vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
-        for name in ("vocoder_raw_weights_count", "vocoder_packed_weights_bytes", "vocoder_workspace_bytes",
-                     "vocoder_state_bytes"):
+        for name in ("vocoder_raw_weights_count", "vocoder_packed_weights_bytes", "vocoder_weights_bytes",
+                     "vocoder_workspace_bytes", "vocoder_state_bytes"):
             getattr(L, name).argtypes = [P]
             getattr(L, name).restype = sz
         L.vocoder_create.argtypes = [P, vp, vp, vp, vp, ctypes.POINTER(vp)]
@@ -194,6 +194,10 @@ def vocoder_raw_weights_count(cfg: VocoderConfig) -> int:
 
 def vocoder_packed_weights_bytes(cfg: VocoderConfig) -> int:
     return lib().vocoder_packed_weights_bytes(ctypes.byref(cfg))
+
+
+def vocoder_weights_bytes(cfg: VocoderConfig) -> int:
+    return lib().vocoder_weights_bytes(ctypes.byref(cfg))
 
 
 def vocoder_workspace_bytes(cfg: VocoderConfig) -> int:

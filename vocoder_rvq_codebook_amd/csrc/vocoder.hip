@@ -842,6 +842,8 @@ size_t vocoder_packed_weights_bytes(const vocoder_config* cfg) {
   return make_plan(cfg, P) ? (size_t)P.packed_floats * 4 : 0;
 }
 
+size_t vocoder_weights_bytes(const vocoder_config* cfg) { return vocoder_packed_weights_bytes(cfg); }
+
 size_t vocoder_workspace_bytes(const vocoder_config* cfg) {
   Plan P;
   return make_plan(cfg, P) ? (size_t)P.ws_floats * 4 : 0;
