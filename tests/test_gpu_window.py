@@ -3,12 +3,14 @@ its taps (the slab windows of conv_gemm_f16_dma_kernel): their tiles cover one
 stream each, and the rows before a stream's first frame come from its state.
 
 A window reads the same fp16 operands as the per-tap kernel and feeds the same
-MFMA sequence, so the bits must not change.  The narrow test decoder (stage-3
-launches of 32 channels) decodes three streams whole, where stage 3 runs in
-windows from zero history, and as 9 + 32 frames, where the 32-frame chunk runs
-in windows whose first tiles read the state the 9-frame chunk wrote.  Each must
-equal a schedule of short chunks that never takes the windows, bit for bit, and
-the last stream must match the oracle's fp16-operand decode.  The profile must
+MFMA sequence, so the bits must not change.  The narrow test decoder (stage-2
+and stage-3 launches of 64 and 32 channels) decodes three streams whole (1968
+stage-3 rows per stream, the last tile of each stream partly idle, zero
+history), as 9 + 32 frames (1536 rows: whole tiles, the first of each stream
+reading the state the 9-frame chunk wrote) and as 10 + 31 frames (1488 rows:
+state rows and a partly idle last tile).  Each must equal a schedule of short
+chunks that never takes the windows, bit for bit, and the last stream must
+match the oracle's fp16-operand decode.  The profile must
 show the window launches, so the path cannot silently go unused."""
 import pytest
 import torch
@@ -38,9 +40,12 @@ def test_f16_slab_windows_bitwise():
     short, st_s, n_short = _profiled(dec, codes, [1, 1, 2, 4, 8, 8, 8, 8, 1])
     whole, st_w, n_whole = _profiled(dec, codes, [T])
     split, st_p, n_split = _profiled(dec, codes, [9, 32])
-    print(f"  window launches: short chunks {n_short}, whole {n_whole}, 9 + 32 {n_split}", flush=True)
-    assert n_short == 0 and n_whole > 0 and n_split > 0
+    cross, st_c, n_cross = _profiled(dec, codes, [10, 31])
+    print(f"  window launches: short chunks {n_short}, whole {n_whole}, 9 + 32 {n_split}, 10 + 31 {n_cross}",
+          flush=True)
+    assert n_short == 0 and n_whole > 0 and n_split > 0 and n_cross > 0
     assert torch.equal(whole, short) and torch.equal(st_w, st_s)
     assert torch.equal(split, short) and torch.equal(st_p, st_s)
+    assert torch.equal(cross, short) and torch.equal(st_c, st_s)
     ref = oracle_stream(model, W, codes[B - 1], [9, 32], operands="f16")
     check_close(split[B - 1].cpu().numpy(), ref, "windowed fp16 stream vs fp16-operand oracle", rel=F16_VS_F16_ORACLE)
