@@ -159,3 +159,40 @@ def test_f16_full_size_streamed_equals_whole(f16_whole_250):
     pcm, _ = run_schedule(dec, codes, S.workload("qwen3_b1_t250_stream")["schedule"])
     assert dec.status() == vb.VOCODER_OK
     assert np.array_equal(pcm[0].cpu().numpy().astype(np.float64), pcm_whole)
+
+
+def test_f16_batched_64_streams_chunk_25():
+    """The fp16 decoder in the benchmark's launch configuration: 64 streams x 25
+    frames after the warm-ups, every BigVGAN stage in slab windows whose first
+    tiles read state rows.  The six stored streams against the float64 decoder
+    at the full-size fp16 bar, every sample; stream 37 decoded alone (other
+    tiles and launches) must equal its batched decode bit for bit."""
+    from tests.test_gpu_full import _warm
+
+    print("\n[f16 full] 64 streams x 25 frames after warm-up", flush=True)
+    model = half(S.QWEN3)
+    dec, _ = decoder(model, 1, 64, 25)
+    codes = S.workload_codes("qwen3_b64_chunk25")
+    warm = [S.batched_warmup_frames(b) for b in range(64)]
+    st = _warm(dec, codes, warm)
+    saved = st.clone()
+    chunk = np.stack([codes[b, warm[b]:warm[b] + 25] for b in range(64)])
+    pre = torch.empty(64 * 25 * model["hop"], device="cuda")
+    dec.set_tap("pre_tanh", pre)
+    vb.vocoder_profile_begin(dec.handle)
+    pcm, _ = run_schedule(dec, chunk, [25], state=st)
+    prof = vb.vocoder_profile_end(dec.handle)
+    dec.set_tap("pre_tanh", None)
+    assert dec.status() == vb.VOCODER_OK
+    assert sum(v.get("launches", 0) for k, v in prof.items() if k.endswith("_win")) > 0, sorted(prof)
+    pcm_np = pcm.cpu().numpy().astype(np.float64)
+    pre_np = pre.view(64, -1).cpu().numpy().astype(np.float64)
+    assert np.isfinite(pcm_np).all() and np.all(np.abs(pcm_np) <= 1.0)
+    g = _golden("qwen3_batched")
+    for k, b in enumerate(g["stream"]):
+        check_close(pre_np[b], g["pre32"][k].astype(np.float64),
+                    f"f16 stream {b} pre-tanh vs float64 decoder (every sample)", rel=F16_VS_F64_PRE)
+        check_close(pcm_np[b], g["pcm32"][k].astype(np.float64),
+                    f"f16 stream {b} pcm vs float64 decoder (every sample)", rel=F16_VS_F64_PCM)
+    alone, _ = run_schedule(dec, chunk[37:38], [25], state=saved[37:38].clone())
+    assert torch.equal(alone[0], pcm[37])
