@@ -285,7 +285,7 @@ def stream_latency(args, wl, torch, S, Decoder, vb):
     pcm = [torch.empty((B, n * dec.hop), device="cuda") for n in sched]
     states = (dec.new_state(B), dec.new_state(B))
     stream = torch.cuda.current_stream()
-    times, pre_times, pre_dec_times = [], [], []
+    times, host_times, pre_times, pre_dec_times = [], [], [], []
 
     def run_prefix(st_a, st_b, decode):
         # the reference prefix into the state: prefill (no audio), or, for
@@ -316,15 +316,19 @@ def stream_latency(args, wl, torch, S, Decoder, vb):
                 pre_dec_times.append(ms)
                 pre_times.append(ms_pre)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(sched) + 1)]
+        host = []
         torch.cuda.synchronize()
         ev[0].record(stream)
         for i, n in enumerate(sched):
+            h0 = time.perf_counter()
             dec.decode(chunks[i], st_a, st_b, pcm[i], graph=args.graph)
+            host.append((time.perf_counter() - h0) * 1e3)
             st_a, st_b = st_b, st_a
             ev[i + 1].record(stream)
         torch.cuda.synchronize()
         if rep >= args.warmup:
             times.append([ev[i].elapsed_time(ev[i + 1]) for i in range(len(sched))])
+            host_times.append(host)
     if dec.status() != vb.VOCODER_OK:
         raise SystemExit("device reported an error")
     kernels = None
@@ -361,6 +365,11 @@ def stream_latency(args, wl, torch, S, Decoder, vb):
            "chunk_ms_median_by_length": {str(n): round(float(np.median(t[:, [i for i, m in enumerate(sched) if m == n]])), 3)
                                          for n in sorted(set(sched))},
            "total_ms_median": round(float(np.median(total)), 3),
+           # host time to enqueue one call (its launches), per chunk length: the
+           # device times above hold while it stays below them
+           "host_enqueue_ms_median_by_length": {
+               str(n): round(float(np.median(np.array(host_times)[:, [i for i, m in enumerate(sched) if m == n]])), 3)
+               for n in sorted(set(sched))},
            "audio_s_per_s": round(audio / (float(np.median(total)) / 1e3), 2),
            "dtype": DTYPES[args.precision], "data": "synthetic"}
     if pre_chunks:
