@@ -164,9 +164,12 @@ def test_binding_rejects_bad_decode_buffers_before_any_call():
 
     kw = dict(n_codebooks=16, state_bytes=512, hop=48, device="cpu", max_batch=4, max_frames=8)
     codes = torch.zeros((2, 3, 16), dtype=torch.int32)
-    st = torch.zeros((4, 512), dtype=torch.uint8)
-    if st.data_ptr() % 256:
-        pytest.skip("host allocation not 256-byte aligned")
+    # the binding wants states on 256-byte boundaries, as device allocations are:
+    # take an aligned view of a larger host buffer
+    raw = torch.zeros(4 * 512 + 256, dtype=torch.uint8)
+    off = -raw.data_ptr() % 256
+    st = raw[off:off + 4 * 512].view(4, 512)
+    assert st.data_ptr() % 256 == 0 and st.is_contiguous()
     st_a, st_b = st[:2], st[2:]
     pcm = torch.zeros((2, 3 * 48))
     vb.check_decode_args(codes, st_a, st_b, pcm, **kw)       # ping-pong
