@@ -1,6 +1,6 @@
 """Throughput of the streaming code2wav decoder on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--precision f32|f16|split] [--weights float|int8] [--graph] [--no-cpu-baseline] [--split-line] [--peaks-only]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--precision f32|f16|split] [--weights float|int8] [--graph] [--no-cpu-baseline] [--split-line] [--peaks-only] [--barrier-probe]
 
 A step decodes one 25-frame chunk (2 s of audio) for each of 64 independent
 streams whose states were first warmed (untimed) to different positions: the
@@ -52,6 +52,9 @@ def parse():
     # measurement helpers (each replaces the timed run)
     ap.add_argument("--peaks-only", action="store_true",
                     help="run only the roofline microbenchmarks (fp32/fp16 MFMA loops, HBM read and copy)")
+    ap.add_argument("--barrier-probe", action="store_true",
+                    help="run only the ordering-point microbenchmarks (a grid-wide barrier inside one kernel "
+                         "against a dependent launch)")
     ap.add_argument("--counters", action="store_true",
                     help="decode exactly one batched step from fresh states, for rocprofv3 --pmc runs")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -199,6 +202,54 @@ def measure_peaks(torch, vb, reps=5):
     torch.cuda.empty_cache()
     res["method"] = (f"register-only MFMA loops ({blocks} workgroups x 4 waves x 4 independent chains), "
                      f"stream read of 2 GiB and copy of 1 GiB (16-byte grid-stride, {rblocks} workgroups); "
+                     f"best of {reps} after a warm-up, HIP events")
+    return res
+
+
+def measure_barrier(torch, vb, rounds=500, launches=1000, reps=3):
+    """The price of one ordering point between dependent steps, measured by
+    the library's microbenchmarks (HIP events on the current stream, best of
+    `reps` after a warm-up): a grid-wide barrier crossed inside one
+    cooperative kernel (2 * rounds barriers per launch, each round checking
+    data written by another block before the barrier), and a dependent launch
+    of an empty kernel."""
+    stream = torch.cuda.current_stream()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    res = {"barrier_us": {}, "method": ""}
+    for blocks in (cus // 4, cus, 2 * cus):
+        flags = torch.zeros(blocks + 1, dtype=torch.int32, device="cuda")
+        slots = torch.empty(blocks * 64, device="cuda")
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        best = None
+        for rep in range(reps + 1):
+            flags.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            rc = vb.vocoder_grid_barrier(flags, slots, err, blocks, rounds)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if rc != vb.VOCODER_OK or int(err.item()) != 0:
+                raise SystemExit(f"vocoder_grid_barrier failed: rc {rc}, err {int(err.item())}")
+            us = 1e3 * e0.elapsed_time(e1) / (2 * rounds)
+            if rep:
+                best = us if best is None else min(best, us)
+        res["barrier_us"][str(blocks)] = round(best, 3)
+    scratch = torch.zeros(2, dtype=torch.int32, device="cuda")
+    best = None
+    for rep in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        if vb.vocoder_empty_launches(scratch, cus, launches) != vb.VOCODER_OK:
+            raise SystemExit("vocoder_empty_launches failed")
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = 1e3 * e0.elapsed_time(e1) / launches
+        if rep:
+            best = us if best is None else min(best, us)
+    res["dependent_launch_us"] = round(best, 3)
+    res["method"] = (f"cooperative grids of {cus // 4}, {cus} and {2 * cus} workgroups x 256 threads, "
+                     f"{2 * rounds} barriers each (a flag per block gathered by block 0, flags and checked data "
+                     f"past the caches); {launches} back-to-back launches of an empty {cus}-workgroup kernel; "
                      f"best of {reps} after a warm-up, HIP events")
     return res
 
@@ -448,6 +499,10 @@ def main():
     if args.peaks_only:
         torch.cuda.set_device(0)
         print(json.dumps({"peaks_measured": measure_peaks(torch, vb)}), flush=True)
+        return
+    if args.barrier_probe:
+        torch.cuda.set_device(0)
+        print(json.dumps({"ordering_point": measure_barrier(torch, vb)}), flush=True)
         return
 
     if args.copy_bytes:

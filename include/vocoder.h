@@ -358,6 +358,26 @@ int vocoder_peak_mfma(int dtype, float* out, int blocks, int iters, void* stream
 int vocoder_stream_read(const float* src, long long n, float* out, int blocks, void* stream);
 int vocoder_stream_copy(const float* src, float* dst, long long n, int blocks, void* stream);
 
+/* The price of an ordering point between dependent steps ("blixt/phonon",
+ * Speed: its note on the cost of an empty dependent dispatch): a grid-wide
+ * barrier inside one kernel, against a launch boundary.
+ * vocoder_grid_barrier: a cooperative grid of `blocks` workgroups of 256
+ * threads (2 <= blocks <= what the GPU holds at once, else VOCODER_EINVAL)
+ * runs `rounds` rounds.  In each round every block writes 64 floats to its
+ * slot of `slots`, crosses a barrier, reads another block's slot and checks it,
+ * and crosses a second barrier: 2 * rounds barriers in all.  A barrier is a
+ * flag per block, gathered by block 0, which then publishes the round; flags
+ * and slots are written and read past the caches.  Device buffers, all the
+ * caller's: `flags` blocks + 1 uint32, zero on entry (the call leaves them
+ * non-zero); `slots` blocks * 64 floats; `err` one int32, zero on entry.
+ * Every wait is bounded: a wait that runs out sets bit 0 of *err (the grid
+ * then drains), and a check that fails sets bit 1.
+ * vocoder_empty_launches: n back-to-back launches of a kernel of `blocks`
+ * workgroups that does nothing observable; `scratch` is 2 device int32 it
+ * reads.  Both enqueue on `stream`.  Errors: VOCODER_EINVAL, VOCODER_EHIP. */
+int vocoder_grid_barrier(unsigned* flags, float* slots, int* err, int blocks, int rounds, void* stream);
+int vocoder_empty_launches(int* scratch, int blocks, int n, void* stream);
+
 /* Free the host handle (device buffers stay the caller's). */
 void vocoder_destroy(vocoder* v);
 

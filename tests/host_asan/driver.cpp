@@ -131,6 +131,11 @@ int main() {
   EXPECT(vocoder_peak_mfma(2, reinterpret_cast<float*>(256), 1, 8, nullptr) == VOCODER_EINVAL);
   EXPECT(vocoder_stream_read(nullptr, 4, nullptr, 1, nullptr) == VOCODER_EINVAL);
   EXPECT(vocoder_stream_copy(nullptr, nullptr, 4, 1, nullptr) == VOCODER_EINVAL);
+  EXPECT(vocoder_grid_barrier(nullptr, nullptr, nullptr, 2, 1, nullptr) == VOCODER_EINVAL);
+  EXPECT(vocoder_grid_barrier(reinterpret_cast<unsigned*>(256), reinterpret_cast<float*>(256),
+                              reinterpret_cast<int*>(256), 1, 1, nullptr) == VOCODER_EINVAL);
+  EXPECT(vocoder_empty_launches(nullptr, 1, 1, nullptr) == VOCODER_EINVAL);
+  EXPECT(vocoder_empty_launches(reinterpret_cast<int*>(256), 1, 0, nullptr) == VOCODER_EINVAL);
   EXPECT(vocoder_peak_mfma_flops(0, 1, 8) == 2.0 * 16 * 16 * 4 * 4 * 4 * 8);
   for (int code = -6; code <= 1; ++code) EXPECT(vocoder_strerror(code) != nullptr);
   vocoder_destroy(nullptr);

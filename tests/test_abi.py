@@ -94,6 +94,9 @@ def test_null_arguments_rejected_before_any_device_call():
     assert L.vocoder_get_status(None, None) == vb.VOCODER_EINVAL
     assert L.vocoder_hop(None) == 0
     assert L.vocoder_set_tap(None, b"embed", None, 0) == vb.VOCODER_EINVAL
+    assert L.vocoder_grid_barrier(None, None, None, 2, 1, None) == vb.VOCODER_EINVAL
+    assert L.vocoder_grid_barrier(256, 256, 256, 1, 1, None) == vb.VOCODER_EINVAL
+    assert L.vocoder_empty_launches(None, 1, 1, None) == vb.VOCODER_EINVAL
     L.vocoder_destroy(None)
     assert vb.vocoder_strerror(vb.VOCODER_ECODE) == "code out of range"
     assert vb.vocoder_strerror(vb.VOCODER_ESTATE).startswith("state")

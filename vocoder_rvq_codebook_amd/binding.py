@@ -130,6 +130,10 @@ def lib():
         L.vocoder_stream_read.restype = i32
         L.vocoder_stream_copy.argtypes = [vp, vp, ctypes.c_longlong, i32, vp]
         L.vocoder_stream_copy.restype = i32
+        L.vocoder_grid_barrier.argtypes = [vp, vp, vp, i32, i32, vp]
+        L.vocoder_grid_barrier.restype = i32
+        L.vocoder_empty_launches.argtypes = [vp, i32, i32, vp]
+        L.vocoder_empty_launches.restype = i32
         L.vocoder_destroy.argtypes = [vp]
         L.vocoder_destroy.restype = None
         L.vocoder_strerror.argtypes = [i32]
@@ -298,6 +302,14 @@ def vocoder_stream_read(src, n: int, out, blocks: int, stream=None) -> int:
 
 def vocoder_stream_copy(src, dst, n: int, blocks: int, stream=None) -> int:
     return lib().vocoder_stream_copy(_ptr(src), _ptr(dst), int(n), int(blocks), _stream(stream))
+
+
+def vocoder_grid_barrier(flags, slots, err, blocks: int, rounds: int, stream=None) -> int:
+    return lib().vocoder_grid_barrier(_ptr(flags), _ptr(slots), _ptr(err), int(blocks), int(rounds), _stream(stream))
+
+
+def vocoder_empty_launches(scratch, blocks: int, n: int, stream=None) -> int:
+    return lib().vocoder_empty_launches(_ptr(scratch), int(blocks), int(n), _stream(stream))
 
 
 def vocoder_destroy(handle) -> None:
