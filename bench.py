@@ -1,6 +1,6 @@
 """Throughput of the streaming code2wav decoder on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--precision f32|f16|split] [--weights float|int8] [--graph] [--no-cpu-baseline] [--split-line] [--peaks-only] [--barrier-probe]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--precision f32|f16|split] [--weights float|int8] [--graph] [--no-cpu-baseline] [--split-line] [--peaks-only] [--barrier-probe] [--library-gemm]
 
 A step decodes one 25-frame chunk (2 s of audio) for each of 64 independent
 streams whose states were first warmed (untimed) to different positions: the
@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--barrier-probe", action="store_true",
                     help="run only the ordering-point microbenchmarks (a grid-wide barrier inside one kernel "
                          "against a dependent launch)")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="time the vendor GEMM (torch.matmul) on the BigVGAN conv shapes, inputs expanded per tap")
     ap.add_argument("--counters", action="store_true",
                     help="decode exactly one batched step from fresh states, for rocprofv3 --pmc runs")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -252,6 +254,40 @@ def measure_barrier(torch, vb, rounds=500, launches=1000, reps=3):
                      f"past the caches); {launches} back-to-back launches of an empty {cus}-workgroup kernel; "
                      f"best of {reps} after a warm-up, HIP events")
     return res
+
+
+def library_gemm(torch, model, batch, frames, reps=5):
+    """For scale: the vendor GEMM (torch.matmul, hipBLASLt on ROCm) on the
+    GEMM shapes of the BigVGAN AMP convs of the batched step (rows = the
+    stage's output rows over the batch, K = channels x taps, N = channels),
+    with the input already expanded per tap (k times the bytes of the conv's
+    input rows) and no epilogue.  HIP events, best of `reps` after a warm-up."""
+    rows = batch * frames * int(np.prod(model["up_strides"]))
+    out = []
+    for si, rate in enumerate(model["rates"]):
+        rows *= rate
+        c = model["stage_channels"][si + 1]
+        for k in model["res_kernels"]:
+            for dt, name in ((torch.float16, "f16"), (torch.float32, "f32")):
+                a = torch.randn(rows, c * k, device="cuda", dtype=dt)
+                w = torch.randn(c * k, c, device="cuda", dtype=dt)
+                y = torch.empty(rows, c, device="cuda", dtype=dt)
+                torch.matmul(a, w, out=y)
+                torch.cuda.synchronize()
+                best = None
+                for _ in range(reps):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    torch.matmul(a, w, out=y)
+                    e1.record()
+                    torch.cuda.synchronize()
+                    ms = e0.elapsed_time(e1)
+                    best = ms if best is None else min(best, ms)
+                out.append({"stage": si, "channels": c, "k": k, "rows": rows, "dtype": name, "ms": round(best, 4),
+                            "tflops": round(2.0 * rows * c * k * c / best / 1e9, 1)})
+                del a, w, y
+                torch.cuda.empty_cache()
+    return out
 
 
 def warm_states(dec, codes, batch, torch):
@@ -499,6 +535,12 @@ def main():
     if args.peaks_only:
         torch.cuda.set_device(0)
         print(json.dumps({"peaks_measured": measure_peaks(torch, vb)}), flush=True)
+        return
+    if args.library_gemm:
+        torch.cuda.set_device(0)
+        wl = S.workload(args.workload)
+        for r in library_gemm(torch, wl["model"], wl["batch"], wl["frames"]):
+            print(json.dumps({"library_gemm": r}), flush=True)
         return
     if args.barrier_probe:
         torch.cuda.set_device(0)
